@@ -1,0 +1,118 @@
+/*
+ * sgemm.h -- C ABI of libsgemm, single-precision GEMM for MI355X (gfx950).
+ *
+ * Operation (all entry points that compute):
+ *
+ *     C := alpha * A * B + beta * C
+ *
+ * with A an M x K, B a K x N and C an M x N matrix of IEEE binary32 values.
+ * The operation and its shapes are the ones defined in "SGEMM CUDA kernel
+ * (First Half)" (introduction: S for single precision, GEMM for
+ * C = alpha*A*B + beta*C, A is M x K, B is K x N, C is M x N, K the inner
+ * dimension) and used by every kernel of "Optimizing Matrix Multiplication in
+ * CUDA" and "1D Register Tiling: One Thread, TM Outputs" (section "The
+ * Kernel": the epilogue alpha * acc + beta * C).
+ *
+ * Layout: row-major with leading dimensions, as in the pages' OFFSET(row, col)
+ * = row * ncols + col addressing ("SGEMM CUDA kernel (First Half)", "Part 1:
+ * CPU version") with the row stride made explicit:
+ *     A(i, k) = A[i * lda + k],  B(k, j) = B[k * ldb + j],  C(i, j) = C[i * ldc + j].
+ * Requirements: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).
+ *
+ * Memory and ownership: A, B and C are DEVICE pointers (e.g. from hipMalloc or
+ * a torch CUDA tensor) owned by the caller.  The library allocates no device
+ * memory and keeps no pointer after it returns.  C must not overlap A or B
+ * (checked, error -10); A and B may overlap each other.
+ *
+ * Streams: work is enqueued on `stream` (0 = the null stream) and the call
+ * returns without waiting for it; the usual stream ordering applies.  There is
+ * no implicit synchronisation.  Calls are thread-safe (no global mutable state).
+ *
+ * Semantics of the special cases:
+ *   - M == 0 or N == 0: nothing is done (returns 0).
+ *   - alpha == 0 or K == 0: A and B are not read; C := beta * C.
+ *   - beta == 0: C is not read (NaN or Inf in C do not propagate); C := alpha * A * B.
+ *   The "beta == 0 skips the read of C" reading follows "Optimizing
+ *   Matrix Multiplication in CUDA", section "1D Thread Tiling", whose epilogue
+ *   does not read C when beta is zero.
+ *
+ * Rounding: products are accumulated in fp32 with fused multiply-adds in an
+ * order that depends on the kernel variant ("SGEMM CUDA kernel (First Half)",
+ * "Part 4", section "FMA": one rounding per multiply-add).  Results differ from
+ * an exact product only by fp32 rounding; integer-valued inputs whose partial
+ * sums stay below 2^24 in magnitude give exact results.
+ *
+ * Return codes (never aborts, never prints):
+ *    0   success (work enqueued, or a valid quick return);
+ *   -i   argument i is invalid (1-based, BLAS style): M=1, N=2, K=3, alpha=4,
+ *        A=5, lda=6, B=7, ldb=8, beta=9, C=10, ldc=11, stream=12,
+ *        variant=13 (sgemm_ex only); nothing is enqueued;
+ *   +e   a hipError_t returned by the kernel launch.
+ */
+#ifndef LIBSGEMM_SGEMM_H
+#define LIBSGEMM_SGEMM_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_API __attribute__((visibility("default")))
+
+/* C := alpha*A*B + beta*C on `stream`, variant chosen by shape and alignment.
+ * Null A or B is accepted only when alpha == 0 or K == 0; null C only when
+ * M == 0 or N == 0. */
+SGEMM_API int sgemm(int M, int N, int K, float alpha,
+                    const float *A, int lda,
+                    const float *B, int ldb,
+                    float beta, float *C, int ldc,
+                    hipStream_t stream);
+
+/* As sgemm, with the kernel variant forced (0 <= variant < sgemm_num_variants()),
+ * or chosen as sgemm does when variant < 0.  Returns -13 when the id is out of
+ * range or the variant's precondition fails (vector variants need A, B and C
+ * 16-byte aligned, lda, ldb, ldc, K and N multiples of 4).  The operation
+ * performed is the same for every variant; only speed and fp32 rounding order
+ * differ.  Used by the autotuner, the bench and the tests. */
+SGEMM_API int sgemm_ex(int M, int N, int K, float alpha,
+                       const float *A, int lda,
+                       const float *B, int ldb,
+                       float beta, float *C, int ldc,
+                       hipStream_t stream, int variant);
+
+/* Number of kernel variants (ids 0 .. n-1). */
+SGEMM_API int sgemm_num_variants(void);
+
+/* Static name of a variant, e.g. "mfma32_128x128x16_w64x64_vec"; NULL when out of range. */
+SGEMM_API const char *sgemm_variant_name(int variant);
+
+/* Tile parameters of a variant, written to info[0 .. n-1] (n >= 9):
+ *   info[0] kind (0 = MFMA 32x32x2 f32, 1 = vector FMA), info[1] BM, info[2] BN,
+ *   info[3] BK, info[4] WM (MFMA wave tile rows) or TM (VALU microtile rows),
+ *   info[5] WN or TN, info[6] threads per workgroup, info[7] vector loads (0/1),
+ *   info[8] LDS bytes per workgroup.
+ * Returns 0, or -1 for a bad id or n < 9. */
+SGEMM_API int sgemm_variant_info(int variant, int *info, int n);
+
+/* The variant id sgemm would use for these arguments (pure host function, no GPU
+ * call); -1 when the arguments describe a quick return or are invalid. */
+SGEMM_API int sgemm_select_variant(int M, int N, int K,
+                                   const float *A, int lda,
+                                   const float *B, int ldb,
+                                   const float *C, int ldc);
+
+/* Host-side copy of the workgroup -> output-tile map every kernel uses (for tests):
+ * fills tile_m[w], tile_n[w] for w in [0, tiles_m * tiles_n).  Returns 0, or -1
+ * on a bad argument. */
+SGEMM_API int sgemm_tile_order(int tiles_m, int tiles_n, int group_m,
+                               int *tile_m, int *tile_n);
+
+/* Library version string. */
+SGEMM_API const char *sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSGEMM_SGEMM_H */
