@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Bench of libsgemm: SGEMM TFLOP/s and % of the MI355X FP32 peak on one GPU.
+
+One step = one call of the library's ``sgemm`` on the whole workload (inputs
+resident in HBM before the timed region).  Default workload: M = N = K = 4096,
+A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload square4096]
+                    [--variant ID] [--no-cpu-baseline]
+
+FLOP count: 2*M*N*K per call (one multiply and one add per (i, j, k); the
+count "SGEMM CUDA kernel (First Half)", "Part 4", gives as 2MNK, and with which
+"1D Register Tiling: One Thread, TM Outputs" turns 10.506 ms at 4096^3 into
+13081.8 GFLOP/s).  The epilogue's alpha/beta operations are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP32_PEAK_TFLOPS = 157.3      # MI355X dense FP32 (MFMA), 256 CUs x 2.4 GHz x 256 FLOP/clk
+FP32_VALU_PEAK_TFLOPS = 78.6  # unpacked v_fma_f32: 256 CUs x 2.4 GHz x 128 FLOP/clk
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources the kernels are built from (ties stored counters to a kernel version)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp32_gemm_05_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, variant: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they match this kernel build."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{variant}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 12.0):
+    """Time the float64 oracle on a bounded sample of the same workload (leading rows of C).
+
+    The oracle's values on those rows also check the GPU output of the first call.
+    Returns (record for the JSON line, parity summary).
+    """
+    import numpy as np
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    flops_per_row = 2.0 * w.N * w.K
+    probe = min(w.M, 16)
+    t0 = time.perf_counter()
+    oracle.ref_rows(A, B, C0, w.alpha, w.beta, rows=(0, probe), nthreads=threads)
+    t_probe = max(time.perf_counter() - t0, 1e-6)
+    rate = probe * flops_per_row / t_probe
+    rows = int(min(w.M, max(probe, rate * target_s / flops_per_row)))
+    t0 = time.perf_counter()
+    ref, bound = oracle.ref_rows(A, B, C0, w.alpha, w.beta, rows=(0, rows), nthreads=threads)
+    dt = time.perf_counter() - t0
+    used = oracle.max_threads()
+    got = out_gpu[:rows].astype(np.float64)
+    err_ratio = np.abs(got - ref) / bound
+    parity = {
+        "rows_checked": rows,
+        "max_err_over_bound": float(err_ratio.max()) if rows else 0.0,
+        "pass": bool(np.isfinite(got).all() and (err_ratio <= 1.0).all()),
+    }
+    rec = {
+        "value": rows * flops_per_row / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows} of C ({rows}x{w.N} outputs, K={w.K}), float64 i-j-k loop, "
+                  f"{dt:.1f} s wall",
+        "seconds": dt,
+    }
+    return rec, parity
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant id (default: dispatch)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): libsgemm is a single-GPU "
+              f"library and no multi-GPU path is built.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp32_gemm_05_amd as sg
+    from fp32_gemm_05_amd.build import build, is_stale
+    from fp32_gemm_05_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    if not os.path.exists(sg.library_path()) or is_stale():
+        log("libsgemm.so missing or stale: building")
+        build()
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload: {w.describe()}")
+    A, B, C0 = make_inputs(w)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.from_numpy(C0).to(dev)
+    vid = args.variant if args.variant >= 0 else sg.sgemm_select_variant(
+        w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N)
+    vname = sg.sgemm_variant_name(vid)
+    info = sg.sgemm_variant_info(vid)
+    log(f"variant: {vname} {info}")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sg.sgemm_ex(w.M, w.N, w.K, w.alpha, dA.data_ptr(), w.K, dB.data_ptr(), w.N, w.beta,
+                    dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
+
+    # first call: its output is the one checked against the oracle
+    step()
+    torch.cuda.synchronize()
+    out_first = dC.cpu().numpy()
+
+    for _ in range(args.warmup):
+        step()
+    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        ev_start[i].record(stream)
+        step()
+        ev_end[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch = np.array([s.elapsed_time(e) for s, e in zip(ev_start, ev_end)])
+    ms_per_step = total_ms / args.steps
+    flops = 2.0 * w.M * w.N * w.K
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    avg_launch_ms = float(per_launch.mean())
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms events, {wall * 1e3:.3f} ms wall; per launch "
+        f"mean {avg_launch_ms:.4f} ms, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
+
+    is_mfma = info["kind"] == "mfma"
+    peak = FP32_PEAK_TFLOPS if is_mfma else FP32_VALU_PEAK_TFLOPS
+    traffic = stored_traffic(w.name, vname)
+    roofline = {
+        "bound": "mfma" if is_mfma else "alu",
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic,
+    }
+    alg_bytes = 4.0 * (w.M * w.K + w.K * w.N + (2 if w.beta != 0 else 1) * w.M * w.N)
+    line = {
+        "metric": "SGEMM TFLOP/s and % of FP32 peak at M=N=K=4096 on 1 MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"sgemm {w.M}x{w.N}x{w.K} alpha={w.alpha:g} beta={w.beta:g} {w.dist} seed={w.seed}",
+            "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+            "variant": vname,
+        },
+        "pct_fp32_peak": round(100.0 * tflops / FP32_PEAK_TFLOPS, 2),
+        "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        rec, parity = cpu_baseline(A, B, C0, w, out_first)
+        line["cpu_baseline"] = {k: rec[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"]["value"] = round(rec["value"], 6)
+        line["parity"] = parity
+        log(f"oracle: {rec['sample']} on {rec['cores']} threads; parity {parity}")
+        if not parity["pass"]:
+            log("PARITY FAILURE: the timed kernel's output is outside the oracle bound")
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0 if line.get("parity", {"pass": True})["pass"] else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,52 @@
+"""Build step of libsgemm: compile the HIP sources for gfx950 into libsgemm.so (in-tree)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsgemm.so")
+SOURCES = [os.path.join(CSRC, "sgemm.hip")]
+DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("sgemm_kernels.hpp", "tuned_table.inc")] + [
+    os.path.join(os.path.dirname(HERE), "include", "sgemm.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-fvisibility=hidden",
+    # no packed-fp32 instructions in any kernel (scalar fp32 VALU and MFMA only)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> str:
+    """Compile every HIP source into one shared library; returns its path."""
+    out = out or LIB
+    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *SOURCES, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass reports the device-only target feature as unknown; drop that line only
+    noise = "is not a recognized feature for this target"
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msg}")
+    if verbose and msg.strip():
+        print(msg, file=sys.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def is_stale(lib: str = LIB) -> bool:
+    if not os.path.exists(lib):
+        return True
+    t = os.path.getmtime(lib)
+    return any(os.path.getmtime(d) > t for d in DEPENDS if os.path.exists(d))
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,423 @@
+// sgemm_kernels.hpp -- HIP kernels of libsgemm for gfx950 (CDNA4, wave64).
+//
+// Every kernel computes C := alpha*A*B + beta*C on row-major fp32 matrices with
+// leading dimensions (the operation of "SGEMM CUDA kernel (First Half)",
+// introduction).  One workgroup owns one BM x BN tile of C and walks K in
+// BK-deep slabs, staging a BM x BK slab of A and a BK x BN slab of B in LDS
+// (the shared-memory tiling of "Shared Memory and Register Blocking", CUDA
+// Handbook ch. 17).  What is MI355X-specific:
+//
+//   * two LDS stages: slab s+1 is fetched from global memory into registers
+//     while slab s is multiplied out of LDS, then written to the other stage,
+//     so each slab costs one workgroup barrier instead of two;
+//   * the MFMA family multiplies with v_mfma_f32_32x32x2_f32: a wave owns a
+//     WM x WN sub-tile made of 32x32 blocks (the warp tiling of "Optimizing
+//     Matrix Multiplication in CUDA", section "Warp Tiling", re-cut for 64-lane
+//     waves and matrix cores);
+//   * the VALU family keeps a TM x TN register microtile per lane (the outer
+//     product of "SGEMM CUDA kernel (First Half)", "Part 4", and Figure 17-3 of
+//     the handbook) with A stored k-major in LDS (the transposed slab of "Part
+//     5: Reduced bank conflict (v3)");
+//   * global loads are 128-bit (the float4 loads of "Part 6: Vectorized load
+//     (v4)") when every row is 16-byte aligned, otherwise 32-bit; in both the
+//     lane-fastest index walks contiguous memory (the coalescing of "Global
+//     Memory Coalescing");
+//   * the workgroup -> tile map is XCD-aware: consecutive workgroup ids are
+//     spread round-robin over the 8 XCDs, so each XCD is handed a contiguous
+//     range of tiles, ordered in groups of rows so that tiles running at the
+//     same time share A rows and B columns in that XCD's L2.
+//
+// Edge handling (out-of-range slab elements are zero, stores are guarded, as
+// in the pages' bounds-checked kernels): A rows past M and B columns past N
+// are clamped to the last valid row/column -- they only feed accumulators of C
+// elements that are never stored -- while slab elements past K are zero, so
+// that they add nothing (and no NaN) to valid outputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace libsgemm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct GemmArgs {
+    int M, N, K;
+    float alpha, beta;
+    const float* A;
+    long lda;
+    const float* B;
+    long ldb;
+    float* C;
+    long ldc;
+};
+
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// Workgroup id -> (tile_m, tile_n).  A bijection of [0, tiles_m*tiles_n).
+__host__ __device__ inline void tile_of(int wg, int nwg, int tiles_m, int tiles_n, int group_m,
+                                        int& tm, int& tn) {
+    // (1) the hardware hands workgroup w to XCD w % 8; renumber so that XCD x
+    //     gets the contiguous range [start_x, start_x + count_x).
+    const int q = nwg / kNumXcd, r = nwg % kNumXcd;
+    const int x = wg % kNumXcd, p = wg / kNumXcd;
+    const int t = x * q + (x < r ? x : r) + p;
+    // (2) grouped order: blocks of group_m tile-rows, swept column by column.
+    const int per_group = group_m * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int rows_left = tiles_m - first_m;
+    const int gsz = rows_left < group_m ? rows_left : group_m;
+    const int local = t - g * per_group;
+    tm = first_m + local % gsz;
+    tn = local / gsz;
+}
+
+__device__ inline int imin(int a, int b) { return a < b ? a : b; }
+
+// ---------------------------------------------------------------------------------
+// Slab loaders (global -> registers -> LDS).  LDS slabs are row-major with a
+// padded pitch: A as [BM][BK + PA] (k contiguous) for the MFMA kernel.
+// ---------------------------------------------------------------------------------
+
+// Loader for a ROWS x COLS row-major panel of a matrix whose valid extent is
+// nrows x ncols.  `clamp_rows` selects what happens to rows past nrows: clamp
+// (true) or zero (false); columns past ncols are clamped when `clamp_cols`,
+// zero otherwise.  Vector form: one 16-byte load covers 4 consecutive columns
+// (needs ld % 4 == 0, ncols % 4 == 0 and a 16-byte aligned base).
+template <int ROWS, int COLS, int NT, bool VEC>
+struct PanelLoader {
+    static constexpr int W = VEC ? 4 : 1;             // floats per load
+    static constexpr int CPR = COLS / W;              // loads per panel row
+    static constexpr int L = ROWS * CPR / NT;         // loads per thread
+    static_assert(COLS % W == 0, "panel width");
+    static_assert((ROWS * CPR) % NT == 0, "panel must split evenly over the workgroup");
+    static_assert(NT % CPR == 0, "a load pass must cover whole panel rows");
+    static constexpr int ROWS_PER_PASS = NT / CPR;
+
+    f32x4 v[L];  // only .x used when !VEC
+    int row0, col;  // this thread's first panel row and its column
+
+    __device__ inline void init(int tid) {
+        row0 = tid / CPR;
+        col = (tid % CPR) * W;
+    }
+
+    // Fetch the panel whose top-left element is (r0, c0) of the matrix.
+    template <bool CLAMP_ROWS, bool CLAMP_COLS>
+    __device__ inline void fetch(const float* __restrict__ base, long ld, int r0, int c0,
+                                 int nrows, int ncols) {
+        int c = c0 + col;
+        bool cok = c < ncols;
+        if (CLAMP_COLS) {
+            c = imin(c, ncols - W);
+            cok = true;
+        }
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            int r = r0 + row0 + l * ROWS_PER_PASS;
+            bool rok = r < nrows;
+            if (CLAMP_ROWS) {
+                r = imin(r, nrows - 1);
+                rok = true;
+            }
+            const float* p = base + (long)r * ld + c;
+            if (VEC) {
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                v[l] = (rok && cok) ? *reinterpret_cast<const f32x4*>(p) : z;
+            } else {
+                v[l].x = (rok && cok) ? *p : 0.f;
+            }
+        }
+    }
+
+    // Store into an LDS panel [ROWS][PITCH].
+    template <int PITCH>
+    __device__ inline void store(float* __restrict__ lds) const {
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            float* q = lds + (row0 + l * ROWS_PER_PASS) * PITCH + col;
+            if (VEC)
+                *reinterpret_cast<f32x4*>(q) = v[l];
+            else
+                *q = v[l].x;
+        }
+    }
+
+    // Store transposed into an LDS panel [COLS][PITCH] (element (r, c) -> lds[c][r]).
+    template <int PITCH>
+    __device__ inline void store_transposed(float* __restrict__ lds) const {
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const int r = row0 + l * ROWS_PER_PASS;
+            if (VEC) {
+                lds[(col + 0) * PITCH + r] = v[l].x;
+                lds[(col + 1) * PITCH + r] = v[l].y;
+                lds[(col + 2) * PITCH + r] = v[l].z;
+                lds[(col + 3) * PITCH + r] = v[l].w;
+            } else {
+                lds[col * PITCH + r] = v[l].x;
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------------
+// MFMA kernel: v_mfma_f32_32x32x2_f32, wave tile WM x WN of 32x32 blocks.
+//
+// Operand mapping of one 32x32x2 step (lane l, h = l / 32, i = l % 32):
+//   A operand: lane l supplies A(i, kA(h)), B operand: lane l supplies B(kB(h), i)
+//   accumulator register r of lane l holds D(8*(r/4) + 4*h + r%4, i).
+// Within one 8-deep group of a slab, step s in 0..3 takes k = 4*h + s for half h,
+// so a lane's four A values are contiguous in the k-major LDS slab (one 128-bit
+// LDS read) and the 8 k's of the group are each used exactly once.
+// ---------------------------------------------------------------------------------
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+struct MfmaCfg {
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int PA = 4;  // A slab pitch BK+4: 128-bit reads of 16 consecutive rows hit distinct banks
+    static constexpr int PB = 8;  // B slab pitch BN+8: the two half-waves (k and k+4) land on opposite bank halves
+    static constexpr int A_PITCH = BK + PA, B_PITCH = BN + PB;
+    static constexpr int A_STAGE = BM * A_PITCH, B_STAGE = BK * B_PITCH;
+    static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 4;
+    static_assert(BM % WM == 0 && BN % WN == 0, "wave tiling");
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
+sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
+    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
+    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
+    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / Cfg::WAVES_N) * WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+
+    PanelLoader<BM, BK, NT, VEC> la;  // A slab: BM rows x BK columns of A
+    PanelLoader<BK, BN, NT, VEC> lb;  // B slab: BK rows x BN columns of B
+    la.init(tid);
+    lb.init(tid);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int K = g.K;
+    const int nslab = (K + BK - 1) / BK;
+
+    // A: rows past M clamped, columns (k) past K zero.  B: rows (k) past K zero, columns past N clamped.
+    la.template fetch<true, false>(g.A, g.lda, m0, 0, g.M, K);
+    lb.template fetch<false, true>(g.B, g.ldb, 0, n0, K, g.N);
+    la.template store<AP>(lds_a);
+    lb.template store<BP>(lds_b);
+    __syncthreads();
+
+    for (int s = 0; s < nslab; ++s) {
+        const int cur = s & 1;
+        const bool more = s + 1 < nslab;
+        if (more) {
+            const int k1 = (s + 1) * BK;
+            la.template fetch<true, false>(g.A, g.lda, m0, k1, g.M, K);
+            lb.template fetch<false, true>(g.B, g.ldb, k1, n0, K, g.N);
+        }
+        const float* sa = lds_a + cur * Cfg::A_STAGE;
+        const float* sb = lds_b + cur * Cfg::B_STAGE;
+#pragma unroll
+        for (int kk = 0; kk < BK / 8; ++kk) {
+            f32x4 a[FM];
+            float b[FN][4];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                a[i] = *reinterpret_cast<const f32x4*>(sa + (wm0 + i * 32 + li) * AP + kk * 8 + lh * 4);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    b[j][t] = sb[(kk * 8 + lh * 4 + t) * BP + wn0 + j * 32 + li];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][t], b[j][t], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            la.template store<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
+            lb.template store<BP>(lds_b + (cur ^ 1) * Cfg::B_STAGE);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: C = alpha*acc + beta*C, C not read when beta == 0.
+    const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn0 + j * 32 + li;
+            if (col >= g.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm0 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                if (row < g.M) {
+                    float* pc = g.C + (long)row * g.ldc + col;
+                    float v = alpha * acc[i][j][r];
+                    if (beta != 0.f) v += beta * *pc;
+                    *pc = v;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// VALU kernel: TM x TN register microtile per lane, A stored k-major in LDS.
+// A lane's TM rows are TM/4 groups of 4 consecutive rows spaced BM/(TM/4)
+// apart (likewise for columns), so the 128-bit LDS reads of a wave touch
+// consecutive addresses (B) or broadcast (A).
+// ---------------------------------------------------------------------------------
+template <int BM, int BN, int BK, int TM, int TN, bool VEC>
+struct ValuCfg {
+    static constexpr int TX = BN / TN, TY = BM / TM, NT = TX * TY;
+    static constexpr int GM = TM / 4, GN = TN / 4;
+    static constexpr int SM = BM / GM, SN = BN / GN;
+    static constexpr int PA = 4, PB = 4;
+    static constexpr int A_PITCH = BM + PA, B_PITCH = BN + PB;
+    static constexpr int A_STAGE = BK * A_PITCH, B_STAGE = BK * B_PITCH;
+    static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 4;
+    static_assert(TM % 4 == 0 && TN % 4 == 0, "microtile in groups of 4");
+    static_assert(BM % TM == 0 && BN % TN == 0, "tiling");
+};
+
+template <int BM, int BN, int BK, int TM, int TN, bool VEC>
+__global__ void __launch_bounds__((ValuCfg<BM, BN, BK, TM, TN, VEC>::NT))
+sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
+    constexpr int NT = Cfg::NT, GM = Cfg::GM, GN = Cfg::GN, SM = Cfg::SM, SN = Cfg::SN;
+    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
+    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
+    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int tx = tid % Cfg::TX, ty = tid / Cfg::TX;
+
+    PanelLoader<BM, BK, NT, VEC> la;
+    PanelLoader<BK, BN, NT, VEC> lb;
+    la.init(tid);
+    lb.init(tid);
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
+
+    const int K = g.K;
+    const int nslab = (K + BK - 1) / BK;
+    la.template fetch<true, false>(g.A, g.lda, m0, 0, g.M, K);
+    lb.template fetch<false, true>(g.B, g.ldb, 0, n0, K, g.N);
+    la.template store_transposed<AP>(lds_a);
+    lb.template store<BP>(lds_b);
+    __syncthreads();
+
+    for (int s = 0; s < nslab; ++s) {
+        const int cur = s & 1;
+        const bool more = s + 1 < nslab;
+        if (more) {
+            const int k1 = (s + 1) * BK;
+            la.template fetch<true, false>(g.A, g.lda, m0, k1, g.M, K);
+            lb.template fetch<false, true>(g.B, g.ldb, k1, n0, K, g.N);
+        }
+        const float* sa = lds_a + cur * Cfg::A_STAGE;
+        const float* sb = lds_b + cur * Cfg::B_STAGE;
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            float a[TM], b[TN];
+#pragma unroll
+            for (int gi = 0; gi < GM; ++gi) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sa + k * AP + gi * SM + ty * 4);
+                a[gi * 4 + 0] = v.x; a[gi * 4 + 1] = v.y; a[gi * 4 + 2] = v.z; a[gi * 4 + 3] = v.w;
+            }
+#pragma unroll
+            for (int gj = 0; gj < GN; ++gj) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sb + k * BP + gj * SN + tx * 4);
+                b[gj * 4 + 0] = v.x; b[gj * 4 + 1] = v.y; b[gj * 4 + 2] = v.z; b[gj * 4 + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+        if (more) {
+            la.template store_transposed<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
+            lb.template store<BP>(lds_b + (cur ^ 1) * Cfg::B_STAGE);
+        }
+        __syncthreads();
+    }
+
+    const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = m0 + (i / 4) * SM + ty * 4 + (i % 4);
+        if (row >= g.M) continue;
+        float* prow = g.C + (long)row * g.ldc;
+#pragma unroll
+        for (int gj = 0; gj < GN; ++gj) {
+            const int col = n0 + gj * SN + tx * 4;
+            if (VEC) {
+                // N % 4 == 0: a 4-column group is entirely inside or outside.
+                if (col < g.N) {
+                    f32x4* pc = reinterpret_cast<f32x4*>(prow + col);
+                    f32x4 v = {alpha * acc[i][gj * 4 + 0], alpha * acc[i][gj * 4 + 1],
+                               alpha * acc[i][gj * 4 + 2], alpha * acc[i][gj * 4 + 3]};
+                    if (beta != 0.f) v += beta * *pc;
+                    *pc = v;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (col + e < g.N) {
+                        float v = alpha * acc[i][gj * 4 + e];
+                        if (beta != 0.f) v += beta * prow[col + e];
+                        prow[col + e] = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// C := beta * C (the alpha == 0 / K == 0 case; beta == 0 writes zeros without reading C).
+// ---------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float beta, float* C, long ldc) {
+    const long total = (long)M * N;
+    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
+        const long i = e / N, j = e - i * N;
+        float* p = C + i * ldc + j;
+        *p = (beta == 0.f) ? 0.f : beta * *p;
+    }
+}
+
+}  // namespace libsgemm

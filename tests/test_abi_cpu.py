@@ -1,0 +1,144 @@
+"""CPU-side checks of the C ABI: the library loads, exports what include/sgemm.h declares,
+validates arguments and chooses variants without touching a GPU.
+
+No call here launches work: every call either fails validation, is a quick
+return with M == 0 or N == 0, or is a pure host function.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_05_amd as sg
+from fp32_gemm_05_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"SGEMM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_abi():
+    names = declared_symbols()
+    for n in ["sgemm", "sgemm_ex", "sgemm_num_variants", "sgemm_variant_name", "sgemm_variant_info",
+              "sgemm_select_variant", "sgemm_tile_order", "sgemm_version"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sg.library_path())
+    for n in declared_symbols():
+        assert hasattr(lib, n), f"{n} declared in sgemm.h but not exported"
+
+
+def test_version_and_variants():
+    assert "libsgemm" in sg.sgemm_version()
+    n = sg.sgemm_num_variants()
+    assert n >= 4
+    names = [sg.sgemm_variant_name(i) for i in range(n)]
+    assert len(set(names)) == n
+    assert sg.sgemm_variant_name(-1) is None and sg.sgemm_variant_name(n) is None
+    kinds = set()
+    for i in range(n):
+        info = sg.sgemm_variant_info(i)
+        kinds.add(info["kind"])
+        assert info["name"].startswith("mfma32_" if info["kind"] == "mfma" else "valu_")
+        assert f"{info['BM']}x{info['BN']}x{info['BK']}" in info["name"]
+        assert info["name"].endswith("_vec") == bool(info["vec"])
+        assert info["threads"] % 64 == 0 and info["threads"] <= 1024
+        assert info["lds_bytes"] <= 160 * 1024
+    assert kinds == {"mfma", "valu"}
+    with pytest.raises(ValueError):
+        sg.sgemm_variant_info(n)
+
+
+FAKE_A, FAKE_B, FAKE_C = 0x10000000, 0x20000000, 0x30000000  # never dereferenced
+
+
+def _call(M, N, K, lda, ldb, ldc, A=FAKE_A, B=FAKE_B, C=FAKE_C, alpha=1.0, beta=0.0, variant=-1):
+    lib = sg.load_library()
+    return lib.sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None, variant)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, 4, 4, 4), -1),
+    ((4, -1, 4, 4, 1, 1), -2),
+    ((4, 4, -1, 1, 4, 4), -3),
+    ((4, 4, 4, 3, 4, 4), -6),
+    ((4, 4, 4, 4, 3, 4), -8),
+    ((4, 4, 4, 4, 4, 3), -11),
+    ((4, 4, 0, 0, 4, 4), -6),   # lda >= max(1, K)
+    ((4, 0, 4, 4, 0, 1), -8),   # ldb >= max(1, N)
+])
+def test_invalid_arguments(args, code):
+    assert _call(*args) == code
+
+
+def test_null_pointers():
+    assert _call(4, 4, 4, 4, 4, 4, C=None) == -10
+    assert _call(4, 4, 4, 4, 4, 4, A=None) == -5
+    assert _call(4, 4, 4, 4, 4, 4, B=None) == -7
+
+
+def test_overlapping_c_rejected():
+    # C overlaps A's addressed range
+    assert _call(4, 4, 4, 4, 4, 4, A=FAKE_C + 16) == -10
+    # C overlaps B's addressed range
+    assert _call(4, 4, 4, 4, 4, 4, B=FAKE_C - 16) == -10
+
+
+def test_quick_returns_need_no_gpu():
+    assert _call(0, 4, 4, 4, 4, 4, A=None, B=None, C=None) == 0
+    assert _call(4, 0, 4, 4, 1, 1, A=None, B=None, C=None) == 0
+
+
+def test_bad_variant_id():
+    assert _call(4, 4, 4, 4, 4, 4, variant=sg.sgemm_num_variants()) == -13
+
+
+def test_vector_variant_refuses_misaligned():
+    vec = [i for i in range(sg.sgemm_num_variants()) if sg.sgemm_variant_info(i)["vec"]]
+    assert vec
+    for v in vec:
+        assert _call(8, 8, 8, 8, 8, 8, A=FAKE_A + 4, variant=v) == -13   # pointer not 16-byte aligned
+        assert _call(8, 8, 8, 9, 8, 8, variant=v) == -13                 # lda % 4 != 0
+        assert _call(8, 7, 8, 8, 7, 7, variant=v) == -13                 # N % 4 != 0
+        assert _call(8, 8, 6, 8, 8, 8, variant=v) == -13                 # K % 4 != 0
+
+
+def test_select_variant_classes():
+    n = sg.sgemm_num_variants()
+    big = sg.sgemm_select_variant(4096, 4096, 4096, FAKE_A, 4096, FAKE_B, 4096, FAKE_C, 4096)
+    assert 0 <= big < n and sg.sgemm_variant_info(big)["vec"] == 1
+    ragged = sg.sgemm_select_variant(3001, 5003, 777, FAKE_A, 777, FAKE_B, 5003, FAKE_C, 5003)
+    assert 0 <= ragged < n and sg.sgemm_variant_info(ragged)["vec"] == 0
+    skinny = sg.sgemm_select_variant(65536, 64, 1024, FAKE_A, 1024, FAKE_B, 64, FAKE_C, 64)
+    assert 0 <= skinny < n and sg.sgemm_variant_info(skinny)["BN"] <= 64
+    mis = sg.sgemm_select_variant(4096, 4096, 4096, FAKE_A + 4, 4096, FAKE_B, 4096, FAKE_C, 4096)
+    assert sg.sgemm_variant_info(mis)["vec"] == 0
+    assert sg.sgemm_select_variant(0, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4) == -1
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,group_m", [
+    (1, 1, 8), (1, 7, 8), (7, 1, 8), (32, 32, 8), (24, 40, 8), (3, 5, 2), (512, 1, 8), (17, 9, 4),
+    (64, 64, 8), (2, 2, 8), (9, 33, 16)])
+def test_tile_order_is_a_bijection(tiles_m, tiles_n, group_m):
+    tm, tn = _binding.tile_order(tiles_m, tiles_n, group_m)
+    pairs = set(zip(tm, tn))
+    assert len(pairs) == tiles_m * tiles_n
+    assert all(0 <= a < tiles_m and 0 <= b < tiles_n for a, b in pairs)
+
+
+def test_tile_order_gives_each_xcd_a_compact_block():
+    """Workgroups w, w+8, w+16, ... share an XCD; their tiles should cluster (few distinct rows/cols)."""
+    tiles_m = tiles_n = 32  # 4096^2 at 128x128 tiles
+    tm, tn = _binding.tile_order(tiles_m, tiles_n, 8)
+    for x in range(8):
+        ws = list(range(x, tiles_m * tiles_n, 8))[:64]    # the first 64 workgroups on XCD x
+        rows = {tm[w] for w in ws}
+        cols = {tn[w] for w in ws}
+        assert len(rows) * len(cols) <= 2 * len(ws), (x, len(rows), len(cols))

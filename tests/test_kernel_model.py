@@ -1,0 +1,136 @@
+"""Host model of the kernels' index math: every global load stays inside the operand,
+every output element of C is stored exactly once, nothing outside C's M x N window
+is stored, and each MFMA accumulator receives every k of a slab exactly once.
+
+The model restates, in numpy, the addressing of sgemm_kernels.hpp (PanelLoader,
+the MFMA and VALU epilogues) for each variant the library reports, over a sweep
+of shapes with ragged edges in every dimension.  It runs on the CPU and guards
+the GPU against out-of-bounds accesses before any kernel is launched.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import fp32_gemm_05_amd as sg
+from fp32_gemm_05_amd import _binding
+
+
+def variants():
+    out = []
+    for i in range(sg.sgemm_num_variants()):
+        out.append(sg.sgemm_variant_info(i))
+    return out
+
+
+VARIANTS = variants()
+
+
+def panel_loads(ROWS, COLS, NT, vec, r0, c0, nrows, ncols, clamp_rows, clamp_cols):
+    """(rows, cols, width, loaded) of every load issued for one panel, mirroring PanelLoader.fetch."""
+    W = 4 if vec else 1
+    CPR = COLS // W
+    assert COLS % W == 0 and (ROWS * CPR) % NT == 0 and NT % CPR == 0
+    L = ROWS * CPR // NT
+    RPP = NT // CPR
+    tid = np.arange(NT)
+    row0 = tid // CPR
+    col = (tid % CPR) * W
+    c = c0 + col
+    cok = c < ncols
+    if clamp_cols:
+        c = np.minimum(c, ncols - W)
+        cok = np.ones_like(cok)
+    rows, cols, ok = [], [], []
+    for l in range(L):
+        r = r0 + row0 + l * RPP
+        rok = r < nrows
+        if clamp_rows:
+            r = np.minimum(r, nrows - 1)
+            rok = np.ones_like(rok)
+        # LDS destination stays inside the panel
+        assert (row0 + l * RPP).max() < ROWS and (col + W).max() <= COLS
+        rows.append(r)
+        cols.append(c)
+        ok.append(rok & cok)
+    return np.concatenate(rows), np.concatenate(cols), W, np.concatenate(ok)
+
+
+def check_loads_in_bounds(v, M, N, K):
+    BM, BN, BK, NT, vec = v["BM"], v["BN"], v["BK"], v["threads"], bool(v["vec"])
+    tiles_m, tiles_n = -(-M // BM), -(-N // BN)
+    nslab = -(-K // BK)
+    for tm in range(tiles_m):
+        for s in range(nslab):
+            r, c, W, ok = panel_loads(BM, BK, NT, vec, tm * BM, s * BK, M, K, True, False)
+            r, c = r[ok], c[ok]
+            assert (r >= 0).all() and (r < M).all() and (c >= 0).all() and (c + W <= K).all()
+    for tn in range(tiles_n):
+        for s in range(nslab):
+            r, c, W, ok = panel_loads(BK, BN, NT, vec, s * BK, tn * BN, K, N, False, True)
+            r, c = r[ok], c[ok]
+            assert (r >= 0).all() and (r < K).all() and (c >= 0).all() and (c + W <= N).all()
+
+
+def stored_elements(v, M, N):
+    """All (row, col) the epilogue stores, over every workgroup of the launch."""
+    BM, BN, NT = v["BM"], v["BN"], v["threads"]
+    tiles_m, tiles_n = -(-M // BM), -(-N // BN)
+    tm_of, tn_of = _binding.tile_order(tiles_m, tiles_n, 8)
+    tid = np.arange(NT)
+    rows_all, cols_all = [], []
+    if v["kind"] == "mfma":
+        WM, WN = v["WM_or_TM"], v["WN_or_TN"]
+        waves_n = BN // WN
+        lane, wave = tid % 64, tid // 64
+        wm0, wn0 = (wave // waves_n) * WM, (wave % waves_n) * WN
+        li, lh = lane % 32, lane // 32
+        local = []
+        for i, j, r in itertools.product(range(WM // 32), range(WN // 32), range(16)):
+            local.append((wm0 + i * 32 + (r // 4) * 8 + lh * 4 + (r % 4), wn0 + j * 32 + li))
+    else:
+        TM, TN = v["WM_or_TM"], v["WN_or_TN"]
+        TX = BN // TN
+        SM, SN = BM // (TM // 4), BN // (TN // 4)
+        tx, ty = tid % TX, tid // TX
+        local = []
+        for i, j in itertools.product(range(TM), range(TN)):
+            local.append(((i // 4) * SM + ty * 4 + (i % 4), (j // 4) * SN + tx * 4 + (j % 4)))
+    lr = np.concatenate([a for a, _ in local])
+    lc = np.concatenate([b for _, b in local])
+    for w in range(tiles_m * tiles_n):
+        r = tm_of[w] * BM + lr
+        c = tn_of[w] * BN + lc
+        keep = (r < M) & (c < N)
+        rows_all.append(r[keep])
+        cols_all.append(c[keep])
+    return np.concatenate(rows_all), np.concatenate(cols_all)
+
+
+SHAPES = [(1, 1, 1), (1, 4, 4), (4, 1, 4), (33, 65, 9), (128, 128, 16), (129, 131, 17), (64, 64, 64),
+          (257, 65, 33), (300, 260, 77), (65, 300, 8), (256, 64, 1024), (130, 68, 12)]
+
+
+@pytest.mark.parametrize("v", VARIANTS, ids=[v["name"] for v in VARIANTS])
+def test_loads_in_bounds(v):
+    for (M, N, K) in SHAPES:
+        if v["vec"] and (N % 4 or K % 4):
+            continue  # the variant refuses these shapes
+        check_loads_in_bounds(v, M, N, K)
+
+
+@pytest.mark.parametrize("v", VARIANTS, ids=[v["name"] for v in VARIANTS])
+def test_every_output_stored_exactly_once(v):
+    for (M, N, _) in SHAPES:
+        r, c = stored_elements(v, M, N)
+        assert (r >= 0).all() and (r < M).all() and (c >= 0).all() and (c < N).all()
+        flat = r.astype(np.int64) * N + c
+        counts = np.bincount(flat, minlength=M * N)
+        assert counts.min() == 1 and counts.max() == 1, (v["name"], M, N)
+
+
+@pytest.mark.parametrize("BK", [8, 16, 32])
+def test_mfma_k_mapping_covers_slab_once(BK):
+    """Group kk, step t, half h uses k = 8*kk + 4*h + t for both operands: each k in the slab once."""
+    ks = [8 * kk + 4 * h + t for kk in range(BK // 8) for t in range(4) for h in range(2)]
+    assert sorted(ks) == list(range(BK))
