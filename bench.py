@@ -16,7 +16,6 @@ count "SGEMM CUDA kernel (First Half)", "Part 4", gives as 2MNK, and with which
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -26,23 +25,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FP32_PEAK_TFLOPS = 157.3      # MI355X dense FP32 (MFMA), 256 CUs x 2.4 GHz x 256 FLOP/clk
-FP32_VALU_PEAK_TFLOPS = 78.6  # unpacked v_fma_f32: 256 CUs x 2.4 GHz x 128 FLOP/clk
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense FP32 matrix (MFMA): 256 CUs x 2.4 GHz x 256 FLOP/clk
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X FP32 vector: 256 CUs x 2.4 GHz x 256 FLOP/clk
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    """Hash of the sources the kernels are built from (ties stored counters to a kernel version)."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "fp32_gemm_05_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str, variant: str):
@@ -52,6 +41,7 @@ def stored_traffic(workload: str, variant: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from fp32_gemm_05_amd.profiling import kernel_source_hash
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")

@@ -188,8 +188,11 @@ struct MfmaCfg {
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+// OCC > 0 asks the compiler for at least OCC waves per SIMD (registers capped at 512 / OCC),
+// so that OCC workgroups of 4 waves fit on one CU.
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
     constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;

@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Tile-parameter autotuner of libsgemm: sweep every kernel variant over each shape
+class, gate each candidate on the float64 oracle, time it, and write the dispatch
+table (fp32_gemm_05_amd/csrc/tuned_table.inc) from the winners.
+
+    python tests/autotune.py [--out results.json] [--write-table] [--classes large,small,skinny]
+
+The tile parameters (BM, BN, BK, wave tile WM x WN or microtile TM x TN, and an
+occupancy target) are compile-time template arguments, as in the pages' kernels
+("Optimizing Matrix Multiplication in CUDA", sections on 2D thread tiling and
+warp tiling, where they are template parameters tuned by hand); each compiled
+instance is one variant of the library, and the sweep runs over all of them.
+
+Selection: within a (shape class, vector-load class) pair, a variant must pass
+the oracle check on every representative workload; the winner minimises the
+geometric mean of (time / best time) over those workloads.  This file imports
+the oracle, so it lives with the tests; the library never runs it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+TABLE = os.path.join(ROOT, "fp32_gemm_05_amd", "csrc", "tuned_table.inc")
+
+# (label, shape class, workload name or None, M, N, K, dist, alpha, beta, vector-load eligible)
+CASES = [
+    ("square4096", "large", "square4096", None, None, None, None, None, None, True),
+    ("square8192", "large", "square8192", None, None, None, None, None, None, True),
+    ("ragged3001x5003x777", "large", "ragged3001x5003x777", None, None, None, None, None, None, False),
+    ("square4096_odd_ld", "large", "square4096", 4096, 4095, 4095, "uniform", 1.0, 0.0, False),
+    ("square256", "small", "square256", None, None, None, None, None, None, True),
+    ("square1024_beta", "small", "square1024_beta", None, None, None, None, None, None, True),
+    ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
+    ("skinny65536x64x1024", "skinny", "skinny65536x64x1024", None, None, None, None, None, None, True),
+    ("skinny65536x61x1021", "skinny", "skinny65536x64x1024", 65536, 61, 1021, None, None, None, False),
+]
+CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge"}
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def write_table(winners):
+    lines = ["// Dispatch table: (shape class, vector-load eligibility) -> variant name.",
+             "// Written by tests/autotune.py from timed, oracle-checked runs on MI355X",
+             f"// ({time.strftime('%Y-%m-%d')}); each entry names the geometric-mean-fastest variant",
+             "// over that class's representative workloads.",
+             "const TableEntry kTunedTable[] = {"]
+    for (cls, vclass), (win, sc) in sorted(winners.items()):
+        lines.append(f'    {{{CLASS_IDS[cls]}, {vclass}, "{win}"}},  // slowdown vs per-case best {sc:.3f}')
+    lines.append("};")
+    with open(TABLE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote {TABLE}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
+    ap.add_argument("--write-table", action="store_true")
+    ap.add_argument("--classes", default="large,small,skinny")
+    ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
+    ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
+    ap.add_argument("--table-from", default=None, help="write the table from a saved results file (no GPU)")
+    args = ap.parse_args()
+    if args.table_from:
+        with open(args.table_from) as f:
+            saved = json.load(f)
+        winners = {tuple(k.split("/")): v for k, v in saved["winners"].items()}
+        write_table({(c, int(v)): tuple(w) for (c, v), w in winners.items()})
+        return 0
+
+    import numpy as np
+    import torch
+
+    import fp32_gemm_05_amd as sg
+    import oracle
+    from fp32_gemm_05_amd.workloads import WORKLOADS, make_inputs, sample_points
+
+    classes = set(args.classes.split(","))
+    nvar = sg.sgemm_num_variants()
+    infos = [sg.sgemm_variant_info(v) for v in range(nvar)]
+    results = []
+    stream = torch.cuda.current_stream()
+    for (label, cls, wname, M, N, K, dist, alpha, beta, vec_ok) in CASES:
+        if cls not in classes:
+            continue
+        w = WORKLOADS[wname]
+        M = M or w.M
+        N = N or w.N
+        K = K or w.K
+        alpha = w.alpha if alpha is None else alpha
+        beta = w.beta if beta is None else beta
+        A, B, C0 = make_inputs(w, M=M, N=N, K=K, dist=dist, beta=beta)
+        I, J = sample_points(M, N, args.points, seed=w.seed + 17, tile=64)
+        ref, bound = oracle.ref_points(A, B, C0, I, J, alpha, beta)
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        dC0 = torch.from_numpy(C0).cuda()
+        dC = torch.empty_like(dC0)
+        flops = 2.0 * M * N * K
+        log(f"== {label} ({cls}, vec={vec_ok}): M={M} N={N} K={K} alpha={alpha} beta={beta}")
+        for v, info in enumerate(infos):
+            if info["vec"] and not vec_ok:
+                continue
+            dC.copy_(dC0)
+
+            def call():
+                sg.sgemm_ex(M, N, K, alpha, dA.data_ptr(), K, dB.data_ptr(), N, beta, dC.data_ptr(), N,
+                            stream=stream.cuda_stream, variant=v)
+
+            call()
+            torch.cuda.synchronize()
+            got = dC.cpu().numpy()[I, J].astype(np.float64)
+            ok = bool(np.isfinite(got).all() and (np.abs(got - ref) <= bound).all())
+            ratio = float((np.abs(got - ref) / bound).max())
+            # timing: beta != 0 keeps reading/writing C; the values drift but the work is identical
+            for _ in range(2):
+                call()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            est = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+            reps = int(max(5, min(500, args.min_time / est)))
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for s, e in evs:
+                s.record(stream)
+                call()
+                e.record(stream)
+            torch.cuda.synchronize()
+            ts = sorted(s.elapsed_time(e) for s, e in evs)
+            med = ts[len(ts) // 2]
+            rec = {"case": label, "class": cls, "vec_class": int(vec_ok), "M": M, "N": N, "K": K,
+                   "variant": info["name"], "variant_id": v, "parity": ok, "max_err_over_bound": ratio,
+                   "ms_median": med, "ms_min": ts[0], "reps": reps, "tflops": flops / (med * 1e-3) / 1e12}
+            results.append(rec)
+            log(f"   {info['name']:36s} {'ok ' if ok else 'BAD'} err/bound={ratio:.3g} "
+                f"median {med:.4f} ms  {rec['tflops']:.2f} TFLOP/s")
+        del dA, dB, dC, dC0
+        torch.cuda.empty_cache()
+
+    # choose winners
+    winners = {}
+    for cls in classes:
+        for vclass in (0, 1):
+            recs = [r for r in results if r["class"] == cls and r["vec_class"] == vclass]
+            if not recs:
+                continue
+            cases = sorted({r["case"] for r in recs})
+            best = {c: min(r["ms_median"] for r in recs if r["case"] == c and r["parity"]) for c in cases}
+            score = {}
+            for name in sorted({r["variant"] for r in recs}):
+                rs = {r["case"]: r for r in recs if r["variant"] == name}
+                if set(rs) != set(cases) or not all(r["parity"] for r in rs.values()):
+                    continue
+                # a vector-load class may also be served by a scalar-load variant, never the reverse
+                score[name] = math.exp(sum(math.log(rs[c]["ms_median"] / best[c]) for c in cases) / len(cases))
+            if score:
+                win = min(score, key=score.get)
+                winners[(cls, vclass)] = (win, score[win])
+                log(f"winner {cls}/{'vec' if vclass else 'scalar'}: {win} (geo-mean slowdown {score[win]:.3f})")
+    os.makedirs(os.path.dirname(args.out), exist_ok=True)
+    with open(args.out, "w") as f:
+        json.dump({"time": time.strftime("%Y-%m-%d %H:%M:%S"), "results": results,
+                   "winners": {f"{c}/{v}": w for (c, v), w in winners.items()}}, f, indent=1)
+    log(f"wrote {args.out}")
+    if args.write_table and winners:
+        write_table(winners)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
