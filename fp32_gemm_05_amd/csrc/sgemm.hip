@@ -45,6 +45,17 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+hipError_t launch_mfma_pipe(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = kGroupM;
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
 template <int BM, int BN, int BK, int TM, int TN, bool VEC>
 hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
@@ -70,6 +81,13 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 // vector-load form only, with an occupancy target of OCC waves per SIMD
 #define VEC_MFMA_OCC(BM, BN, BK, WM, WN, OCC) \
     MFMA_VARIANT(BM, BN, BK, WM, WN, OCC, true, MFMA_NAME(BM, BN, BK, WM, WN) "_o" #OCC "_vec")
+#define PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, NAME)                                       \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_pipe<BM, BN, BK, WM, WN, VEC, OCC>}
+#define PIPE_NAME(BM, BN, BK, WM, WN, OCC) "mfma32p_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_o" #OCC
+#define BOTH_PIPE(BM, BN, BK, WM, WN, OCC)                                                      \
+    PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, true, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_vec"),     \
+        PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, false, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_scalar")
 #define BOTH_VALU(BM, BN, BK, TM, TN) \
     VALU_VARIANT(BM, BN, BK, TM, TN, true, "_vec"), VALU_VARIANT(BM, BN, BK, TM, TN, false, "_scalar")
 
@@ -84,6 +102,10 @@ const Variant kVariants[] = {
     BOTH_MFMA(64, 64, 32, 32, 32),
     VEC_MFMA_OCC(128, 128, 16, 64, 64, 4),
     VEC_MFMA_OCC(128, 128, 32, 64, 64, 2),
+    BOTH_PIPE(128, 128, 32, 64, 64, 2),
+    BOTH_PIPE(256, 128, 16, 64, 64, 2),
+    BOTH_PIPE(64, 64, 16, 32, 32, 4),
+    BOTH_PIPE(256, 64, 16, 64, 64, 2),
     BOTH_VALU(128, 128, 8, 8, 8),
     BOTH_VALU(64, 64, 16, 4, 4),
 };

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace libsgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -81,12 +83,17 @@ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
 // padded pitch: A as [BM][BK + PA] (k contiguous) for the MFMA kernel.
 // ---------------------------------------------------------------------------------
 
-// Loader for a ROWS x COLS row-major panel of a matrix whose valid extent is
-// nrows x ncols.  `clamp_rows` selects what happens to rows past nrows: clamp
-// (true) or zero (false); columns past ncols are clamped when `clamp_cols`,
-// zero otherwise.  Vector form: one 16-byte load covers 4 consecutive columns
-// (needs ld % 4 == 0, ncols % 4 == 0 and a 16-byte aligned base).
-template <int ROWS, int COLS, int NT, bool VEC>
+// Loader of one operand's slab: a ROWS x COLS row-major panel, moved one slab
+// along K per call of advance().  KROWS selects which panel dimension runs
+// along K: false for A (the slab is BM rows x BK columns, K along columns),
+// true for B (BK rows x BN columns, K along rows).  The other dimension is
+// clamped once, at init, to the operand's last valid row/column (those lanes
+// feed only C elements that are never stored); elements past K are zero and
+// are checked only in the last, partial slab.  Vector form: one 16-byte load
+// covers 4 consecutive columns (needs ld % 4 == 0, ncols % 4 == 0 and a
+// 16-byte aligned base, which also make every 4-column group wholly inside or
+// outside K).
+template <int ROWS, int COLS, int NT, bool VEC, bool KROWS>
 struct PanelLoader {
     static constexpr int W = VEC ? 4 : 1;             // floats per load
     static constexpr int CPR = COLS / W;              // loads per panel row
@@ -96,40 +103,56 @@ struct PanelLoader {
     static_assert(NT % CPR == 0, "a load pass must cover whole panel rows");
     static constexpr int ROWS_PER_PASS = NT / CPR;
 
-    f32x4 v[L];  // only .x used when !VEC
-    int row0, col;  // this thread's first panel row and its column
+    f32x4 v[L];            // only .x used when !VEC
+    const float* p[L];     // address of this thread's l-th element/vector in the current slab
+    int row0, col;         // this thread's first panel row and its column (panel coordinates)
+    long step;             // address step from one slab to the next
 
-    __device__ inline void init(int tid) {
+    // The panel's top-left element is (r0, c0) of an nrows x ncols operand with leading dimension ld.
+    __device__ inline void init(int tid, const float* __restrict__ base, long ld, int r0, int c0, int nrows,
+                                int ncols, int bk) {
         row0 = tid / CPR;
         col = (tid % CPR) * W;
-    }
-
-    // Fetch the panel whose top-left element is (r0, c0) of the matrix.
-    template <bool CLAMP_ROWS, bool CLAMP_COLS>
-    __device__ inline void fetch(const float* __restrict__ base, long ld, int r0, int c0,
-                                 int nrows, int ncols) {
+        step = KROWS ? (long)bk * ld : (long)bk;
         int c = c0 + col;
-        bool cok = c < ncols;
-        if (CLAMP_COLS) {
-            c = imin(c, ncols - W);
-            cok = true;
-        }
+        if (KROWS) c = imin(c, ncols - W);  // B: clamp columns past N
 #pragma unroll
         for (int l = 0; l < L; ++l) {
             int r = r0 + row0 + l * ROWS_PER_PASS;
-            bool rok = r < nrows;
-            if (CLAMP_ROWS) {
-                r = imin(r, nrows - 1);
-                rok = true;
-            }
-            const float* p = base + (long)r * ld + c;
+            if (!KROWS) r = imin(r, nrows - 1);  // A: clamp rows past M
+            p[l] = base + (long)r * ld + c;
+        }
+    }
+
+    __device__ inline void advance() {
+#pragma unroll
+        for (int l = 0; l < L; ++l) p[l] += step;
+    }
+
+    // Position along K of the l-th element, relative to the slab start.
+    __device__ inline int kpos(int l) const { return KROWS ? row0 + l * ROWS_PER_PASS : col; }
+
+    // Fetch the current slab; with TAIL, elements whose K index (kbase + kpos) is >= K become zero.
+    template <bool TAIL>
+    __device__ inline void fetch(int kbase, int K) {
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const bool ok = !TAIL || kbase + kpos(l) < K;
             if (VEC) {
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                v[l] = (rok && cok) ? *reinterpret_cast<const f32x4*>(p) : z;
+                v[l] = ok ? *reinterpret_cast<const f32x4*>(p[l]) : z;
             } else {
-                v[l].x = (rok && cok) ? *p : 0.f;
+                v[l].x = ok ? *p[l] : 0.f;
             }
         }
+    }
+
+    // Fetch the slab starting at K index kbase (the pointers must already point at it).
+    __device__ inline void fetch_slab(int kbase, int bk, int K) {
+        if (kbase + bk <= K)
+            fetch<false>(kbase, K);
+        else
+            fetch<true>(kbase, K);
     }
 
     // Store into an LDS panel [ROWS][PITCH].
@@ -209,10 +232,11 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int wn0 = (wave % Cfg::WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
 
-    PanelLoader<BM, BK, NT, VEC> la;  // A slab: BM rows x BK columns of A
-    PanelLoader<BK, BN, NT, VEC> lb;  // B slab: BK rows x BN columns of B
-    la.init(tid);
-    lb.init(tid);
+    const int K = g.K;
+    PanelLoader<BM, BK, NT, VEC, false> la;  // A slab: BM rows x BK columns of A
+    PanelLoader<BK, BN, NT, VEC, true> lb;   // B slab: BK rows x BN columns of B
+    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
+    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -222,23 +246,27 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int K = g.K;
     const int nslab = (K + BK - 1) / BK;
+    const int nfull = K / BK;  // slabs with no element past K
 
-    // A: rows past M clamped, columns (k) past K zero.  B: rows (k) past K zero, columns past N clamped.
-    la.template fetch<true, false>(g.A, g.lda, m0, 0, g.M, K);
-    lb.template fetch<false, true>(g.B, g.ldb, 0, n0, K, g.N);
+    la.fetch_slab(0, BK, K);
+    lb.fetch_slab(0, BK, K);
     la.template store<AP>(lds_a);
     lb.template store<BP>(lds_b);
     __syncthreads();
 
-    for (int s = 0; s < nslab; ++s) {
+    // One slab: prefetch slab s+1 (PREFETCH 1: a full slab, 2: the partial last slab,
+    // 0: none), multiply slab s out of LDS, store the prefetched slab to the other stage.
+    auto slab = [&](int s, auto prefetch) {
+        constexpr int PREFETCH = decltype(prefetch)::value;
         const int cur = s & 1;
-        const bool more = s + 1 < nslab;
-        if (more) {
-            const int k1 = (s + 1) * BK;
-            la.template fetch<true, false>(g.A, g.lda, m0, k1, g.M, K);
-            lb.template fetch<false, true>(g.B, g.ldb, k1, n0, K, g.N);
+        if (PREFETCH != 0) {
+            la.advance();
+            lb.advance();
+            la.template fetch<PREFETCH == 2>((s + 1) * BK, K);
+            lb.template fetch<PREFETCH == 2>((s + 1) * BK, K);
+            // keep the prefetch at the top of the slab: its latency hides under the MFMAs below
+            __builtin_amdgcn_sched_barrier(0);
         }
         const float* sa = lds_a + cur * Cfg::A_STAGE;
         const float* sb = lds_b + cur * Cfg::B_STAGE;
@@ -262,14 +290,157 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
                     for (int j = 0; j < FN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][t], b[j][t], acc[i][j], 0, 0, 0);
         }
-        if (more) {
+        if (PREFETCH != 0) {
             la.template store<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
             lb.template store<BP>(lds_b + (cur ^ 1) * Cfg::B_STAGE);
         }
         __syncthreads();
-    }
+    };
+    int s = 0;
+    for (; s + 1 < nfull; ++s) slab(s, std::integral_constant<int, 1>{});
+    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{});
+    slab(s, std::integral_constant<int, 0>{});
 
     // Epilogue: C = alpha*acc + beta*C, C not read when beta == 0.
+    const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn0 + j * 32 + li;
+            if (col >= g.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm0 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                if (row < g.M) {
+                    float* pc = g.C + (long)row * g.ldc + col;
+                    float v = alpha * acc[i][j][r];
+                    if (beta != 0.f) v += beta * *pc;
+                    *pc = v;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Pipelined MFMA kernel: same tiling, operand mapping and LDS layout as
+// sgemm_mfma_kernel, with the LDS -> register fragments double-buffered:
+// while the MFMAs of one 8-deep group run, the fragments of the next group are
+// read; the next slab's first fragments are read right after the slab's barrier,
+// under the MFMAs of the current slab's last group.  One barrier per slab:
+//   store slab s+1 (registers -> LDS stage (s+1)&1); barrier; fetch slab s+2
+//   (global -> registers); read group 0 of slab s+1; MFMAs of slab s's last group.
+// Stage (s+1)&1 was last read during slab s-1, whose reads all completed before
+// the barrier of iteration s-1 (the barrier waits for outstanding LDS accesses).
+// ---------------------------------------------------------------------------------
+template <int FM, int FN>
+struct MfmaFrag {
+    f32x4 a[FM];
+    float b[FN][4];
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
+sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
+    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
+    constexpr int KK = BK / 8;
+    static_assert(KK % 2 == 0, "the fragment double buffer alternates per 8-deep group: BK must be 16 or 32");
+    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
+    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / Cfg::WAVES_N) * WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int K = g.K;
+    PanelLoader<BM, BK, NT, VEC, false> la;
+    PanelLoader<BK, BN, NT, VEC, true> lb;
+    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
+    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // per-lane offsets of the fragment reads inside one LDS stage
+    const int a_off = (wm0 + li) * AP + lh * 4;
+    const int b_off = (lh * 4) * BP + wn0 + li;
+
+    auto read_frag = [&](MfmaFrag<FM, FN>& f, const float* sa, const float* sb, int kk) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = *reinterpret_cast<const f32x4*>(sa + a_off + i * 32 * AP + kk * 8);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) f.b[j][t] = sb[b_off + (kk * 8 + t) * BP + j * 32];
+    };
+    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][t], f.b[j][t], acc[i][j], 0, 0, 0);
+    };
+
+    const int nslab = (K + BK - 1) / BK;
+
+    la.fetch_slab(0, BK, K);
+    lb.fetch_slab(0, BK, K);
+    la.template store<AP>(lds_a);
+    lb.template store<BP>(lds_b);
+    __syncthreads();
+    if (nslab > 1) {
+        la.advance();
+        lb.advance();
+        la.fetch_slab(BK, BK, K);
+        lb.fetch_slab(BK, BK, K);
+    }
+    MfmaFrag<FM, FN> F[2];
+    read_frag(F[0], lds_a, lds_b, 0);
+
+    for (int s = 0; s < nslab; ++s) {
+        const int cur = s & 1;
+        const float* sa = lds_a + cur * Cfg::A_STAGE;
+        const float* sb = lds_b + cur * Cfg::B_STAGE;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) {
+                read_frag(F[(kk + 1) & 1], sa, sb, kk + 1);
+            } else if (s + 1 < nslab) {
+                float* na = lds_a + (cur ^ 1) * Cfg::A_STAGE;
+                float* nb = lds_b + (cur ^ 1) * Cfg::B_STAGE;
+                la.template store<AP>(na);
+                lb.template store<BP>(nb);
+                __syncthreads();
+                if (s + 2 < nslab) {
+                    const int k2 = (s + 2) * BK;
+                    la.advance();
+                    lb.advance();
+                    la.fetch_slab(k2, BK, K);
+                    lb.fetch_slab(k2, BK, K);
+                }
+                read_frag(F[0], na, nb, 0);
+            }
+            mfma_frag(F[kk & 1]);
+        }
+    }
+
     const float alpha = g.alpha, beta = g.beta;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -325,10 +496,11 @@ sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int tid = threadIdx.x;
     const int tx = tid % Cfg::TX, ty = tid / Cfg::TX;
 
-    PanelLoader<BM, BK, NT, VEC> la;
-    PanelLoader<BK, BN, NT, VEC> lb;
-    la.init(tid);
-    lb.init(tid);
+    const int K = g.K;
+    PanelLoader<BM, BK, NT, VEC, false> la;
+    PanelLoader<BK, BN, NT, VEC, true> lb;
+    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
+    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
 
     float acc[TM][TN];
 #pragma unroll
@@ -336,21 +508,24 @@ sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 
-    const int K = g.K;
     const int nslab = (K + BK - 1) / BK;
-    la.template fetch<true, false>(g.A, g.lda, m0, 0, g.M, K);
-    lb.template fetch<false, true>(g.B, g.ldb, 0, n0, K, g.N);
+    const int nfull = K / BK;
+    la.fetch_slab(0, BK, K);
+    lb.fetch_slab(0, BK, K);
     la.template store_transposed<AP>(lds_a);
     lb.template store<BP>(lds_b);
     __syncthreads();
 
-    for (int s = 0; s < nslab; ++s) {
+    auto slab = [&](int s, auto prefetch) {
+        constexpr int PREFETCH = decltype(prefetch)::value;
         const int cur = s & 1;
-        const bool more = s + 1 < nslab;
-        if (more) {
-            const int k1 = (s + 1) * BK;
-            la.template fetch<true, false>(g.A, g.lda, m0, k1, g.M, K);
-            lb.template fetch<false, true>(g.B, g.ldb, k1, n0, K, g.N);
+        if (PREFETCH != 0) {
+            la.advance();
+            lb.advance();
+            la.template fetch<PREFETCH == 2>((s + 1) * BK, K);
+            lb.template fetch<PREFETCH == 2>((s + 1) * BK, K);
+            // keep the prefetch at the top of the slab: its latency hides under the MFMAs below
+            __builtin_amdgcn_sched_barrier(0);
         }
         const float* sa = lds_a + cur * Cfg::A_STAGE;
         const float* sb = lds_b + cur * Cfg::B_STAGE;
@@ -372,12 +547,16 @@ sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
         }
-        if (more) {
+        if (PREFETCH != 0) {
             la.template store_transposed<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
             lb.template store<BP>(lds_b + (cur ^ 1) * Cfg::B_STAGE);
         }
         __syncthreads();
-    }
+    };
+    int s = 0;
+    for (; s + 1 < nfull; ++s) slab(s, std::integral_constant<int, 1>{});
+    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{});
+    slab(s, std::integral_constant<int, 0>{});
 
     const float alpha = g.alpha, beta = g.beta;
 #pragma unroll

@@ -46,7 +46,7 @@ def test_version_and_variants():
     for i in range(n):
         info = sg.sgemm_variant_info(i)
         kinds.add(info["kind"])
-        assert info["name"].startswith("mfma32_" if info["kind"] == "mfma" else "valu_")
+        assert info["name"].startswith("mfma32" if info["kind"] == "mfma" else "valu_")
         assert f"{info['BM']}x{info['BN']}x{info['BK']}" in info["name"]
         assert info["name"].endswith("_vec") == bool(info["vec"])
         assert info["threads"] % 64 == 0 and info["threads"] <= 1024
