@@ -5,7 +5,7 @@ One step = one call of the library's ``sgemm`` on the whole workload (inputs
 resident in HBM before the timed region).  Default workload: M = N = K = 4096,
 A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload square4096]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
                     [--variant ID] [--no-cpu-baseline]
 
 FLOP count: 2*M*N*K per call (one multiply and one add per (i, j, k); the
@@ -47,7 +47,7 @@ def stored_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 12.0):
+def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0):
     """Time the float64 oracle on a bounded sample of the same workload (leading rows of C).
 
     The oracle's values on those rows also check the GPU output of the first call.
@@ -91,8 +91,9 @@ def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 12.0):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the engine clock ramps up over the first tens of milliseconds of sustained MFMA work
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant id (default: dispatch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -10,6 +10,15 @@
         HBM bytes per launch of one kernel from two --pmc runs, each scaled by the copy calibration.
     python -m fp32_gemm_05_amd.profiling counters <counter_collection.csv> --kernel SUBSTR --out X.md
         per-dispatch means of any collected counters for one kernel.
+    python -m fp32_gemm_05_amd.profiling report --dir D --workload W --out-dir profiles
+        one summary per (kernel, workload) from the runs the profiling commands below leave in D:
+          D/trace_W   rocprofv3 --kernel-trace --stats ... -- python bench.py --workload W --no-cpu-baseline
+          D/fetch_W   rocprofv3 --pmc FETCH_SIZE ...        -- python bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline
+          D/write_W   rocprofv3 --pmc WRITE_SIZE ...        (same bench command)
+          D/rdreq_W   rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum ...
+          D/sq_W      rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT
+                      SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE ...
+          D/copy_fetch, D/copy_write, D/copy_rdreq: the same counters over `profiling copy --mib 1024 --reps 3`
 
 No arithmetic of the GEMM lives here; this is measurement plumbing only.
 """
@@ -119,6 +128,125 @@ def cmd_counters(args) -> None:
     print(text)
 
 
+N_XCD, N_CU, N_SIMD = 8, 256, 1024  # MI355X
+
+
+def _stats_rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _mean_counter(path, substr, name):
+    return _mean(_read_counters(path, substr).get(name, []))
+
+
+def _workload_figures(workload):
+    from fp32_gemm_05_amd.workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    flops = 2.0 * w.M * w.N * w.K
+    alg_bytes = 4.0 * (w.M * w.K + w.K * w.N + (2 if w.beta != 0 else 1) * w.M * w.N)
+    return w, flops, alg_bytes
+
+
+def cmd_report(args) -> None:
+    d, W = args.dir, args.workload
+    w, flops, alg_bytes = _workload_figures(W)
+    rows = _stats_rows(os.path.join(d, f"trace_{W}", "run_kernel_stats.csv"))
+    kern = [r for r in rows if "sgemm" in r["Name"]]
+    if len(kern) != 1:
+        raise SystemExit(f"expected one sgemm kernel in the trace of {W}, found {len(kern)}")
+    k = kern[0]
+    name = k["Name"]
+    avg_ns = float(k["AverageNs"])
+    # the bench's timed region is its last `steps` launches (after the first call and the warmup)
+    with open(os.path.join(d, f"trace_{W}", "run_kernel_trace.csv")) as f:
+        disp = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in csv.DictReader(f)
+                if r["Kernel_Name"] == name]
+    timed = disp[-args.steps:]
+    timed_ns = _mean(timed)
+    # variant name from the kernel signature is not unique; take it from the bench log
+    variant = args.variant
+    sq = {c: _mean(v) for c, v in _read_counters(os.path.join(d, f"sq_{W}", "run_counter_collection.csv"), "sgemm").items()}
+    fetch = _mean_counter(os.path.join(d, f"fetch_{W}", "run_counter_collection.csv"), "sgemm", "FETCH_SIZE")
+    write = _mean_counter(os.path.join(d, f"write_{W}", "run_counter_collection.csv"), "sgemm", "WRITE_SIZE")
+    rd = {c: _mean(v) for c, v in _read_counters(os.path.join(d, f"rdreq_{W}", "run_counter_collection.csv"), "sgemm").items()}
+    cfetch = _mean_counter(os.path.join(d, "copy_fetch", "run_counter_collection.csv"), "copyBuffer", "FETCH_SIZE")
+    cwrite = _mean_counter(os.path.join(d, "copy_write", "run_counter_collection.csv"), "copyBuffer", "WRITE_SIZE")
+    copy_bytes = 1024.0 ** 3
+    f_scale = copy_bytes / (cfetch * 1024.0)
+    w_scale = copy_bytes / (cwrite * 1024.0)
+    hbm = fetch * 1024.0 * f_scale + write * 1024.0 * w_scale
+    rd_bytes = 32 * rd.get("TCC_EA0_RDREQ_32B_sum", 0.0) + 64 * rd.get("TCC_EA0_RDREQ_64B_sum", 0.0) + \
+        128 * rd.get("TCC_EA0_RDREQ_128B_sum", 0.0)
+    gui = sq.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
+    mfma_util = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (N_SIMD * gui)
+    lds_conf = sq.get("SQ_LDS_BANK_CONFLICT", float("nan")) / (N_CU * gui)
+    expect_mfma = w.M * w.N * w.K / 2048.0  # 32x32x2 MFMAs of the exact problem (no tile padding)
+    tflops = flops / (avg_ns * 1e-9) / 1e12
+    tflops_timed = flops / (timed_ns * 1e-9) / 1e12
+    bench = "python -u bench.py --workload %s" % W
+    cmds = [
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} --no-cpu-baseline",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
+        "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE, then the three TCC_EA0_RDREQ_*_sum) --output-format csv -d <dir>/copy_fetch (copy_write, copy_rdreq) -o run -- python -u -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3",
+        f"python -m fp32_gemm_05_amd.profiling report --dir <dir> --workload {W} --variant {variant} --out-dir profiles",
+    ]
+    lines = [
+        f"# `{variant}` on {W}", "",
+        f"Workload: {w.describe()}; {flops / 1e9:.2f} GFLOP and {alg_bytes / 1e6:.1f} MB of algorithmic traffic per call.",
+        f"Kernel: `{name}`", "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+        "| Dispatches | Mean duration | TFLOP/s | % of 157.3 |", "|---|---|---|---|",
+        f"| all {k['Calls']} (first call + warmup + timed; the --stats average) | {avg_ns / 1e3:.1f} us | "
+        f"{tflops:.1f} | {100 * tflops / 157.3:.1f} % |",
+        f"| the last {len(timed)} (the bench's timed region) | {timed_ns / 1e3:.1f} us | {tflops_timed:.1f} | "
+        f"{100 * tflops_timed / 157.3:.1f} % |", "",
+        f"Min {float(k['MinNs']) / 1e3:.1f} us, max {float(k['MaxNs']) / 1e3:.1f} us over all dispatches.", "",
+        "## Counters (means per dispatch)", "",
+        "| Counter | Value |", "|---|---|",
+    ]
+    for c in sorted(sq):
+        lines.append(f"| {c} | {sq[c]:.6g} |")
+    lines += [
+        f"| FETCH_SIZE (KiB) | {fetch:.6g} |", f"| WRITE_SIZE (KiB) | {write:.6g} |",
+    ]
+    for c in sorted(rd):
+        lines.append(f"| {c} | {rd[c]:.6g} |")
+    lines += [
+        "", "## Derived", "",
+        f"* MFMA instructions: {sq.get('SQ_INSTS_MFMA', float('nan')):.6g} (the problem needs M*N*K/2048 = "
+        f"{expect_mfma:.6g} v_mfma_f32_32x32x2_f32; the rest is tile padding at ragged edges)",
+        f"* MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) = {100 * mfma_util:.1f} %",
+        f"* LDS bank-conflict cycles per CU-cycle: SQ_LDS_BANK_CONFLICT / (256 CUs x GRBM_GUI_ACTIVE / 8) = "
+        f"{100 * lds_conf:.2f} %",
+        f"* Copy calibration: a {copy_bytes / 2**20:.0f} MiB device copy reads FETCH_SIZE {cfetch:.6g} KiB "
+        f"(scale {f_scale:.4f}) and writes WRITE_SIZE {cwrite:.6g} KiB (scale {w_scale:.4f})",
+        f"* HBM-side traffic per launch (copy-calibrated FETCH_SIZE + WRITE_SIZE): {hbm / 1e6:.1f} MB "
+        f"= {hbm / alg_bytes:.2f} x the algorithmic {alg_bytes / 1e6:.1f} MB",
+        f"* L2 read requests by size: {rd_bytes / 1e6:.1f} MB read (32/64/128 B requests counted at their size)",
+        "", "## Commands", "", "```", *cmds, "```", "",
+    ]
+    if args.note:
+        lines += [args.note, ""]
+    os.makedirs(args.out_dir, exist_ok=True)
+    base = f"{variant}__{W}"
+    with open(os.path.join(args.out_dir, base + ".md"), "w") as f:
+        f.write("\n".join(lines))
+    rec = {"workload": W, "variant": variant, "kernel": name, "avg_ns_all_dispatches": avg_ns,
+           "avg_ns_timed_region": timed_ns,
+           "FETCH_SIZE_KiB_per_launch": fetch, "WRITE_SIZE_KiB_per_launch": write,
+           "fetch_scale": f_scale, "write_scale": w_scale, "hbm_bytes_per_launch": hbm,
+           "l2_read_bytes_by_request_size": rd_bytes, "algorithmic_bytes_per_launch": alg_bytes,
+           "mfma_busy": mfma_util, "lds_bank_conflict_per_cu_cycle": lds_conf,
+           "kernel_source_hash": kernel_source_hash(), "commands": cmds}
+    with open(os.path.join(args.out_dir, f"traffic_{variant}_{W}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -151,8 +279,17 @@ def main(argv=None) -> int:
     p.add_argument("--command", required=True)
     p.add_argument("--note", default="")
     p.add_argument("--out", required=True)
+    p = sub.add_parser("report")
+    p.add_argument("--dir", required=True)
+    p.add_argument("--workload", required=True)
+    p.add_argument("--variant", required=True)
+    p.add_argument("--steps", type=int, default=200, help="timed steps of the traced bench run")
+    p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    p.add_argument("--note", default="")
     args = ap.parse_args(argv)
-    if args.cmd == "copy":
+    if args.cmd == "report":
+        cmd_report(args)
+    elif args.cmd == "copy":
         run_copy(args.mib, args.reps)
     elif args.cmd == "stats":
         cmd_stats(args)
