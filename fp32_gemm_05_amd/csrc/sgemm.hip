@@ -102,10 +102,12 @@ const Variant kVariants[] = {
     BOTH_MFMA(64, 64, 32, 32, 32),
     VEC_MFMA_OCC(128, 128, 16, 64, 64, 4),
     VEC_MFMA_OCC(128, 128, 32, 64, 64, 2),
-    BOTH_PIPE(128, 128, 32, 64, 64, 2),
+    PIPE_VARIANT(128, 128, 32, 64, 64, 2, true, PIPE_NAME(128, 128, 32, 64, 64, 2) "_vec"),
     BOTH_PIPE(256, 128, 16, 64, 64, 2),
     BOTH_PIPE(64, 64, 16, 32, 32, 4),
     BOTH_PIPE(256, 64, 16, 64, 64, 2),
+    PIPE_VARIANT(128, 256, 16, 64, 128, 2, true, PIPE_NAME(128, 256, 16, 64, 128, 2) "_vec"),
+    PIPE_VARIANT(256, 128, 16, 128, 64, 2, true, PIPE_NAME(256, 128, 16, 128, 64, 2) "_vec"),
     BOTH_VALU(128, 128, 8, 8, 8),
     BOTH_VALU(64, 64, 16, 4, 4),
 };

@@ -104,30 +104,32 @@ struct PanelLoader {
     static constexpr int ROWS_PER_PASS = NT / CPR;
 
     f32x4 v[L];            // only .x used when !VEC
-    const float* p[L];     // address of this thread's l-th element/vector in the current slab
+    const float* base;     // workgroup-uniform address of the current slab's first row/column
+    uint32_t off[L];       // this thread's BYTE offsets from base (same for every slab)
     int row0, col;         // this thread's first panel row and its column (panel coordinates)
     long step;             // address step from one slab to the next
 
-    // The panel's top-left element is (r0, c0) of an nrows x ncols operand with leading dimension ld.
-    __device__ inline void init(int tid, const float* __restrict__ base, long ld, int r0, int c0, int nrows,
+    // The panel's top-left element is (r0, c0) of an nrows x ncols operand with leading
+    // dimension ld.  Byte offsets are 32-bit (the load then takes the uniform base from
+    // scalar registers and only the offset from a vector register): the caller guarantees
+    // ((ROWS - 1) * ld + COLS) * 4 < 2^32.
+    __device__ inline void init(int tid, const float* __restrict__ op, long ld, int r0, int c0, int nrows,
                                 int ncols, int bk) {
         row0 = tid / CPR;
         col = (tid % CPR) * W;
         step = KROWS ? (long)bk * ld : (long)bk;
-        int c = c0 + col;
-        if (KROWS) c = imin(c, ncols - W);  // B: clamp columns past N
+        base = op + (long)r0 * ld + c0;
+        int c = col;
+        if (KROWS) c = imin(c0 + col, ncols - W) - c0;  // B: clamp columns past N
 #pragma unroll
         for (int l = 0; l < L; ++l) {
-            int r = r0 + row0 + l * ROWS_PER_PASS;
-            if (!KROWS) r = imin(r, nrows - 1);  // A: clamp rows past M
-            p[l] = base + (long)r * ld + c;
+            int r = row0 + l * ROWS_PER_PASS;
+            if (!KROWS) r = imin(r0 + r, nrows - 1) - r0;  // A: clamp rows past M
+            off[l] = (uint32_t)(((long)r * ld + c) * 4);
         }
     }
 
-    __device__ inline void advance() {
-#pragma unroll
-        for (int l = 0; l < L; ++l) p[l] += step;
-    }
+    __device__ inline void advance() { base += step; }
 
     // Position along K of the l-th element, relative to the slab start.
     __device__ inline int kpos(int l) const { return KROWS ? row0 + l * ROWS_PER_PASS : col; }
@@ -138,11 +140,16 @@ struct PanelLoader {
 #pragma unroll
         for (int l = 0; l < L; ++l) {
             const bool ok = !TAIL || kbase + kpos(l) < K;
+            // An empty asm statement that "redefines" the 32-bit offset keeps its zero extension
+            // inside the loop, where it folds into the load's scalar-base + 32-bit-offset form
+            // instead of becoming a 64-bit vector add per load and slab.
+            asm volatile("" : "+v"(off[l]));
+            const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + off[l]);
             if (VEC) {
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                v[l] = ok ? *reinterpret_cast<const f32x4*>(p[l]) : z;
+                v[l] = ok ? *reinterpret_cast<const f32x4*>(p) : z;
             } else {
-                v[l].x = ok ? *p[l] : 0.f;
+                v[l].x = ok ? *p : 0.f;
             }
         }
     }
@@ -257,9 +264,11 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 
     // One slab: prefetch slab s+1 (PREFETCH 1: a full slab, 2: the partial last slab,
     // 0: none), multiply slab s out of LDS, store the prefetched slab to the other stage.
-    auto slab = [&](int s, auto prefetch) {
+    // STAGE is s & 1 when known at compile time (the unrolled main loop), -1 otherwise.
+    auto slab = [&](int s, auto prefetch, auto stage) {
         constexpr int PREFETCH = decltype(prefetch)::value;
-        const int cur = s & 1;
+        constexpr int STAGE = decltype(stage)::value;
+        const int cur = STAGE >= 0 ? STAGE : (s & 1);
         if (PREFETCH != 0) {
             la.advance();
             lb.advance();
@@ -296,10 +305,17 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         }
         __syncthreads();
     };
+    using Full = std::integral_constant<int, 1>;
+    using Dyn = std::integral_constant<int, -1>;
     int s = 0;
-    for (; s + 1 < nfull; ++s) slab(s, std::integral_constant<int, 1>{});
-    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{});
-    slab(s, std::integral_constant<int, 0>{});
+    // main loop, two slabs per trip so that both LDS stage offsets are constants
+    for (; s + 2 < nfull; s += 2) {
+        slab(s, Full{}, std::integral_constant<int, 0>{});
+        slab(s + 1, Full{}, std::integral_constant<int, 1>{});
+    }
+    for (; s + 1 < nfull; ++s) slab(s, Full{}, Dyn{});
+    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{}, Dyn{});
+    slab(s, std::integral_constant<int, 0>{}, Dyn{});
 
     // Epilogue: C = alpha*acc + beta*C, C not read when beta == 0.
     const float alpha = g.alpha, beta = g.beta;
@@ -399,6 +415,7 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     };
 
     const int nslab = (K + BK - 1) / BK;
+    const int nfull = K / BK;
 
     la.fetch_slab(0, BK, K);
     lb.fetch_slab(0, BK, K);
@@ -414,7 +431,10 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     MfmaFrag<FM, FN> F[2];
     read_frag(F[0], lds_a, lds_b, 0);
 
-    for (int s = 0; s < nslab; ++s) {
+    // One slab.  MODE 0: s is the last slab; 1: slab s+1 exists and a full slab s+2 is
+    // prefetched; 2: the partial slab s+2 is prefetched; 3: slab s+1 exists, no s+2.
+    auto slab = [&](int s, auto mode) {
+        constexpr int MODE = decltype(mode)::value;
         const int cur = s & 1;
         const float* sa = lds_a + cur * Cfg::A_STAGE;
         const float* sb = lds_b + cur * Cfg::B_STAGE;
@@ -422,24 +442,29 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         for (int kk = 0; kk < KK; ++kk) {
             if (kk + 1 < KK) {
                 read_frag(F[(kk + 1) & 1], sa, sb, kk + 1);
-            } else if (s + 1 < nslab) {
+            } else if (MODE != 0) {
                 float* na = lds_a + (cur ^ 1) * Cfg::A_STAGE;
                 float* nb = lds_b + (cur ^ 1) * Cfg::B_STAGE;
                 la.template store<AP>(na);
                 lb.template store<BP>(nb);
                 __syncthreads();
-                if (s + 2 < nslab) {
-                    const int k2 = (s + 2) * BK;
+                if (MODE == 1 || MODE == 2) {
                     la.advance();
                     lb.advance();
-                    la.fetch_slab(k2, BK, K);
-                    lb.fetch_slab(k2, BK, K);
+                    la.template fetch<MODE == 2>((s + 2) * BK, K);
+                    lb.template fetch<MODE == 2>((s + 2) * BK, K);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 read_frag(F[0], na, nb, 0);
             }
             mfma_frag(F[kk & 1]);
         }
-    }
+    };
+    int s = 0;
+    for (; s + 2 < nfull; ++s) slab(s, std::integral_constant<int, 1>{});
+    for (; s + 2 < nslab; ++s) slab(s, std::integral_constant<int, 2>{});
+    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 3>{});
+    slab(s, std::integral_constant<int, 0>{});
 
     const float alpha = g.alpha, beta = g.beta;
 #pragma unroll

@@ -50,7 +50,22 @@ def log(msg):
     print(msg, flush=True)
 
 
+def read_table():
+    """Existing (class, vec) -> (variant, score) entries of the dispatch table."""
+    import re
+    out = {}
+    if os.path.exists(TABLE):
+        ids = {v: k for k, v in CLASS_IDS.items()}
+        for m in re.finditer(r'\{(k\w+), (\d), "([\w]+)"\},\s*//[^\n]*?([\d.]+)\s*$', open(TABLE).read(), re.M):
+            out[(ids[m.group(1)], int(m.group(2)))] = (m.group(3), float(m.group(4)))
+    return out
+
+
 def write_table(winners):
+    """Write the table: the new winners replace the entries of their classes, others are kept."""
+    merged = read_table()
+    merged.update(winners)
+    winners = merged
     lines = ["// Dispatch table: (shape class, vector-load eligibility) -> variant name.",
              "// Written by tests/autotune.py from timed, oracle-checked runs on MI355X",
              f"// ({time.strftime('%Y-%m-%d')}); each entry names the geometric-mean-fastest variant",
