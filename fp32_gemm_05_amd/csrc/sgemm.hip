@@ -28,52 +28,56 @@ struct Variant {
     int vec;
     int lds_bytes;
     LaunchFn launch;
+    int wide;  // 64-bit per-lane load offsets (no 4 GiB limit on one workgroup's operand span)
 };
 
 constexpr int kGroupM = 8;  // tile-rows per group of the workgroup -> tile map
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
 hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = kGroupM;
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE>),
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
 hipError_t launch_mfma_pipe(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = kGroupM;
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE>),
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
-template <int BM, int BN, int BK, int TM, int TN, bool VEC>
+template <int BM, int BN, int BK, int TM, int TN, bool VEC, bool WIDE>
 hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = kGroupM;
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_valu_kernel<BM, BN, BK, TM, TN, VEC>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_valu_kernel<BM, BN, BK, TM, TN, VEC, WIDE>),
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
 #define MFMA_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, NAME)                                       \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
-     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma<BM, BN, BK, WM, WN, VEC, OCC>}
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma<BM, BN, BK, WM, WN, VEC, OCC, false>, 0}
+#define WIDE_MFMA_VARIANT(BM, BN, BK, WM, WN, VEC, NAME)                                         \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, true>, 1}
 #define VALU_VARIANT(BM, BN, BK, TM, TN, VEC, SUFFIX)                                             \
     {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN SUFFIX, kValu, BM, BN, BK, TM, TN,              \
      ValuCfg<BM, BN, BK, TM, TN, VEC>::NT, VEC, ValuCfg<BM, BN, BK, TM, TN, VEC>::LDS_BYTES,     \
-     &launch_valu<BM, BN, BK, TM, TN, VEC>}
+     &launch_valu<BM, BN, BK, TM, TN, VEC, false>, 0}
 #define MFMA_NAME(BM, BN, BK, WM, WN) "mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
 #define BOTH_MFMA(BM, BN, BK, WM, WN)                                                       \
     MFMA_VARIANT(BM, BN, BK, WM, WN, 0, true, MFMA_NAME(BM, BN, BK, WM, WN) "_vec"),        \
@@ -83,7 +87,7 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     MFMA_VARIANT(BM, BN, BK, WM, WN, OCC, true, MFMA_NAME(BM, BN, BK, WM, WN) "_o" #OCC "_vec")
 #define PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, NAME)                                       \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
-     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_pipe<BM, BN, BK, WM, WN, VEC, OCC>}
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_pipe<BM, BN, BK, WM, WN, VEC, OCC, false>, 0}
 #define PIPE_NAME(BM, BN, BK, WM, WN, OCC) "mfma32p_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_o" #OCC
 #define BOTH_PIPE(BM, BN, BK, WM, WN, OCC)                                                      \
     PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, true, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_vec"),     \
@@ -110,6 +114,9 @@ const Variant kVariants[] = {
     PIPE_VARIANT(256, 128, 16, 128, 64, 2, true, PIPE_NAME(256, 128, 16, 128, 64, 2) "_vec"),
     BOTH_VALU(128, 128, 8, 8, 8),
     BOTH_VALU(64, 64, 16, 4, 4),
+    // 64-bit offsets: used whenever one workgroup's operand span does not fit 32-bit offsets
+    WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, true, MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec"),
+    WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, false, MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -160,6 +167,21 @@ bool vec_ok(int N, int K, const float* A, int lda, const float* B, int ldb, cons
            (ldc % 4 == 0) && (K % 4 == 0) && (N % 4 == 0);
 }
 
+// Do one workgroup's A and B panels fit 32-bit per-lane byte offsets? (narrow variants only)
+bool offsets_fit(const Variant& v, int lda, int ldb) {
+    if (v.wide) return true;
+    const unsigned long long lim = 1ull << 32;
+    const unsigned long long a = ((unsigned long long)(v.bm - 1) * (unsigned)lda + (unsigned)v.bk) * 4ull;
+    const unsigned long long b = ((unsigned long long)(v.bk - 1) * (unsigned)ldb + (unsigned)v.bn) * 4ull;
+    return a < lim && b < lim;
+}
+
+int wide_fallback(bool vec) {
+    static const int ids[2] = {find_variant(MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
+                               find_variant(MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec")};
+    return ids[vec ? 1 : 0];
+}
+
 int shape_class(int M, int N) {
     if (N <= 64) return kSkinny;
     long tiles128 = (long)ceil_div(M, 128) * ceil_div(N, 128);
@@ -170,7 +192,8 @@ int shape_class(int M, int N) {
 int select_variant(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
                    int ldc) {
     const bool v = vec_ok(N, K, A, lda, B, ldb, C, ldc);
-    return dispatch_table().id[shape_class(M, N)][v ? 1 : 0];
+    const int id = dispatch_table().id[shape_class(M, N)][v ? 1 : 0];
+    return offsets_fit(kVariants[id], lda, ldb) ? id : wide_fallback(v);
 }
 
 // Argument checks shared by every computing entry point.  Returns 0 or -i.
@@ -225,6 +248,7 @@ int run(int M, int N, int K, float alpha, const float* A, int lda, const float* 
     }
     const Variant& v = kVariants[variant];
     if (v.vec && !vec_ok(N, K, A, lda, B, ldb, C, ldc)) return -13;
+    if (!offsets_fit(v, lda, ldb)) return -13;
     const long tiles = (long)ceil_div(M, v.bm) * (long)ceil_div(N, v.bn);
     if (tiles > INT_MAX) return -1;
     GemmArgs g{M, N, K, alpha, beta, A, (long)lda, B, (long)ldb, C, (long)ldc};
@@ -265,6 +289,7 @@ int sgemm_variant_info(int variant, int* info, int n) {
     info[6] = v.threads;
     info[7] = v.vec;
     info[8] = v.lds_bytes;
+    if (n >= 10) info[9] = v.wide;
     return 0;
 }
 

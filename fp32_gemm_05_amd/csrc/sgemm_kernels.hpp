@@ -92,9 +92,11 @@ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
 // are checked only in the last, partial slab.  Vector form: one 16-byte load
 // covers 4 consecutive columns (needs ld % 4 == 0, ncols % 4 == 0 and a
 // 16-byte aligned base, which also make every 4-column group wholly inside or
-// outside K).
-template <int ROWS, int COLS, int NT, bool VEC, bool KROWS>
+// outside K).  Per-lane offsets are 32-bit unless WIDE (64-bit, for leading
+// dimensions so large that one workgroup's panel spans 4 GiB or more).
+template <int ROWS, int COLS, int NT, bool VEC, bool KROWS, bool WIDE>
 struct PanelLoader {
+    using OffT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
     static constexpr int W = VEC ? 4 : 1;             // floats per load
     static constexpr int CPR = COLS / W;              // loads per panel row
     static constexpr int L = ROWS * CPR / NT;         // loads per thread
@@ -105,14 +107,14 @@ struct PanelLoader {
 
     f32x4 v[L];            // only .x used when !VEC
     const float* base;     // workgroup-uniform address of the current slab's first row/column
-    uint32_t off[L];       // this thread's BYTE offsets from base (same for every slab)
+    OffT off[L];           // this thread's BYTE offsets from base (same for every slab)
     int row0, col;         // this thread's first panel row and its column (panel coordinates)
     long step;             // address step from one slab to the next
 
     // The panel's top-left element is (r0, c0) of an nrows x ncols operand with leading
-    // dimension ld.  Byte offsets are 32-bit (the load then takes the uniform base from
-    // scalar registers and only the offset from a vector register): the caller guarantees
-    // ((ROWS - 1) * ld + COLS) * 4 < 2^32.
+    // dimension ld.  Unless WIDE, byte offsets are 32-bit (the load then takes the uniform
+    // base from scalar registers and only the offset from a vector register): the caller
+    // guarantees ((ROWS - 1) * ld + COLS) * 4 < 2^32.
     __device__ inline void init(int tid, const float* __restrict__ op, long ld, int r0, int c0, int nrows,
                                 int ncols, int bk) {
         row0 = tid / CPR;
@@ -125,7 +127,7 @@ struct PanelLoader {
         for (int l = 0; l < L; ++l) {
             int r = row0 + l * ROWS_PER_PASS;
             if (!KROWS) r = imin(r0 + r, nrows - 1) - r0;  // A: clamp rows past M
-            off[l] = (uint32_t)(((long)r * ld + c) * 4);
+            off[l] = (OffT)(((long)r * ld + c) * 4);
         }
     }
 
@@ -143,7 +145,7 @@ struct PanelLoader {
             // An empty asm statement that "redefines" the 32-bit offset keeps its zero extension
             // inside the loop, where it folds into the load's scalar-base + 32-bit-offset form
             // instead of becoming a 64-bit vector add per load and slab.
-            asm volatile("" : "+v"(off[l]));
+            if (!WIDE) asm volatile("" : "+v"(off[l]));
             const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + off[l]);
             if (VEC) {
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -220,7 +222,7 @@ struct MfmaCfg {
 
 // OCC > 0 asks the compiler for at least OCC waves per SIMD (registers capped at 512 / OCC),
 // so that OCC workgroups of 4 waves fit on one CU.
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -240,8 +242,8 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int li = lane & 31, lh = lane >> 5;
 
     const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false> la;  // A slab: BM rows x BK columns of A
-    PanelLoader<BK, BN, NT, VEC, true> lb;   // B slab: BK rows x BN columns of B
+    PanelLoader<BM, BK, NT, VEC, false, WIDE> la;  // A slab: BM rows x BK columns of A
+    PanelLoader<BK, BN, NT, VEC, true, WIDE> lb;   // B slab: BK rows x BN columns of B
     la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
     lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
 
@@ -356,7 +358,7 @@ struct MfmaFrag {
     float b[FN][4];
 };
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -378,8 +380,8 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int li = lane & 31, lh = lane >> 5;
 
     const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false> la;
-    PanelLoader<BK, BN, NT, VEC, true> lb;
+    PanelLoader<BM, BK, NT, VEC, false, WIDE> la;
+    PanelLoader<BK, BN, NT, VEC, true, WIDE> lb;
     la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
     lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
 
@@ -433,9 +435,10 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 
     // One slab.  MODE 0: s is the last slab; 1: slab s+1 exists and a full slab s+2 is
     // prefetched; 2: the partial slab s+2 is prefetched; 3: slab s+1 exists, no s+2.
-    auto slab = [&](int s, auto mode) {
+    auto slab = [&](int s, auto mode, auto stage) {
         constexpr int MODE = decltype(mode)::value;
-        const int cur = s & 1;
+        constexpr int STAGE = decltype(stage)::value;  // s & 1 when known at compile time, else -1
+        const int cur = STAGE >= 0 ? STAGE : (s & 1);
         const float* sa = lds_a + cur * Cfg::A_STAGE;
         const float* sb = lds_b + cur * Cfg::B_STAGE;
 #pragma unroll
@@ -460,11 +463,16 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             mfma_frag(F[kk & 1]);
         }
     };
+    using Dyn = std::integral_constant<int, -1>;
     int s = 0;
-    for (; s + 2 < nfull; ++s) slab(s, std::integral_constant<int, 1>{});
-    for (; s + 2 < nslab; ++s) slab(s, std::integral_constant<int, 2>{});
-    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 3>{});
-    slab(s, std::integral_constant<int, 0>{});
+    for (; s + 3 < nfull; s += 2) {  // two slabs per trip: constant LDS stage offsets
+        slab(s, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+        slab(s + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    }
+    for (; s + 2 < nfull; ++s) slab(s, std::integral_constant<int, 1>{}, Dyn{});
+    for (; s + 2 < nslab; ++s) slab(s, std::integral_constant<int, 2>{}, Dyn{});
+    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 3>{}, Dyn{});
+    slab(s, std::integral_constant<int, 0>{}, Dyn{});
 
     const float alpha = g.alpha, beta = g.beta;
 #pragma unroll
@@ -506,7 +514,7 @@ struct ValuCfg {
     static_assert(BM % TM == 0 && BN % TN == 0, "tiling");
 };
 
-template <int BM, int BN, int BK, int TM, int TN, bool VEC>
+template <int BM, int BN, int BK, int TM, int TN, bool VEC, bool WIDE>
 __global__ void __launch_bounds__((ValuCfg<BM, BN, BK, TM, TN, VEC>::NT))
 sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
@@ -522,8 +530,8 @@ sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int tx = tid % Cfg::TX, ty = tid / Cfg::TX;
 
     const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false> la;
-    PanelLoader<BK, BN, NT, VEC, true> lb;
+    PanelLoader<BM, BK, NT, VEC, false, WIDE> la;
+    PanelLoader<BK, BN, NT, VEC, true, WIDE> lb;
     la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
     lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
 

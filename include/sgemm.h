@@ -71,10 +71,15 @@ SGEMM_API int sgemm(int M, int N, int K, float alpha,
 
 /* As sgemm, with the kernel variant forced (0 <= variant < sgemm_num_variants()),
  * or chosen as sgemm does when variant < 0.  Returns -13 when the id is out of
- * range or the variant's precondition fails (vector variants need A, B and C
- * 16-byte aligned, lda, ldb, ldc, K and N multiples of 4).  The operation
- * performed is the same for every variant; only speed and fp32 rounding order
- * differ.  Used by the autotuner, the bench and the tests. */
+ * range or a precondition of the variant fails:
+ *   - vector variants ("_vec") need A, B and C 16-byte aligned and lda, ldb,
+ *     ldc, K and N multiples of 4;
+ *   - variants other than "_wide" ones address one workgroup's operand panels
+ *     with 32-bit offsets and need ((BM-1)*lda + BK)*4 < 2^32 and
+ *     ((BK-1)*ldb + BN)*4 < 2^32 (sgemm itself switches to a "_wide" variant
+ *     when these fail, so it has no such limit).
+ * The operation performed is the same for every variant; only speed and fp32
+ * rounding order differ.  Used by the autotuner, the bench and the tests. */
 SGEMM_API int sgemm_ex(int M, int N, int K, float alpha,
                        const float *A, int lda,
                        const float *B, int ldb,
@@ -91,7 +96,7 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   info[0] kind (0 = MFMA 32x32x2 f32, 1 = vector FMA), info[1] BM, info[2] BN,
  *   info[3] BK, info[4] WM (MFMA wave tile rows) or TM (VALU microtile rows),
  *   info[5] WN or TN, info[6] threads per workgroup, info[7] vector loads (0/1),
- *   info[8] LDS bytes per workgroup.
+ *   info[8] LDS bytes per workgroup, and when n >= 10, info[9] 64-bit offsets (0/1).
  * Returns 0, or -1 for a bad id or n < 9. */
 SGEMM_API int sgemm_variant_info(int variant, int *info, int n);
 

@@ -142,3 +142,20 @@ def test_tile_order_gives_each_xcd_a_compact_block():
         rows = {tm[w] for w in ws}
         cols = {tn[w] for w in ws}
         assert len(rows) * len(cols) <= 2 * len(ws), (x, len(rows), len(cols))
+
+
+def test_huge_leading_dimension_uses_wide_offsets():
+    """A workgroup panel spanning >= 4 GiB cannot use 32-bit offsets: sgemm picks a _wide variant,
+    and a forced narrow variant is refused before any launch."""
+    lda = 20_000_000  # (64 - 1) * lda * 4 bytes > 2^32
+    vid = sg.sgemm_select_variant(200, 64, 64, FAKE_A, lda, FAKE_B, 64, FAKE_C, 64)
+    info = sg.sgemm_variant_info(vid)
+    assert info["wide"] == 1 and info["name"].endswith("_wide_vec")
+    narrow = [i for i in range(sg.sgemm_num_variants())
+              if not sg.sgemm_variant_info(i)["wide"] and sg.sgemm_variant_info(i)["BM"] >= 64]
+    big_a = 0x100000000  # far from C, so no overlap
+    for v in narrow:
+        assert _call(200, 64, 64, lda, 64, 64, A=big_a, variant=v) == -13
+    # an ordinary leading dimension keeps the narrow variant
+    vid = sg.sgemm_select_variant(4096, 4096, 4096, FAKE_A, 4096, FAKE_B, 4096, FAKE_C, 4096)
+    assert sg.sgemm_variant_info(vid)["wide"] == 0

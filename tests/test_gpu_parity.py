@@ -273,6 +273,28 @@ def test_error_codes_no_launch():
     assert e.value.code == -13
 
 
+def test_huge_leading_dimension_wide_variant():
+    """lda = 20,000,000 (a 12 GB strided A): the workgroup panel spans more than 4 GiB, so the
+    dispatcher must use 64-bit offsets; the result must still match the oracle exactly."""
+    w = WORKLOADS["square1024_beta"].as_int()
+    M, N, K, lda = 150, 64, 68, 20_000_000
+    A, B, C = make_inputs(w, M=M, N=N, K=K)
+    bufA = torch.empty(M * lda, dtype=torch.float32, device="cuda")
+    vA = bufA.as_strided((M, K), (lda, 1))
+    vA.copy_(torch.from_numpy(A))
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.from_numpy(C).cuda()
+    vid = sg.sgemm_select_variant(M, N, K, vA, lda, dB, N, dC, N)
+    assert sg.sgemm_variant_info(vid)["wide"] == 1
+    _say(f"[huge-ld] variant={sg.sgemm_variant_name(vid)}")
+    sg.sgemm(M, N, K, 1.0, vA, lda, dB, N, 0.5, dC, N)
+    torch.cuda.synchronize()
+    ref, _ = oracle.ref_rows(A, B, C, 1.0, 0.5)
+    check_exact(dC.cpu().numpy(), ref, "huge lda")
+    del bufA, vA
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------------------------------
 # self-consistency: scaling, determinism, streams, transpose identity
 # ------------------------------------------------------------------------------------------
