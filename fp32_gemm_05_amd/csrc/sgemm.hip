@@ -121,7 +121,7 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Shape classes of the dispatch table.
-enum ShapeClass { kSkinny = 0, kSmall = 1, kLarge = 2, kNumClasses = 3 };
+enum ShapeClass { kSkinny = 0, kSmall = 1, kLarge = 2, kHuge = 3, kNumClasses = 4 };
 
 struct TableEntry {
     int shape_class;
@@ -182,11 +182,14 @@ int wide_fallback(bool vec) {
     return ids[vec ? 1 : 0];
 }
 
+// skinny: N <= 64; small: fewer than 256 output tiles of 128x128 (under one per CU);
+// large: up to 2048 such tiles; huge: more.
 int shape_class(int M, int N) {
     if (N <= 64) return kSkinny;
     long tiles128 = (long)ceil_div(M, 128) * ceil_div(N, 128);
     if (tiles128 < 256) return kSmall;
-    return kLarge;
+    if (tiles128 < 2048) return kLarge;
+    return kHuge;
 }
 
 int select_variant(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,

@@ -198,9 +198,13 @@ struct PanelLoader {
 // ---------------------------------------------------------------------------------
 // MFMA kernel: v_mfma_f32_32x32x2_f32, wave tile WM x WN of 32x32 blocks.
 //
-// Operand mapping of one 32x32x2 step (lane l, h = l / 32, i = l % 32):
-//   A operand: lane l supplies A(i, kA(h)), B operand: lane l supplies B(kB(h), i)
-//   accumulator register r of lane l holds D(8*(r/4) + 4*h + r%4, i).
+// One 32x32x2 step computes D += X * Y where lane l (h = l / 32, i = l % 32)
+// supplies X(i, h) and Y(h, i), and accumulator register r of lane l holds
+// D(8*(r/4) + 4*h + r%4, i).  In the 128-bit variants each 32x32 block of C is
+// accumulated transposed: X is fed from B (X(i, h) = B(k(h), n0 + i)) and Y from A
+// (Y(h, i) = A(m0 + i, k(h))), so D = (A B)^T and register r of lane l holds
+// C(m0 + i, n0 + 8*(r/4) + 4*h + r%4): every group of four registers is four
+// consecutive columns of one row of C, written back with a single 128-bit store.
 // Within one 8-deep group of a slab, step s in 0..3 takes k = 4*h + s for half h,
 // so a lane's four A values are contiguous in the k-major LDS slab (one 128-bit
 // LDS read) and the 8 k's of the group are each used exactly once.
@@ -222,6 +226,71 @@ struct MfmaCfg {
 
 // OCC > 0 asks the compiler for at least OCC waves per SIMD (registers capped at 512 / OCC),
 // so that OCC workgroups of 4 waves fit on one CU.
+// One 32x32x2 step on a block.  TRANS (used by the 128-bit variants) accumulates the block
+// transposed, as described above; otherwise X comes from A and Y from B, D = A B, and register
+// r of lane l holds C(m0 + 8*(r/4) + 4*h + r%4, n0 + i): lanes run along a row of C, which
+// keeps the 32-bit stores of the unaligned variants coalesced.
+template <bool TRANS>
+__device__ __attribute__((always_inline)) inline f32x16 mfma_step(float a, float b, const f32x16& c) {
+    return TRANS ? __builtin_amdgcn_mfma_f32_32x32x2f32(b, a, c, 0, 0, 0)
+                 : __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Epilogue of the MFMA kernels: C = alpha*acc + beta*C (C not read when beta == 0) for a
+// wave whose tile starts at (m_base, n_base).  The 128-bit variants hold blocks transposed
+// (four consecutive columns per four registers: one 128-bit store); the others hold them
+// upright (32 lanes along a row: coalesced 32-bit stores).
+// (Scalars are passed by value: taking the argument struct by reference makes the compiler
+// keep an addressable copy of it, which it may place in LDS.)
+template <int FM, int FN, bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N, float alpha, float beta,
+                                                                    float* __restrict__ C, long ldc,
+                                                                    const f32x16 (&acc)[FM][FN], int m_base,
+                                                                    int n_base, int li, int lh) {
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = m_base + i * 32 + li;
+            if (row >= M) continue;
+            float* prow = C + (long)row * ldc;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // N % 4 == 0 and col % 4 == 0: the 4 columns are all inside or all outside
+                    const int col = n_base + j * 32 + q * 8 + lh * 4;
+                    if (col >= N) continue;
+                    f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                               acc[i][j][4 * q + 3]};
+                    v *= alpha;
+                    f32x4* pc = reinterpret_cast<f32x4*>(prow + col);
+                    if (beta != 0.f) v += beta * *pc;
+                    *pc = v;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n_base + j * 32 + li;
+                if (col >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m_base + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                    if (row < M) {
+                        float* pc = C + (long)row * ldc + col;
+                        float x = alpha * acc[i][j][r];
+                        if (beta != 0.f) x += beta * *pc;
+                        *pc = x;
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
@@ -299,7 +368,7 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][t], b[j][t], acc[i][j], 0, 0, 0);
+                        acc[i][j] = mfma_step<VEC>(a[i][t], b[j][t], acc[i][j]);
         }
         if (PREFETCH != 0) {
             la.template store<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
@@ -319,26 +388,7 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{}, Dyn{});
     slab(s, std::integral_constant<int, 0>{}, Dyn{});
 
-    // Epilogue: C = alpha*acc + beta*C, C not read when beta == 0.
-    const float alpha = g.alpha, beta = g.beta;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn0 + j * 32 + li;
-            if (col >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm0 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                if (row < g.M) {
-                    float* pc = g.C + (long)row * g.ldc + col;
-                    float v = alpha * acc[i][j][r];
-                    if (beta != 0.f) v += beta * *pc;
-                    *pc = v;
-                }
-            }
-        }
-    }
+    mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
 }
 
 // ---------------------------------------------------------------------------------
@@ -413,7 +463,7 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][t], f.b[j][t], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
     };
 
     const int nslab = (K + BK - 1) / BK;
@@ -474,25 +524,7 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 3>{}, Dyn{});
     slab(s, std::integral_constant<int, 0>{}, Dyn{});
 
-    const float alpha = g.alpha, beta = g.beta;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn0 + j * 32 + li;
-            if (col >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm0 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                if (row < g.M) {
-                    float* pc = g.C + (long)row * g.ldc + col;
-                    float v = alpha * acc[i][j][r];
-                    if (beta != 0.f) v += beta * *pc;
-                    *pc = v;
-                }
-            }
-        }
-    }
+    mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
 }
 
 // ---------------------------------------------------------------------------------

@@ -34,7 +34,9 @@ TABLE = os.path.join(ROOT, "fp32_gemm_05_amd", "csrc", "tuned_table.inc")
 # (label, shape class, workload name or None, M, N, K, dist, alpha, beta, vector-load eligible)
 CASES = [
     ("square4096", "large", "square4096", None, None, None, None, None, None, True),
-    ("square8192", "large", "square8192", None, None, None, None, None, None, True),
+    ("square8192", "huge", "square8192", None, None, None, None, None, None, True),
+    ("square6144", "huge", "square4096", 6144, 6144, 6144, None, None, None, True),
+    ("ragged8191x8190x2047", "huge", "ragged3001x5003x777", 8191, 8190, 2047, None, None, None, False),
     ("ragged3001x5003x777", "large", "ragged3001x5003x777", None, None, None, None, None, None, False),
     ("square4096_odd_ld", "large", "square4096", 4096, 4095, 4095, "uniform", 1.0, 0.0, False),
     ("square256", "small", "square256", None, None, None, None, None, None, True),
@@ -43,7 +45,7 @@ CASES = [
     ("skinny65536x64x1024", "skinny", "skinny65536x64x1024", None, None, None, None, None, None, True),
     ("skinny65536x61x1021", "skinny", "skinny65536x64x1024", 65536, 61, 1021, None, None, None, False),
 ]
-CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge"}
+CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge"}
 
 
 def log(msg):
@@ -83,7 +85,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
     ap.add_argument("--write-table", action="store_true")
-    ap.add_argument("--classes", default="large,small,skinny")
+    ap.add_argument("--classes", default="large,huge,small,skinny")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--table-from", default=None, help="write the table from a saved results file (no GPU)")

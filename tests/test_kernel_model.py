@@ -87,7 +87,12 @@ def stored_elements(v, M, N):
         li, lh = lane % 32, lane // 32
         local = []
         for i, j, r in itertools.product(range(WM // 32), range(WN // 32), range(16)):
-            local.append((wm0 + i * 32 + (r // 4) * 8 + lh * 4 + (r % 4), wn0 + j * 32 + li))
+            if v["vec"]:
+                # blocks accumulated transposed: register r holds row li, column 8*(r/4) + 4*lh + r%4
+                local.append((wm0 + i * 32 + li, wn0 + j * 32 + (r // 4) * 8 + lh * 4 + (r % 4)))
+            else:
+                # upright blocks: register r holds row 8*(r/4) + 4*lh + r%4, column li
+                local.append((wm0 + i * 32 + (r // 4) * 8 + lh * 4 + (r % 4), wn0 + j * 32 + li))
     else:
         TM, TN = v["WM_or_TM"], v["WN_or_TN"]
         TX = BN // TN
