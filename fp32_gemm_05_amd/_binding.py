@@ -116,10 +116,10 @@ def sgemm_variant_name(variant: int):
 
 
 def sgemm_variant_info(variant: int) -> dict:
-    info = (ctypes.c_int * 10)()
-    if load_library().sgemm_variant_info(int(variant), info, 10) != 0:
+    info = (ctypes.c_int * 11)()
+    if load_library().sgemm_variant_info(int(variant), info, 11) != 0:
         raise ValueError(f"no variant {variant}")
-    keys = ["kind", "BM", "BN", "BK", "WM_or_TM", "WN_or_TN", "threads", "vec", "lds_bytes", "wide"]
+    keys = ["kind", "BM", "BN", "BK", "WM_or_TM", "WN_or_TN", "threads", "vec", "lds_bytes", "wide", "ksplit"]
     d = dict(zip(keys, list(info)))
     d["kind"] = "mfma" if d["kind"] == 0 else "valu"
     d["name"] = sgemm_variant_name(variant)

@@ -29,6 +29,7 @@ struct Variant {
     int lds_bytes;
     LaunchFn launch;
     int wide;  // 64-bit per-lane load offsets (no 4 GiB limit on one workgroup's operand span)
+    int ks;    // k-groups sharing one tile inside a workgroup (split-K); 0 means 1
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -61,6 +62,17 @@ hipError_t launch_mfma_pipe(const GemmArgs& g, hipStream_t stream) {
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
     return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool VEC>
+hipError_t launch_mfma_splitk(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_splitk_kernel<BM, BN, BK, WM, WN, KS, VEC>),
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
@@ -99,6 +111,13 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define BOTH_PIPE(BM, BN, BK, WM, WN, OCC)                                                      \
     PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, true, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_vec"),     \
         PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, false, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_scalar")
+#define SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, VEC, NAME)                                     \
+    {NAME, kMfma, BM, BN, BK, WM, WN, SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>::NT, VEC,            \
+     SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>::LDS_BYTES, &launch_mfma_splitk<BM, BN, BK, WM, WN, KS, VEC>, 0, KS}
+#define SPLITK_NAME(BM, BN, BK, WM, WN, KS) "mfma32k" #KS "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
+#define BOTH_SPLITK(BM, BN, BK, WM, WN, KS)                                                     \
+    SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, true, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_vec"),   \
+        SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, false, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_scalar")
 #define BOTH_VALU(BM, BN, BK, TM, TN) \
     VALU_VARIANT(BM, BN, BK, TM, TN, true, "_vec"), VALU_VARIANT(BM, BN, BK, TM, TN, false, "_scalar")
 
@@ -119,6 +138,12 @@ const Variant kVariants[] = {
     BOTH_PIPE(256, 64, 16, 64, 64, 2),
     PIPE_VARIANT(128, 256, 16, 64, 128, 2, true, PIPE_NAME(128, 256, 16, 64, 128, 2) "_vec"),
     PIPE_VARIANT(256, 128, 16, 128, 64, 2, true, PIPE_NAME(256, 128, 16, 128, 64, 2) "_vec"),
+    BOTH_SPLITK(64, 64, 32, 32, 32, 2),
+    BOTH_SPLITK(64, 64, 32, 32, 32, 4),
+    BOTH_MFMA(64, 64, 64, 32, 32),
+    BOTH_MFMA(128, 64, 32, 64, 64),
+    BOTH_MFMA(128, 64, 64, 64, 64),
+    BOTH_MFMA(64, 64, 32, 64, 32),
     BOTH_VALU(128, 128, 8, 8, 8),
     BOTH_VALU(64, 64, 16, 4, 4),
     // 64-bit offsets: used whenever one workgroup's operand span does not fit 32-bit offsets
@@ -300,6 +325,7 @@ int sgemm_variant_info(int variant, int* info, int n) {
     info[7] = v.vec;
     info[8] = v.lds_bytes;
     if (n >= 10) info[9] = v.wide;
+    if (n >= 11) info[10] = v.ks > 1 ? v.ks : 1;
     return 0;
 }
 

@@ -96,7 +96,8 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   info[0] kind (0 = MFMA 32x32x2 f32, 1 = vector FMA), info[1] BM, info[2] BN,
  *   info[3] BK, info[4] WM (MFMA wave tile rows) or TM (VALU microtile rows),
  *   info[5] WN or TN, info[6] threads per workgroup, info[7] vector loads (0/1),
- *   info[8] LDS bytes per workgroup, and when n >= 10, info[9] 64-bit offsets (0/1).
+ *   info[8] LDS bytes per workgroup; when n >= 10, info[9] 64-bit offsets (0/1); when
+ *   n >= 11, info[10] the number of k-groups splitting K inside one workgroup (1 = none).
  * Returns 0, or -1 for a bad id or n < 9. */
 SGEMM_API int sgemm_variant_info(int variant, int *info, int n);
 

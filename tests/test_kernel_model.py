@@ -57,7 +57,8 @@ def panel_loads(ROWS, COLS, NT, vec, r0, c0, nrows, ncols, clamp_rows, clamp_col
 
 
 def check_loads_in_bounds(v, M, N, K):
-    BM, BN, BK, NT, vec = v["BM"], v["BN"], v["BK"], v["threads"], bool(v["vec"])
+    # split-K variants: each k-group loads its slabs with its own threads (threads / ksplit)
+    BM, BN, BK, NT, vec = v["BM"], v["BN"], v["BK"], v["threads"] // v["ksplit"], bool(v["vec"])
     tiles_m, tiles_n = -(-M // BM), -(-N // BN)
     nslab = -(-K // BK)
     for tm in range(tiles_m):
@@ -73,8 +74,10 @@ def check_loads_in_bounds(v, M, N, K):
 
 
 def stored_elements(v, M, N):
-    """All (row, col) the epilogue stores, over every workgroup of the launch."""
-    BM, BN, NT = v["BM"], v["BN"], v["threads"]
+    """All (row, col) the epilogue stores, over every workgroup of the launch.
+
+    In split-K variants only k-group 0 (the first threads / ksplit threads) stores."""
+    BM, BN, NT = v["BM"], v["BN"], v["threads"] // v["ksplit"]
     tiles_m, tiles_n = -(-M // BM), -(-N // BN)
     tm_of, tn_of = _binding.tile_order(tiles_m, tiles_n, 8)
     tid = np.arange(NT)
@@ -132,6 +135,19 @@ def test_every_output_stored_exactly_once(v):
         flat = r.astype(np.int64) * N + c
         counts = np.bincount(flat, minlength=M * N)
         assert counts.min() == 1 and counts.max() == 1, (v["name"], M, N)
+
+
+@pytest.mark.parametrize("ks", [2, 4])
+@pytest.mark.parametrize("K,BK", [(1, 16), (16, 16), (17, 16), (777, 16), (96, 32), (4096, 32)])
+def test_splitk_slab_assignment_covers_k_once(ks, K, BK):
+    """Group g multiplies slabs g, g+KS, ... for ceil(nslab/KS) steps; slabs past K load zeros.
+    Every slab below nslab is taken by exactly one (step, group)."""
+    nslab = -(-K // BK)
+    niter = -(-nslab // ks)
+    taken = [i * ks + g for i in range(niter) for g in range(ks)]
+    real = [t for t in taken if t < nslab]
+    assert sorted(real) == list(range(nslab))
+    assert len(taken) - len(real) < ks
 
 
 @pytest.mark.parametrize("BK", [8, 16, 32])
