@@ -6,7 +6,10 @@ resident in HBM before the timed region).  Default workload: M = N = K = 4096,
 A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
-                    [--variant ID] [--no-cpu-baseline]
+                    [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline]
+
+``--op`` other than NN stores A as K x M and/or B as N x K and times
+``sgemm_op`` (op(A) * op(B)) on the same logical product.
 
 FLOP count: 2*M*N*K per call (one multiply and one add per (i, j, k); the
 count "SGEMM CUDA kernel (First Half)", "Part 4", gives as 2MNK, and with which
@@ -96,6 +99,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant id (default: dispatch)")
+    ap.add_argument("--op", default="NN", choices=["NN", "NT", "TN", "TT"],
+                    help="storage of A and B: op(A) op(B), T = stored transposed (sgemm_op)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -123,19 +128,29 @@ def main() -> int:
     torch.cuda.set_device(dev)
     log(f"workload: {w.describe()}")
     A, B, C0 = make_inputs(w)
-    dA = torch.from_numpy(A).to(dev)
-    dB = torch.from_numpy(B).to(dev)
+    ta, tb = args.op[0], args.op[1]
+    # the stored operands: A^T is K x M, B^T is N x K
+    As = np.ascontiguousarray(A.T) if ta == "T" else A
+    Bs = np.ascontiguousarray(B.T) if tb == "T" else B
+    lda, ldb = As.shape[1], Bs.shape[1]
+    dA = torch.from_numpy(As).to(dev)
+    dB = torch.from_numpy(Bs).to(dev)
     dC = torch.from_numpy(C0).to(dev)
-    vid = args.variant if args.variant >= 0 else sg.sgemm_select_variant(
-        w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N)
+    vid = args.variant if args.variant >= 0 else sg.sgemm_op_select_variant(
+        ta, tb, w.M, w.N, w.K, dA, lda, dB, ldb, dC, w.N)
     vname = sg.sgemm_variant_name(vid)
     info = sg.sgemm_variant_info(vid)
     log(f"variant: {vname} {info}")
     stream = torch.cuda.current_stream()
 
-    def step():
-        sg.sgemm_ex(w.M, w.N, w.K, w.alpha, dA.data_ptr(), w.K, dB.data_ptr(), w.N, w.beta,
-                    dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
+    if args.op == "NN":
+        def step():
+            sg.sgemm_ex(w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, w.beta,
+                        dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
+    else:
+        def step():
+            sg.sgemm_op_ex(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, w.beta,
+                           dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
 
     # first call: its output is the one checked against the oracle
     step()
@@ -194,9 +209,10 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"sgemm {w.M}x{w.N}x{w.K} alpha={w.alpha:g} beta={w.beta:g} {w.dist} seed={w.seed}",
+            "workload": (f"sgemm{'' if args.op == 'NN' else '_op ' + args.op} {w.M}x{w.N}x{w.K} "
+                         f"alpha={w.alpha:g} beta={w.beta:g} {w.dist} seed={w.seed}"),
             "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
-            "variant": vname,
+            "op": args.op, "variant": vname,
         },
         "pct_fp32_peak": round(100.0 * tflops / FP32_PEAK_TFLOPS, 2),
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),

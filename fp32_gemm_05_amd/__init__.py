@@ -1,4 +1,4 @@
-"""libsgemm: single-precision GEMM (C = alpha*A*B + beta*C, row-major fp32) for MI355X.
+"""libsgemm: single-precision GEMM (C = alpha*op(A)*op(B) + beta*C, row-major fp32) for MI355X.
 
 The compute path is hand-written HIP for gfx950 behind a C ABI
 (``include/sgemm.h``, ``libsgemm.so``); this package is the thin ctypes binding
@@ -14,6 +14,9 @@ from ._binding import (  # noqa: F401
     sgemm,
     sgemm_ex,
     sgemm_num_variants,
+    sgemm_op,
+    sgemm_op_ex,
+    sgemm_op_select_variant,
     sgemm_select_variant,
     sgemm_variant_info,
     sgemm_variant_name,

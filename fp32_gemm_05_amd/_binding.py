@@ -19,6 +19,8 @@ _lib = None
 
 _ARG_NAMES = {1: "M", 2: "N", 3: "K", 4: "alpha", 5: "A", 6: "lda", 7: "B", 8: "ldb", 9: "beta",
               10: "C", 11: "ldc", 12: "stream", 13: "variant"}
+# sgemm_op / sgemm_op_ex number the two transposition characters first
+_OP_ARG_NAMES = {1: "transa", 2: "transb", **{k + 2: v for k, v in _ARG_NAMES.items()}}
 
 
 class SgemmError(RuntimeError):
@@ -27,7 +29,8 @@ class SgemmError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
         if code < 0:
-            what = f"argument {-code} ({_ARG_NAMES.get(-code, '?')}) is invalid"
+            names = _OP_ARG_NAMES if where.startswith("sgemm_op") else _ARG_NAMES
+            what = f"argument {-code} ({names.get(-code, '?')}) is invalid"
         else:
             what = f"kernel launch failed with hipError_t {code}"
         super().__init__(f"{where}: {what}")
@@ -54,6 +57,13 @@ def load_library(path: str | None = None):
         lib.sgemm.restype = i
         lib.sgemm_ex.argtypes = gemm_args + [i]
         lib.sgemm_ex.restype = i
+        ch = ctypes.c_char
+        lib.sgemm_op.argtypes = [ch, ch] + gemm_args
+        lib.sgemm_op.restype = i
+        lib.sgemm_op_ex.argtypes = [ch, ch] + gemm_args + [i]
+        lib.sgemm_op_ex.restype = i
+        lib.sgemm_op_select_variant.argtypes = [ch, ch, i, i, i, vp, i, vp, i, vp, i]
+        lib.sgemm_op_select_variant.restype = i
         lib.sgemm_num_variants.argtypes = []
         lib.sgemm_num_variants.restype = i
         lib.sgemm_variant_name.argtypes = [i]
@@ -106,6 +116,33 @@ def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, variant=
         raise SgemmError(rc, "sgemm_ex")
 
 
+def _trans(t) -> bytes:
+    if isinstance(t, bool):
+        return b"T" if t else b"N"
+    if isinstance(t, str) and len(t) == 1:
+        return t.encode()
+    if isinstance(t, bytes) and len(t) == 1:
+        return t
+    raise TypeError(f"transposition must be one character or a bool, got {t!r}")
+
+
+def sgemm_op(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """C := alpha*op(A)*op(B) + beta*C; transa/transb 'N' or 'T' (or bools). Raises SgemmError."""
+    rc = load_library().sgemm_op(_trans(transa), _trans(transb), int(M), int(N), int(K), float(alpha), _ptr(A),
+                                 int(lda), _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc), _stream(stream))
+    if rc != 0:
+        raise SgemmError(rc, "sgemm_op")
+
+
+def sgemm_op_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, variant=-1):
+    """sgemm_op with a forced kernel variant (variant < 0: choose as sgemm_op does)."""
+    rc = load_library().sgemm_op_ex(_trans(transa), _trans(transb), int(M), int(N), int(K), float(alpha),
+                                    _ptr(A), int(lda), _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+                                    _stream(stream), int(variant))
+    if rc != 0:
+        raise SgemmError(rc, "sgemm_op_ex")
+
+
 def sgemm_num_variants() -> int:
     return int(load_library().sgemm_num_variants())
 
@@ -116,10 +153,11 @@ def sgemm_variant_name(variant: int):
 
 
 def sgemm_variant_info(variant: int) -> dict:
-    info = (ctypes.c_int * 11)()
-    if load_library().sgemm_variant_info(int(variant), info, 11) != 0:
+    info = (ctypes.c_int * 13)()
+    if load_library().sgemm_variant_info(int(variant), info, 13) != 0:
         raise ValueError(f"no variant {variant}")
-    keys = ["kind", "BM", "BN", "BK", "WM_or_TM", "WN_or_TN", "threads", "vec", "lds_bytes", "wide", "ksplit"]
+    keys = ["kind", "BM", "BN", "BK", "WM_or_TM", "WN_or_TN", "threads", "vec", "lds_bytes", "wide", "ksplit",
+            "trans_a", "trans_b"]
     d = dict(zip(keys, list(info)))
     d["kind"] = "mfma" if d["kind"] == 0 else "valu"
     d["name"] = sgemm_variant_name(variant)
@@ -129,6 +167,11 @@ def sgemm_variant_info(variant: int) -> dict:
 def sgemm_select_variant(M, N, K, A, lda, B, ldb, C, ldc) -> int:
     return int(load_library().sgemm_select_variant(int(M), int(N), int(K), _ptr(A), int(lda), _ptr(B),
                                                    int(ldb), _ptr(C), int(ldc)))
+
+
+def sgemm_op_select_variant(transa, transb, M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return int(load_library().sgemm_op_select_variant(_trans(transa), _trans(transb), int(M), int(N), int(K),
+                                                      _ptr(A), int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc)))
 
 
 def sgemm_version() -> str:
@@ -158,14 +201,24 @@ def _check_matrix(t, name):
     return t.stride(0) if t.shape[0] > 1 else max(1, t.shape[1])
 
 
-def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = -1, stream=None):
-    """Tensor form: C := alpha*A@B + beta*C in place for 2-D float32 device tensors; returns C."""
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = -1, stream=None,
+         trans_a: bool = False, trans_b: bool = False):
+    """Tensor form: C := alpha*op(A)@op(B) + beta*C in place for 2-D float32 device tensors; returns C.
+
+    A and B are the stored row-major arrays; ``trans_a`` reads A (K x M) as A^T, ``trans_b`` reads
+    B (N x K) as B^T."""
     lda = _check_matrix(A, "A")
     ldb = _check_matrix(B, "B")
     ldc = _check_matrix(C, "C")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
-    sgemm_ex(M, N, K, alpha, A, max(lda, K, 1), B, max(ldb, N, 1), beta, C, max(ldc, N, 1), stream, variant)
+    lda = max(lda, A.shape[1], 1)
+    ldb = max(ldb, B.shape[1], 1)
+    ldc = max(ldc, N, 1)
+    if trans_a or trans_b:
+        sgemm_op_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
+    else:
+        sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
     return C

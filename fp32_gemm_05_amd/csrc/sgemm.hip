@@ -8,6 +8,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 
 #include "../../include/sgemm.h"
@@ -30,6 +31,8 @@ struct Variant {
     LaunchFn launch;
     int wide;  // 64-bit per-lane load offsets (no 4 GiB limit on one workgroup's operand span)
     int ks;    // k-groups sharing one tile inside a workgroup (split-K); 0 means 1
+    int ta;    // op(A) = A^T: A stored K x M
+    int tb;    // op(B) = B^T: B stored N x K
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -43,14 +46,14 @@ int group_rows(int tiles_m, int tiles_n) {
     return tiles_m < 4 ? tiles_m : 4;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false>
 hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB>),
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
@@ -118,6 +121,18 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define BOTH_SPLITK(BM, BN, BK, WM, WN, KS)                                                     \
     SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, true, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_vec"),   \
         SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, false, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_scalar")
+#define TRANS_VARIANT(BM, BN, BK, WM, WN, VEC, WIDE, TA, TB, NAME)                              \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT, VEC,          \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::LDS_BYTES,                                         \
+     &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, WIDE, TA, TB>, WIDE, 0, TA, TB}
+// the variants of one transposition (TAG: "nt", "tn" or "tt"; first letter op(A), second op(B))
+#define TRANS_SET(TA, TB, TAG)                                                                     \
+    TRANS_VARIANT(128, 128, 16, 64, 64, true, false, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_vec"),     \
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, false, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_scalar"), \
+        TRANS_VARIANT(64, 64, 32, 32, 32, true, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_vec"),         \
+        TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
+        TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
 #define BOTH_VALU(BM, BN, BK, TM, TN) \
     VALU_VARIANT(BM, BN, BK, TM, TN, true, "_vec"), VALU_VARIANT(BM, BN, BK, TM, TN, false, "_scalar")
 
@@ -149,6 +164,10 @@ const Variant kVariants[] = {
     // 64-bit offsets: used whenever one workgroup's operand span does not fit 32-bit offsets
     WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, true, MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec"),
     WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, false, MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
+    // transposed operands (sgemm_op): op(A) x op(B) = N x T, T x N, T x T
+    TRANS_SET(false, true, "nt"),
+    TRANS_SET(true, false, "tn"),
+    TRANS_SET(true, true, "tt"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -193,25 +212,49 @@ const DispatchTable& dispatch_table() {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Precondition of the 128-bit load/store variants.
-bool vec_ok(int N, int K, const float* A, int lda, const float* B, int ldb, const float* C, int ldc) {
-    return aligned16(A) && aligned16(B) && aligned16(C) && (lda % 4 == 0) && (ldb % 4 == 0) &&
-           (ldc % 4 == 0) && (K % 4 == 0) && (N % 4 == 0);
+// One call's arguments.  op(A) is M x K and op(B) is K x N; the stored A is M x K (row length
+// K) or, when ta, K x M (row length M); the stored B is K x N or, when tb, N x K.
+struct Problem {
+    bool ta, tb;
+    int M, N, K;
+    float alpha, beta;
+    const float* A;
+    int lda;
+    const float* B;
+    int ldb;
+    float* C;
+    int ldc;
+    int a_rows() const { return ta ? K : M; }
+    int a_cols() const { return ta ? M : K; }
+    int b_rows() const { return tb ? N : K; }
+    int b_cols() const { return tb ? K : N; }
+};
+
+// Arguments, for error reporting; each entry point maps them to its own 1-based positions.
+enum Arg {
+    kArgTransA = 1, kArgTransB, kArgM, kArgN, kArgK, kArgAlpha, kArgA, kArgLda, kArgB, kArgLdb, kArgBeta,
+    kArgC, kArgLdc, kArgStream, kArgVariant, kNumArgs
+};
+// positions in sgemm / sgemm_ex (no transposition arguments) and in sgemm_op / sgemm_op_ex
+const int kPosPlain[kNumArgs] = {0, 0, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13};
+const int kPosOp[kNumArgs] = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15};
+
+// Precondition of the 128-bit load/store variants: every operand row starts 16-byte aligned
+// and has a multiple of 4 elements.
+bool vec_ok(const Problem& p) {
+    return aligned16(p.A) && aligned16(p.B) && aligned16(p.C) && (p.lda % 4 == 0) && (p.ldb % 4 == 0) &&
+           (p.ldc % 4 == 0) && (p.a_cols() % 4 == 0) && (p.b_cols() % 4 == 0) && (p.N % 4 == 0);
 }
 
 // Do one workgroup's A and B panels fit 32-bit per-lane byte offsets? (narrow variants only)
-bool offsets_fit(const Variant& v, int lda, int ldb) {
+bool offsets_fit(const Variant& v, const Problem& p) {
     if (v.wide) return true;
     const unsigned long long lim = 1ull << 32;
-    const unsigned long long a = ((unsigned long long)(v.bm - 1) * (unsigned)lda + (unsigned)v.bk) * 4ull;
-    const unsigned long long b = ((unsigned long long)(v.bk - 1) * (unsigned)ldb + (unsigned)v.bn) * 4ull;
+    const unsigned long long a_rows = v.ta ? v.bk : v.bm, a_cols = v.ta ? v.bm : v.bk;
+    const unsigned long long b_rows = v.tb ? v.bn : v.bk, b_cols = v.tb ? v.bk : v.bn;
+    const unsigned long long a = ((a_rows - 1) * (unsigned)p.lda + a_cols) * 4ull;
+    const unsigned long long b = ((b_rows - 1) * (unsigned)p.ldb + b_cols) * 4ull;
     return a < lim && b < lim;
-}
-
-int wide_fallback(bool vec) {
-    static const int ids[2] = {find_variant(MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
-                               find_variant(MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec")};
-    return ids[vec ? 1 : 0];
 }
 
 // skinny: N <= 64; small: fewer than 256 output tiles of 128x128 (under one per CU);
@@ -224,37 +267,76 @@ int shape_class(int M, int N) {
     return kHuge;
 }
 
-int select_variant(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
-                   int ldc) {
-    const bool v = vec_ok(N, K, A, lda, B, ldb, C, ldc);
-    const int id = dispatch_table().id[shape_class(M, N)][v ? 1 : 0];
-    return offsets_fit(kVariants[id], lda, ldb) ? id : wide_fallback(v);
+int wide_fallback(bool vec) {
+    static const int ids[2] = {find_variant(MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
+                               find_variant(MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec")};
+    return ids[vec ? 1 : 0];
 }
 
-// Argument checks shared by every computing entry point.  Returns 0 or -i.
-int validate(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float* C,
-             int ldc) {
-    if (M < 0) return -1;
-    if (N < 0) return -2;
-    if (K < 0) return -3;
-    if (lda < (K > 1 ? K : 1)) return -6;
-    if (ldb < (N > 1 ? N : 1)) return -8;
-    if (ldc < (N > 1 ? N : 1)) return -11;
-    if (M == 0 || N == 0) return 0;
-    if (C == nullptr) return -10;
-    const bool reads_ab = alpha != 0.f && K > 0;
-    if (reads_ab && A == nullptr) return -5;
-    if (reads_ab && B == nullptr) return -7;
+// Transposed-operand dispatch: [ta*2+tb-1][small/large][vec], and the wide forms [..][vec].
+struct TransTable {
+    int id[3][2][2];
+    int wide[3][2];
+    TransTable() {
+        static const char* tags[3] = {"nt", "tn", "tt"};
+        char name[96];
+        for (int c = 0; c < 3; ++c) {
+            for (int vec = 0; vec < 2; ++vec) {
+                const char* suffix = vec ? "vec" : "scalar";
+                std::snprintf(name, sizeof(name), MFMA_NAME(64, 64, 32, 32, 32) "_%s_%s", tags[c], suffix);
+                id[c][0][vec] = find_variant(name);
+                std::snprintf(name, sizeof(name), MFMA_NAME(128, 128, 16, 64, 64) "_%s_%s", tags[c], suffix);
+                id[c][1][vec] = find_variant(name);
+                std::snprintf(name, sizeof(name), MFMA_NAME(128, 128, 16, 64, 64) "_%s_wide_%s", tags[c], suffix);
+                wide[c][vec] = find_variant(name);
+            }
+        }
+    }
+};
+
+const TransTable& trans_table() {
+    static const TransTable t;
+    return t;
+}
+
+int select_variant(const Problem& p) {
+    const bool v = vec_ok(p);
+    const int cls = shape_class(p.M, p.N);
+    if (!p.ta && !p.tb) {
+        const int id = dispatch_table().id[cls][v ? 1 : 0];
+        return offsets_fit(kVariants[id], p) ? id : wide_fallback(v);
+    }
+    const int combo = (p.ta ? 2 : 0) + (p.tb ? 1 : 0) - 1;
+    const bool big = cls == kLarge || cls == kHuge;
+    const int id = trans_table().id[combo][big ? 1 : 0][v ? 1 : 0];
+    return offsets_fit(kVariants[id], p) ? id : trans_table().wide[combo][v ? 1 : 0];
+}
+
+// Argument checks shared by every computing entry point.  Returns 0 or -Arg.
+int validate(const Problem& p) {
+    if (p.M < 0) return -kArgM;
+    if (p.N < 0) return -kArgN;
+    if (p.K < 0) return -kArgK;
+    if (p.lda < (p.a_cols() > 1 ? p.a_cols() : 1)) return -kArgLda;
+    if (p.ldb < (p.b_cols() > 1 ? p.b_cols() : 1)) return -kArgLdb;
+    if (p.ldc < (p.N > 1 ? p.N : 1)) return -kArgLdc;
+    if (p.M == 0 || p.N == 0) return 0;
+    if (p.C == nullptr) return -kArgC;
+    const bool reads_ab = p.alpha != 0.f && p.K > 0;
+    if (reads_ab && p.A == nullptr) return -kArgA;
+    if (reads_ab && p.B == nullptr) return -kArgB;
     // C must not overlap A or B (byte ranges of the addressed elements).
-    const uintptr_t c0 = reinterpret_cast<uintptr_t>(C);
-    const uintptr_t c1 = c0 + ((uintptr_t)(M - 1) * (uintptr_t)ldc + (uintptr_t)N) * sizeof(float);
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(p.C);
+    const uintptr_t c1 = c0 + ((uintptr_t)(p.M - 1) * (uintptr_t)p.ldc + (uintptr_t)p.N) * sizeof(float);
     if (reads_ab) {
-        const uintptr_t a0 = reinterpret_cast<uintptr_t>(A);
-        const uintptr_t a1 = a0 + ((uintptr_t)(M - 1) * (uintptr_t)lda + (uintptr_t)K) * sizeof(float);
-        if (a0 < c1 && c0 < a1) return -10;
-        const uintptr_t b0 = reinterpret_cast<uintptr_t>(B);
-        const uintptr_t b1 = b0 + ((uintptr_t)(K - 1) * (uintptr_t)ldb + (uintptr_t)N) * sizeof(float);
-        if (b0 < c1 && c0 < b1) return -10;
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(p.A);
+        const uintptr_t a1 =
+            a0 + ((uintptr_t)(p.a_rows() - 1) * (uintptr_t)p.lda + (uintptr_t)p.a_cols()) * sizeof(float);
+        if (a0 < c1 && c0 < a1) return -kArgC;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(p.B);
+        const uintptr_t b1 =
+            b0 + ((uintptr_t)(p.b_rows() - 1) * (uintptr_t)p.ldb + (uintptr_t)p.b_cols()) * sizeof(float);
+        if (b0 < c1 && c0 < b1) return -kArgC;
     }
     return 0;
 }
@@ -270,24 +352,46 @@ hipError_t launch_scale(int M, int N, float beta, float* C, int ldc, hipStream_t
                            args, 0, stream);
 }
 
-int run(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta, float* C,
-        int ldc, hipStream_t stream, int variant) {
-    int rc = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+// Returns 0, a positive hipError_t, or -Arg.
+int run(const Problem& p, hipStream_t stream, int variant) {
+    int rc = validate(p);
     if (rc != 0) return rc;
-    if (variant >= kNumVariants) return -13;
-    if (M == 0 || N == 0) return 0;
-    if (alpha == 0.f || K == 0) return (int)launch_scale(M, N, beta, C, ldc, stream);
+    if (variant >= kNumVariants) return -kArgVariant;
+    if (p.M == 0 || p.N == 0) return 0;
+    if (p.alpha == 0.f || p.K == 0) return (int)launch_scale(p.M, p.N, p.beta, p.C, p.ldc, stream);
     if (variant < 0) {
-        variant = select_variant(M, N, K, A, lda, B, ldb, C, ldc);
-        if (variant < 0) return -13;
+        variant = select_variant(p);
+        if (variant < 0) return -kArgVariant;
     }
     const Variant& v = kVariants[variant];
-    if (v.vec && !vec_ok(N, K, A, lda, B, ldb, C, ldc)) return -13;
-    if (!offsets_fit(v, lda, ldb)) return -13;
-    const long tiles = (long)ceil_div(M, v.bm) * (long)ceil_div(N, v.bn);
-    if (tiles > INT_MAX) return -1;
-    GemmArgs g{M, N, K, alpha, beta, A, (long)lda, B, (long)ldb, C, (long)ldc};
+    if ((v.ta != 0) != p.ta || (v.tb != 0) != p.tb) return -kArgVariant;
+    if (v.vec && !vec_ok(p)) return -kArgVariant;
+    if (!offsets_fit(v, p)) return -kArgVariant;
+    const long tiles = (long)ceil_div(p.M, v.bm) * (long)ceil_div(p.N, v.bn);
+    if (tiles > INT_MAX) return -kArgM;
+    GemmArgs g{p.M, p.N, p.K, p.alpha, p.beta, p.A, (long)p.lda, p.B, (long)p.ldb, p.C, (long)p.ldc};
     return (int)v.launch(g, stream);
+}
+
+// 'N'/'n': as stored; 'T'/'t' or 'C'/'c' (real data: the conjugate transpose is the transpose).
+int parse_trans(char c) {
+    if (c == 'N' || c == 'n') return 0;
+    if (c == 'T' || c == 't' || c == 'C' || c == 'c') return 1;
+    return -1;
+}
+
+int run_entry(const Problem& p, hipStream_t stream, int variant, const int* pos) {
+    const int rc = run(p, stream, variant);
+    return rc < 0 ? -pos[-rc] : rc;
+}
+
+int run_op(char transa, char transb, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+           int ldb, float beta, float* C, int ldc, hipStream_t stream, int variant) {
+    const int ta = parse_trans(transa), tb = parse_trans(transb);
+    if (ta < 0) return -kPosOp[kArgTransA];
+    if (tb < 0) return -kPosOp[kArgTransB];
+    const Problem p{ta != 0, tb != 0, M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    return run_entry(p, stream, variant, kPosOp);
 }
 
 }  // namespace
@@ -297,12 +401,24 @@ extern "C" {
 
 int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta, float* C,
           int ldc, hipStream_t stream) {
-    return libsgemm::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+    const libsgemm::Problem p{false, false, M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    return libsgemm::run_entry(p, stream, -1, libsgemm::kPosPlain);
 }
 
 int sgemm_ex(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
              float* C, int ldc, hipStream_t stream, int variant) {
-    return libsgemm::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+    const libsgemm::Problem p{false, false, M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    return libsgemm::run_entry(p, stream, variant, libsgemm::kPosPlain);
+}
+
+int sgemm_op(char transa, char transb, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+             int ldb, float beta, float* C, int ldc, hipStream_t stream) {
+    return libsgemm::run_op(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+}
+
+int sgemm_op_ex(char transa, char transb, int M, int N, int K, float alpha, const float* A, int lda,
+                const float* B, int ldb, float beta, float* C, int ldc, hipStream_t stream, int variant) {
+    return libsgemm::run_op(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
 }
 
 int sgemm_num_variants(void) { return libsgemm::kNumVariants; }
@@ -326,14 +442,25 @@ int sgemm_variant_info(int variant, int* info, int n) {
     info[8] = v.lds_bytes;
     if (n >= 10) info[9] = v.wide;
     if (n >= 11) info[10] = v.ks > 1 ? v.ks : 1;
+    if (n >= 13) {
+        info[11] = v.ta;
+        info[12] = v.tb;
+    }
     return 0;
 }
 
 int sgemm_select_variant(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
                          int ldc) {
-    if (M <= 0 || N <= 0 || K <= 0) return -1;
-    if (lda < K || ldb < N || ldc < N) return -1;
-    return libsgemm::select_variant(M, N, K, A, lda, B, ldb, C, ldc);
+    return sgemm_op_select_variant('N', 'N', M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+int sgemm_op_select_variant(char transa, char transb, int M, int N, int K, const float* A, int lda,
+                            const float* B, int ldb, const float* C, int ldc) {
+    const int ta = libsgemm::parse_trans(transa), tb = libsgemm::parse_trans(transb);
+    if (ta < 0 || tb < 0 || M <= 0 || N <= 0 || K <= 0) return -1;
+    const libsgemm::Problem p{ta != 0, tb != 0, M, N, K, 1.f, 0.f, A, lda, B, ldb, const_cast<float*>(C), ldc};
+    if (lda < p.a_cols() || ldb < p.b_cols() || ldc < N) return -1;
+    return libsgemm::select_variant(p);
 }
 
 int sgemm_tile_order(int tiles_m, int tiles_n, int group_m, int* tile_m, int* tile_n) {

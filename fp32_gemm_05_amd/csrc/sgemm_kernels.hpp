@@ -209,15 +209,19 @@ struct PanelLoader {
 // so a lane's four A values are contiguous in the k-major LDS slab (one 128-bit
 // LDS read) and the 8 k's of the group are each used exactly once.
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+// TA / TB: op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K).  The LDS slab of an
+// operand keeps the layout of its global rows: k-contiguous [rows][BK + 4] when K runs along
+// the stored rows (A, or B^T), and [BK][cols + 8] when it runs down the stored columns (B, or A^T).
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool TA = false, bool TB = false>
 struct MfmaCfg {
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int PA = 4;  // A slab pitch BK+4: 128-bit reads of 16 consecutive rows hit distinct banks
-    static constexpr int PB = 8;  // B slab pitch BN+8: the two half-waves (k and k+4) land on opposite bank halves
-    static constexpr int A_PITCH = BK + PA, B_PITCH = BN + PB;
-    static constexpr int A_STAGE = BM * A_PITCH, B_STAGE = BK * B_PITCH;
+    // k-contiguous slabs: pitch BK+4, so the 128-bit reads of 16 consecutive rows hit distinct
+    // banks; k-strided slabs: pitch (width)+8, so the two half-waves (k and k+4) land on
+    // opposite bank halves.
+    static constexpr int A_PITCH = TA ? BM + 8 : BK + 4, B_PITCH = TB ? BK + 4 : BN + 8;
+    static constexpr int A_STAGE = (TA ? BK : BM) * A_PITCH, B_STAGE = (TB ? BN : BK) * B_PITCH;
     static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 4;
     static_assert(BM % WM == 0 && BN % WN == 0, "wave tiling");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
@@ -291,11 +295,11 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
-__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false>
+__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
     constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
     constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
     __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
@@ -311,10 +315,22 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int li = lane & 31, lh = lane >> 5;
 
     const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false, WIDE> la;  // A slab: BM rows x BK columns of A
-    PanelLoader<BK, BN, NT, VEC, true, WIDE> lb;   // B slab: BK rows x BN columns of B
-    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
-    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
+    // A slab: BM rows x BK columns of A, or (TA) BK rows x BM columns of the stored A^T.
+    // B slab: BK rows x BN columns of B, or (TB) BN rows x BK columns of the stored B^T.
+    using LoaderA = typename std::conditional<TA, PanelLoader<BK, BM, NT, VEC, true, WIDE>,
+                                              PanelLoader<BM, BK, NT, VEC, false, WIDE>>::type;
+    using LoaderB = typename std::conditional<TB, PanelLoader<BN, BK, NT, VEC, false, WIDE>,
+                                              PanelLoader<BK, BN, NT, VEC, true, WIDE>>::type;
+    LoaderA la;
+    LoaderB lb;
+    if (TA)
+        la.init(tid, g.A, g.lda, 0, m0, K, g.M, BK);
+    else
+        la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
+    if (TB)
+        lb.init(tid, g.B, g.ldb, n0, 0, g.N, K, BK);
+    else
+        lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -355,13 +371,27 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             f32x4 a[FM];
             float b[FN][4];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                a[i] = *reinterpret_cast<const f32x4*>(sa + (wm0 + i * 32 + li) * AP + kk * 8 + lh * 4);
+            for (int i = 0; i < FM; ++i) {
+                if (TA) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+                    for (int t = 0; t < 4; ++t) a[i][t] = sa[(kk * 8 + lh * 4 + t) * AP + wm0 + i * 32 + li];
+                } else {
+                    a[i] = *reinterpret_cast<const f32x4*>(sa + (wm0 + i * 32 + li) * AP + kk * 8 + lh * 4);
+                }
+            }
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    b[j][t] = sb[(kk * 8 + lh * 4 + t) * BP + wn0 + j * 32 + li];
+            for (int j = 0; j < FN; ++j) {
+                if (TB) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(sb + (wn0 + j * 32 + li) * BP + kk * 8 + lh * 4);
+                    b[j][0] = v.x;
+                    b[j][1] = v.y;
+                    b[j][2] = v.z;
+                    b[j][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) b[j][t] = sb[(kk * 8 + lh * 4 + t) * BP + wn0 + j * 32 + li];
+                }
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll

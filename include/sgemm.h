@@ -42,11 +42,27 @@
  * an exact product only by fp32 rounding; integer-valued inputs whose partial
  * sums stay below 2^24 in magnitude give exact results.
  *
+ * Transposed operands (sgemm_op, sgemm_op_ex):
+ *
+ *     C := alpha * op(A) * op(B) + beta * C,   op(X) = X or X^T,
+ *
+ * op(A) M x K, op(B) K x N.  With op(A) = A^T the stored A is K x M,
+ * A^T(i, k) = A[k * lda + i], lda >= max(1, M); with op(B) = B^T the stored B
+ * is N x K, B^T(k, j) = B[j * ldb + k], ldb >= max(1, K).  A row-major K x M
+ * array read as its transpose is the column-major M x K matrix, so these entry
+ * points also serve column-major callers.  The kernels read both stored forms
+ * with coalesced global loads and transpose while staging into LDS, the staging
+ * transpose of "SGEMM CUDA kernel (First Half)", "Part 5: Reduced bank
+ * conflict (v3)" (the A tile is written k-major into shared memory).
+ *
  * Return codes (never aborts, never prints):
  *    0   success (work enqueued, or a valid quick return);
  *   -i   argument i is invalid (1-based, BLAS style): M=1, N=2, K=3, alpha=4,
  *        A=5, lda=6, B=7, ldb=8, beta=9, C=10, ldc=11, stream=12,
- *        variant=13 (sgemm_ex only); nothing is enqueued;
+ *        variant=13 (sgemm_ex only); nothing is enqueued.  In sgemm_op and
+ *        sgemm_op_ex the positions include the two leading characters:
+ *        transa=1, transb=2, M=3, N=4, K=5, alpha=6, A=7, lda=8, B=9, ldb=10,
+ *        beta=11, C=12, ldc=13, stream=14, variant=15 (sgemm_op_ex only);
  *   +e   a hipError_t returned by the kernel launch.
  */
 #ifndef LIBSGEMM_SGEMM_H
@@ -71,7 +87,8 @@ SGEMM_API int sgemm(int M, int N, int K, float alpha,
 
 /* As sgemm, with the kernel variant forced (0 <= variant < sgemm_num_variants()),
  * or chosen as sgemm does when variant < 0.  Returns -13 when the id is out of
- * range or a precondition of the variant fails:
+ * range, names a transposed-operand variant (those serve sgemm_op_ex only), or
+ * a precondition of the variant fails:
  *   - vector variants ("_vec") need A, B and C 16-byte aligned and lda, ldb,
  *     ldc, K and N multiples of 4;
  *   - variants other than "_wide" ones address one workgroup's operand panels
@@ -86,6 +103,31 @@ SGEMM_API int sgemm_ex(int M, int N, int K, float alpha,
                        float beta, float *C, int ldc,
                        hipStream_t stream, int variant);
 
+/* C := alpha*op(A)*op(B) + beta*C (see "Transposed operands" above).  transa and
+ * transb are 'N' or 'n' (as stored), or 'T', 't', 'C' or 'c' (transposed; for
+ * real data the conjugate transpose is the transpose); anything else returns
+ * -1 or -2.  sgemm_op('N', 'N', ...) computes exactly what sgemm computes.  Null
+ * pointers, overlap and quick returns follow sgemm, with the stored extents:
+ * A spans (rows-1)*lda + cols elements for its stored rows x cols, B likewise. */
+SGEMM_API int sgemm_op(char transa, char transb, int M, int N, int K, float alpha,
+                       const float *A, int lda,
+                       const float *B, int ldb,
+                       float beta, float *C, int ldc,
+                       hipStream_t stream);
+
+/* As sgemm_op with the kernel variant forced, as sgemm_ex.  Returns -15 when the
+ * id is out of range, when the variant's transposition (info[11], info[12]) is
+ * not the requested one, or when a precondition of the variant fails: "_vec"
+ * variants need A, B and C 16-byte aligned and lda, ldb, ldc, N and the stored
+ * row lengths of A and B (K or M, N or K) multiples of 4; narrow variants need
+ * one workgroup's stored panel spans to fit 32-bit byte offsets, as for sgemm_ex
+ * with the panel's stored rows and columns. */
+SGEMM_API int sgemm_op_ex(char transa, char transb, int M, int N, int K, float alpha,
+                          const float *A, int lda,
+                          const float *B, int ldb,
+                          float beta, float *C, int ldc,
+                          hipStream_t stream, int variant);
+
 /* Number of kernel variants (ids 0 .. n-1). */
 SGEMM_API int sgemm_num_variants(void);
 
@@ -97,7 +139,9 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   info[3] BK, info[4] WM (MFMA wave tile rows) or TM (VALU microtile rows),
  *   info[5] WN or TN, info[6] threads per workgroup, info[7] vector loads (0/1),
  *   info[8] LDS bytes per workgroup; when n >= 10, info[9] 64-bit offsets (0/1); when
- *   n >= 11, info[10] the number of k-groups splitting K inside one workgroup (1 = none).
+ *   n >= 11, info[10] the number of k-groups splitting K inside one workgroup (1 = none);
+ *   when n >= 13, info[11] and info[12]: the variant reads A, resp. B, transposed (0/1).
+ *   Variants with info[11] or info[12] set serve only sgemm_op / sgemm_op_ex.
  * Returns 0, or -1 for a bad id or n < 9. */
 SGEMM_API int sgemm_variant_info(int variant, int *info, int n);
 
@@ -107,6 +151,13 @@ SGEMM_API int sgemm_select_variant(int M, int N, int K,
                                    const float *A, int lda,
                                    const float *B, int ldb,
                                    const float *C, int ldc);
+
+/* The variant id sgemm_op would use (pure host function); -1 when the arguments
+ * describe a quick return or are invalid. */
+SGEMM_API int sgemm_op_select_variant(char transa, char transb, int M, int N, int K,
+                                      const float *A, int lda,
+                                      const float *B, int ldb,
+                                      const float *C, int ldc);
 
 /* Host-side copy of the workgroup -> output-tile map every kernel uses (for tests):
  * fills tile_m[w], tile_n[w] for w in [0, tiles_m * tiles_n).  Returns 0, or -1

@@ -130,6 +130,8 @@ def main() -> int:
         for v, info in enumerate(infos):
             if info["vec"] and not vec_ok:
                 continue
+            if info["trans_a"] or info["trans_b"]:
+                continue  # transposed-operand variants serve sgemm_op only
             dC.copy_(dC0)
 
             def call():

@@ -28,8 +28,14 @@ import fp32_gemm_05_amd as sg  # noqa: E402
 
 
 def _variants():
+    """The variants sgemm / sgemm_ex serve (the transposed-operand ones are tested in test_gpu_trans)."""
     try:
-        return [(i, sg.sgemm_variant_name(i)) for i in range(sg.sgemm_num_variants())]
+        out = []
+        for i in range(sg.sgemm_num_variants()):
+            info = sg.sgemm_variant_info(i)
+            if not info["trans_a"] and not info["trans_b"]:
+                out.append((i, info["name"]))
+        return out
     except OSError:
         return []
 

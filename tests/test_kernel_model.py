@@ -57,20 +57,34 @@ def panel_loads(ROWS, COLS, NT, vec, r0, c0, nrows, ncols, clamp_rows, clamp_col
 
 
 def check_loads_in_bounds(v, M, N, K):
+    """Loads of every A and B panel stay inside the STORED operand: A is M x K, or K x M when the
+    variant reads it transposed (a BK x BM panel whose columns past M are clamped); B is K x N, or
+    N x K when transposed (a BN x BK panel whose rows past N are clamped)."""
     # split-K variants: each k-group loads its slabs with its own threads (threads / ksplit)
     BM, BN, BK, NT, vec = v["BM"], v["BN"], v["BK"], v["threads"] // v["ksplit"], bool(v["vec"])
+    ta, tb = v.get("trans_a", 0), v.get("trans_b", 0)
     tiles_m, tiles_n = -(-M // BM), -(-N // BN)
     nslab = -(-K // BK)
     for tm in range(tiles_m):
         for s in range(nslab):
-            r, c, W, ok = panel_loads(BM, BK, NT, vec, tm * BM, s * BK, M, K, True, False)
+            if ta:
+                r, c, W, ok = panel_loads(BK, BM, NT, vec, s * BK, tm * BM, K, M, False, True)
+                rows, cols = K, M
+            else:
+                r, c, W, ok = panel_loads(BM, BK, NT, vec, tm * BM, s * BK, M, K, True, False)
+                rows, cols = M, K
             r, c = r[ok], c[ok]
-            assert (r >= 0).all() and (r < M).all() and (c >= 0).all() and (c + W <= K).all()
+            assert (r >= 0).all() and (r < rows).all() and (c >= 0).all() and (c + W <= cols).all()
     for tn in range(tiles_n):
         for s in range(nslab):
-            r, c, W, ok = panel_loads(BK, BN, NT, vec, s * BK, tn * BN, K, N, False, True)
+            if tb:
+                r, c, W, ok = panel_loads(BN, BK, NT, vec, tn * BN, s * BK, N, K, True, False)
+                rows, cols = N, K
+            else:
+                r, c, W, ok = panel_loads(BK, BN, NT, vec, s * BK, tn * BN, K, N, False, True)
+                rows, cols = K, N
             r, c = r[ok], c[ok]
-            assert (r >= 0).all() and (r < K).all() and (c >= 0).all() and (c + W <= N).all()
+            assert (r >= 0).all() and (r < rows).all() and (c >= 0).all() and (c + W <= cols).all()
 
 
 def stored_elements(v, M, N):
@@ -116,13 +130,16 @@ def stored_elements(v, M, N):
 
 
 SHAPES = [(1, 1, 1), (1, 4, 4), (4, 1, 4), (33, 65, 9), (128, 128, 16), (129, 131, 17), (64, 64, 64),
-          (257, 65, 33), (300, 260, 77), (65, 300, 8), (256, 64, 1024), (130, 68, 12)]
+          (257, 65, 33), (300, 260, 77), (65, 300, 8), (256, 64, 1024), (130, 68, 12), (4, 4, 4),
+          (132, 132, 20), (68, 260, 36)]
 
 
 @pytest.mark.parametrize("v", VARIANTS, ids=[v["name"] for v in VARIANTS])
 def test_loads_in_bounds(v):
     for (M, N, K) in SHAPES:
-        if v["vec"] and (N % 4 or K % 4):
+        a_len = M if v["trans_a"] else K   # stored row lengths
+        b_len = K if v["trans_b"] else N
+        if v["vec"] and (N % 4 or a_len % 4 or b_len % 4):
             continue  # the variant refuses these shapes
         check_loads_in_bounds(v, M, N, K)
 
