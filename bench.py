@@ -159,22 +159,20 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
+    # K + 1 events on the kernels' stream: event i before step i, event i + 1 after it.  One event
+    # between consecutive launches (not two) keeps the stream as close to back-to-back as timing
+    # every launch allows; launch i's duration is elapsed(ev[i], ev[i + 1]).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_all0.record(stream)
+    ev[0].record(stream)
     for i in range(args.steps):
-        ev_start[i].record(stream)
         step()
-        ev_end[i].record(stream)
-    t_all1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_all0.elapsed_time(t_all1)
-    per_launch = np.array([s.elapsed_time(e) for s, e in zip(ev_start, ev_end)])
+    total_ms = ev[0].elapsed_time(ev[args.steps])
+    per_launch = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     ms_per_step = total_ms / args.steps
     flops = 2.0 * w.M * w.N * w.K
     tflops = flops / (ms_per_step * 1e-3) / 1e12

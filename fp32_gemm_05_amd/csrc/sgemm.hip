@@ -57,6 +57,17 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
 hipError_t launch_mfma_pipe(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
@@ -133,6 +144,13 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
         TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
         TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
         TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
+#define DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, NAME)                                             \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0>, 0}
+#define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
+#define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
+    DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
+        DEEP_VARIANT(BM, BN, BK, WM, WN, false, DEEP_NAME(BM, BN, BK, WM, WN) "_scalar")
 #define BOTH_VALU(BM, BN, BK, TM, TN) \
     VALU_VARIANT(BM, BN, BK, TM, TN, true, "_vec"), VALU_VARIANT(BM, BN, BK, TM, TN, false, "_scalar")
 
@@ -146,6 +164,7 @@ const Variant kVariants[] = {
     BOTH_MFMA(64, 64, 16, 32, 32),
     BOTH_MFMA(64, 64, 32, 32, 32),
     VEC_MFMA_OCC(128, 128, 16, 64, 64, 4),
+    MFMA_VARIANT(128, 128, 16, 64, 64, 4, false, MFMA_NAME(128, 128, 16, 64, 64) "_o4_scalar"),
     VEC_MFMA_OCC(128, 128, 32, 64, 64, 2),
     PIPE_VARIANT(128, 128, 32, 64, 64, 2, true, PIPE_NAME(128, 128, 32, 64, 64, 2) "_vec"),
     BOTH_PIPE(256, 128, 16, 64, 64, 2),
@@ -164,6 +183,9 @@ const Variant kVariants[] = {
     // 64-bit offsets: used whenever one workgroup's operand span does not fit 32-bit offsets
     WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, true, MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec"),
     WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, false, MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
+    // deep prefetch (one wave per SIMD)
+    BOTH_DEEP(64, 64, 32, 32, 32),
+    BOTH_DEEP(64, 64, 64, 32, 32),
     // transposed operands (sgemm_op): op(A) x op(B) = N x T, T x N, T x T
     TRANS_SET(false, true, "nt"),
     TRANS_SET(true, false, "tn"),
@@ -172,7 +194,7 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Shape classes of the dispatch table.
-enum ShapeClass { kSkinny = 0, kSmall = 1, kLarge = 2, kHuge = 3, kNumClasses = 4 };
+enum ShapeClass { kSkinny = 0, kSmall = 1, kLarge = 2, kHuge = 3, kShallow = 4, kNumClasses = 5 };
 
 struct TableEntry {
     int shape_class;
@@ -258,12 +280,13 @@ bool offsets_fit(const Variant& v, const Problem& p) {
 }
 
 // skinny: N <= 64; small: fewer than 256 output tiles of 128x128 (under one per CU);
-// large: up to 2048 such tiles; huge: more.
-int shape_class(int M, int N) {
+// large: up to 2048 such tiles; huge: more; shallow: a large tile count with K <= 1024 (each
+// tile's K loop is short, so the last round of tiles weighs more: smaller tiles win there).
+int shape_class(int M, int N, int K) {
     if (N <= 64) return kSkinny;
     long tiles128 = (long)ceil_div(M, 128) * ceil_div(N, 128);
     if (tiles128 < 256) return kSmall;
-    if (tiles128 < 2048) return kLarge;
+    if (tiles128 < 2048) return K <= 1024 ? kShallow : kLarge;
     return kHuge;
 }
 
@@ -301,13 +324,13 @@ const TransTable& trans_table() {
 
 int select_variant(const Problem& p) {
     const bool v = vec_ok(p);
-    const int cls = shape_class(p.M, p.N);
+    const int cls = shape_class(p.M, p.N, p.K);
     if (!p.ta && !p.tb) {
         const int id = dispatch_table().id[cls][v ? 1 : 0];
         return offsets_fit(kVariants[id], p) ? id : wide_fallback(v);
     }
     const int combo = (p.ta ? 2 : 0) + (p.tb ? 1 : 0) - 1;
-    const bool big = cls == kLarge || cls == kHuge;
+    const bool big = cls == kLarge || cls == kHuge || cls == kShallow;
     const int id = trans_table().id[combo][big ? 1 : 0][v ? 1 : 0];
     return offsets_fit(kVariants[id], p) ? id : trans_table().wide[combo][v ? 1 : 0];
 }

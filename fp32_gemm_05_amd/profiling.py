@@ -185,14 +185,17 @@ def cmd_report(args) -> None:
     tflops = flops / (avg_ns * 1e-9) / 1e12
     tflops_timed = flops / (timed_ns * 1e-9) / 1e12
     bench = "python -u bench.py --workload %s" % W
+    trace_opt = f"--trace-args='{args.trace_args}' " if args.trace_args else ""
     cmds = [
-        f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} --no-cpu-baseline",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} "
+        f"{args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
         f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
         f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
         "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE, then the three TCC_EA0_RDREQ_*_sum) --output-format csv -d <dir>/copy_fetch (copy_write, copy_rdreq) -o run -- python -u -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3",
-        f"python -m fp32_gemm_05_amd.profiling report --dir <dir> --workload {W} --variant {variant} --out-dir profiles",
+        f"python -m fp32_gemm_05_amd.profiling report --dir <dir> --workload {W} --variant {variant} "
+        f"{trace_opt}--out-dir profiles",
     ]
     lines = [
         f"# `{variant}` on {W}", "",
@@ -284,6 +287,8 @@ def main(argv=None) -> int:
     p.add_argument("--workload", required=True)
     p.add_argument("--variant", required=True)
     p.add_argument("--steps", type=int, default=200, help="timed steps of the traced bench run")
+    p.add_argument("--trace-args", default="", help="extra bench.py arguments of the traced run (e.g. a longer "
+                   "warmup, so that short kernels are traced at the ramped-up engine clock)")
     p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     p.add_argument("--note", default="")
     args = ap.parse_args(argv)
