@@ -6,7 +6,8 @@ resident in HBM before the timed region).  Default workload: M = N = K = 4096,
 A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
-                    [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline]
+                    [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline] [--cpu-full]
+                    [--cpu-threads N] [--cold] [--no-sclk]
 
 ``--op`` other than NN stores A as K x M and/or B as N x K and times
 ``sgemm_op`` (op(A) * op(B)) on the same logical product.
@@ -55,8 +56,9 @@ def stored_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0):
-    """Time the float64 oracle on a bounded sample of the same workload (leading rows of C).
+def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0, full: bool = False, threads: int = 0):
+    """Time the float64 oracle on a bounded sample of the same workload (leading rows of C), or on
+    the whole workload with full=True; threads <= 0 means all host threads.
 
     The oracle's values on those rows also check the GPU output of the first call.
     Returns (record for the JSON line, parity summary).
@@ -65,18 +67,29 @@ def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0):
 
     import oracle
 
-    threads = len(os.sched_getaffinity(0))
+    threads = threads if threads > 0 else len(os.sched_getaffinity(0))
     flops_per_row = 2.0 * w.N * w.K
     probe = min(w.M, 16)
     t0 = time.perf_counter()
     oracle.ref_rows(A, B, C0, w.alpha, w.beta, rows=(0, probe), nthreads=threads)
     t_probe = max(time.perf_counter() - t0, 1e-6)
     rate = probe * flops_per_row / t_probe
-    rows = int(min(w.M, max(probe, rate * target_s / flops_per_row)))
+    rows = w.M if full else int(min(w.M, max(probe, rate * target_s / flops_per_row)))
+    # in blocks of about 10 s, each logged, so that a long full-workload run shows progress
+    chunk = max(1, int(rate * 10.0 / flops_per_row))
+    parts_ref, parts_bound = [], []
     t0 = time.perf_counter()
-    ref, bound = oracle.ref_rows(A, B, C0, w.alpha, w.beta, rows=(0, rows), nthreads=threads)
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        rr, bb = oracle.ref_rows(A, B, C0, w.alpha, w.beta, rows=(r0, r1), nthreads=threads)
+        parts_ref.append(rr)
+        parts_bound.append(bb)
+        if rows > chunk:
+            log(f"oracle: rows {r1}/{rows} after {time.perf_counter() - t0:.1f} s")
     dt = time.perf_counter() - t0
-    used = oracle.max_threads()
+    ref = np.concatenate(parts_ref) if parts_ref else np.zeros((0, w.N))
+    bound = np.concatenate(parts_bound) if parts_bound else np.zeros((0, w.N))
+    used = min(threads, oracle.max_threads())
     got = out_gpu[:rows].astype(np.float64)
     err_ratio = np.abs(got - ref) / bound
     parity = {
@@ -94,6 +107,45 @@ def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0):
         "seconds": dt,
     }
     return rec, parity
+
+
+def sample_sclk(step, stream, seconds: float = 1.5):
+    """Engine clock under this kernel's sustained load: keep launching `step` for `seconds` while
+    `amd-smi metric -c` reads the clock of every XCD.  Returns {"mean_mhz", "min_mhz", "max_mhz"}
+    over the XCDs, or None when amd-smi is unavailable or fails."""
+    import json as _json
+    import shutil
+    import subprocess
+
+    import torch
+
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if exe is None:
+        return None
+    t_end = time.perf_counter() + seconds
+    for _ in range(20):  # get the queue busy before the query starts
+        step()
+    proc = subprocess.Popen([exe, "metric", "-g", "0", "-c", "--json"], stdout=subprocess.PIPE,
+                            stderr=subprocess.DEVNULL, text=True)
+    while time.perf_counter() < t_end or proc.poll() is None:
+        for _ in range(10):
+            step()
+        stream.synchronize() if hasattr(stream, "synchronize") else torch.cuda.synchronize()
+        if time.perf_counter() > t_end + 10:
+            proc.kill()
+            break
+    try:
+        out, _ = proc.communicate(timeout=10)
+        data = _json.loads(out)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                  if k.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        clocks = [float(c) for c in clocks if isinstance(c, (int, float))]
+        if not clocks:
+            return None
+        return {"mean_mhz": round(sum(clocks) / len(clocks), 1), "min_mhz": min(clocks), "max_mhz": max(clocks)}
+    except Exception:  # a missing or differently shaped report: no clock figure
+        return None
 
 
 def cpu_blocked_baseline(A, B, C0, w, reps: int = 3):
@@ -132,6 +184,13 @@ def main() -> int:
     ap.add_argument("--op", default="NN", choices=["NN", "NT", "TN", "TT"],
                     help="storage of A and B: op(A) op(B), T = stored transposed (sgemm_op)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on the whole workload instead of a bounded sample of rows")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: all host threads)")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 512 MiB buffer before every timed launch (evicts the caches, so the "
+                         "operands come from HBM); each launch is then timed between its own two events")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the engine-clock sample (amd-smi)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -189,27 +248,50 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    # K + 1 events on the kernels' stream: event i before step i, event i + 1 after it.  One event
-    # between consecutive launches (not two) keeps the stream as close to back-to-back as timing
-    # every launch allows; launch i's duration is elapsed(ev[i], ev[i + 1]).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = ev[0].elapsed_time(ev[args.steps])
-    per_launch = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    if args.cold:
+        # 512 MiB > the 256 MB Infinity Cache and every L2: the fill before each launch evicts the
+        # operands.  Launch i is timed between its own events (the fill is outside them).
+        flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for i in range(args.steps):
+            flush.fill_(float(i))
+            ev_s[i].record(stream)
+            step()
+            ev_e[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
+        total_ms = float(per_launch.sum())
+        del flush
+    else:
+        # K + 1 events on the kernels' stream: event i before step i, event i + 1 after it.  One
+        # event between consecutive launches (not two) keeps the stream as close to back-to-back as
+        # timing every launch allows; launch i's duration is elapsed(ev[i], ev[i + 1]).
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = ev[0].elapsed_time(ev[args.steps])
+        per_launch = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     ms_per_step = total_ms / args.steps
     flops = 2.0 * w.M * w.N * w.K
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(per_launch.mean())
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    log(f"timed {args.steps} steps: {total_ms:.3f} ms events, {wall * 1e3:.3f} ms wall; per launch "
-        f"mean {avg_launch_ms:.4f} ms, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
+    log(f"timed {args.steps} steps{' (cold)' if args.cold else ''}: {total_ms:.3f} ms events, "
+        f"{wall * 1e3:.3f} ms wall; per launch mean {avg_launch_ms:.4f} ms, median "
+        f"{float(np.median(per_launch)):.4f}, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
+    sclk = None if args.no_sclk else sample_sclk(step, stream)
+    if sclk is not None:
+        log(f"engine clock under this load (amd-smi, per XCD): {sclk}")
 
     is_mfma = info["kind"] == "mfma"
     peak = FP32_PEAK_TFLOPS if is_mfma else FP32_VALU_PEAK_TFLOPS
@@ -243,11 +325,16 @@ def main() -> int:
             "op": args.op, "variant": vname,
         },
         "pct_fp32_peak": round(100.0 * tflops / FP32_PEAK_TFLOPS, 2),
+        "median_ms": round(float(np.median(per_launch)), 5),
+        "min_ms": round(float(per_launch.min()), 5),
+        "cold": bool(args.cold),
+        "sclk_mhz": sclk,
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "pct_hbm_peak_alg": round(100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        rec, parity = cpu_baseline(A, B, C0, w, out_first)
+        rec, parity = cpu_baseline(A, B, C0, w, out_first, full=args.cpu_full, threads=args.cpu_threads)
         line["cpu_baseline"] = {k: rec[k] for k in ("value", "unit", "cores", "kind", "sample")}
         line["cpu_baseline"]["value"] = round(rec["value"], 6)
         line["parity"] = parity

@@ -7,7 +7,9 @@ the first call, and a missing library raises instead of falling back to any
 other implementation.
 """
 from ._binding import (  # noqa: F401
+    SgemmArgumentError,
     SgemmError,
+    SgemmLaunchError,
     gemm,
     library_path,
     load_library,

@@ -24,7 +24,8 @@ _OP_ARG_NAMES = {1: "transa", 2: "transb", **{k + 2: v for k, v in _ARG_NAMES.it
 
 
 class SgemmError(RuntimeError):
-    """A non-zero return code of the C ABI (``code`` holds it)."""
+    """A non-zero return code of the C ABI (``code`` holds it).  Raised as one of the two
+    subclasses below."""
 
     def __init__(self, code: int, where: str):
         self.code = code
@@ -34,6 +35,18 @@ class SgemmError(RuntimeError):
         else:
             what = f"kernel launch failed with hipError_t {code}"
         super().__init__(f"{where}: {what}")
+
+
+class SgemmArgumentError(SgemmError, ValueError):
+    """A negative return code: argument ``-code`` is invalid; nothing was enqueued."""
+
+
+class SgemmLaunchError(SgemmError):
+    """A positive return code: the kernel launch failed with that hipError_t."""
+
+
+def _error(code: int, where: str) -> SgemmError:
+    return (SgemmArgumentError if code < 0 else SgemmLaunchError)(code, where)
 
 
 def library_path() -> str:
@@ -105,7 +118,7 @@ def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
     rc = load_library().sgemm(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb),
                               float(beta), _ptr(C), int(ldc), _stream(stream))
     if rc != 0:
-        raise SgemmError(rc, "sgemm")
+        raise _error(rc, "sgemm")
 
 
 def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, variant=-1):
@@ -113,7 +126,7 @@ def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, variant=
     rc = load_library().sgemm_ex(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb),
                                  float(beta), _ptr(C), int(ldc), _stream(stream), int(variant))
     if rc != 0:
-        raise SgemmError(rc, "sgemm_ex")
+        raise _error(rc, "sgemm_ex")
 
 
 def _trans(t) -> bytes:
@@ -131,7 +144,7 @@ def sgemm_op(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, strea
     rc = load_library().sgemm_op(_trans(transa), _trans(transb), int(M), int(N), int(K), float(alpha), _ptr(A),
                                  int(lda), _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc), _stream(stream))
     if rc != 0:
-        raise SgemmError(rc, "sgemm_op")
+        raise _error(rc, "sgemm_op")
 
 
 def sgemm_op_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, variant=-1):
@@ -140,7 +153,7 @@ def sgemm_op_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st
                                     _ptr(A), int(lda), _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
                                     _stream(stream), int(variant))
     if rc != 0:
-        raise SgemmError(rc, "sgemm_op_ex")
+        raise _error(rc, "sgemm_op_ex")
 
 
 def sgemm_num_variants() -> int:

@@ -295,3 +295,15 @@ def test_binding_error_names_the_op_argument():
         sg.sgemm_op("T", "N", 8, 4, 4, 1.0, FAKE_A, 7, FAKE_B, 4, 0.0, FAKE_C, 4, stream=0)
     with pytest.raises(sg.SgemmError, match=r"argument 1 \(transa\)"):
         sg.sgemm_op("X", "N", 8, 4, 4, 1.0, FAKE_A, 8, FAKE_B, 4, 0.0, FAKE_C, 4, stream=0)
+
+
+def test_binding_error_classes():
+    """Negative codes raise SgemmArgumentError (also a ValueError), positive ones SgemmLaunchError;
+    both are SgemmError."""
+    with pytest.raises(ValueError) as e:
+        sg.sgemm(-1, 4, 4, 1.0, FAKE_A, 4, FAKE_B, 4, 0.0, FAKE_C, 4, stream=0)
+    assert isinstance(e.value, sg.SgemmArgumentError) and isinstance(e.value, sg.SgemmError)
+    assert e.value.code == -1
+    err = _binding._error(1, "sgemm")
+    assert isinstance(err, sg.SgemmLaunchError) and not isinstance(err, ValueError)
+    assert "hipError_t 1" in str(err)

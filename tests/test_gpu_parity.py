@@ -381,3 +381,61 @@ def test_full_size_sampled(wname, kind):
         worst = check_within_bound(got, ref, bound, f"full {w.name}")
         _say(f"[full] {w.name}: max err/bound over {len(I)} points = {worst:.3g}")
     assert np.all(np.isfinite(out))
+
+
+# ------------------------------------------------------------------------------------------
+# sub-matrices through pointer offsets, and subnormal behaviour
+# ------------------------------------------------------------------------------------------
+
+def test_submatrix_call_equals_block_of_full_product():
+    """A call on a block -- A's rows i0.., B's columns j0.., through pointer offsets with the full
+    leading dimensions -- equals that block of the full product (integer data: exact)."""
+    w = WORKLOADS["ragged3001x5003x777"].as_int()
+    M, N, K = 300, 260, 96
+    A, B, C = make_inputs(w, M=M, N=N, K=K)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    full = torch.from_numpy(C).cuda()
+    sg.sgemm(M, N, K, w.alpha, dA, K, dB, N, w.beta, full, N)
+    for (i0, i1, j0, j1) in [(0, 128, 0, 128), (37, 261, 5, 203), (129, 300, 131, 260), (299, 300, 0, 1)]:
+        blk = torch.from_numpy(C).cuda()  # same starting C, block updated in place
+        ptrA = dA.data_ptr() + i0 * K * 4
+        ptrB = dB.data_ptr() + j0 * 4
+        ptrC = blk.data_ptr() + (i0 * N + j0) * 4
+        _say(f"[submatrix] rows {i0}:{i1} cols {j0}:{j1}")
+        sg.sgemm(i1 - i0, j1 - j0, K, w.alpha, ptrA, K, ptrB, N, w.beta, ptrC, N)
+        torch.cuda.synchronize()
+        got = blk.cpu().numpy()
+        ref = full.cpu().numpy()
+        assert np.array_equal(got[i0:i1, j0:j1], ref[i0:i1, j0:j1])
+        outside = np.ones((M, N), bool)
+        outside[i0:i1, j0:j1] = False
+        assert np.array_equal(got[outside], C[outside]), "a store outside the block"
+
+
+def _subnormal_case(vid, a_val, b_val, K=8):
+    M, N = 64, 64
+    A = np.full((M, K), a_val, np.float32)
+    B = np.full((K, N), b_val, np.float32)
+    C = np.zeros((M, N), np.float32)
+    got, _, _ = run_gemm(A, B, C, 1.0, 0.0, variant=vid)
+    return got
+
+
+@pytest.mark.parametrize("vid", [v[0] for v in VARIANTS
+                                 if "_o4" not in v[1] and "_wide" not in v[1] and "mfma32k" not in v[1]],
+                         ids=[v[1] for v in VARIANTS
+                              if "_o4" not in v[1] and "_wide" not in v[1] and "mfma32k" not in v[1]])
+def test_subnormal_behaviour_recorded(vid):
+    """Records whether a variant keeps fp32 subnormals (the method does not fix this; either way
+    is accepted): products 2^-70 * 2^-70 = 2^-140 (subnormal results), and subnormal inputs
+    2^-130 * 2^10 = 2^-120 (normal results).  Each output must be the exact value or zero."""
+    name = sg.sgemm_variant_name(vid)
+    sub_out = _subnormal_case(vid, 2.0 ** -70, 2.0 ** -70)          # exact: 8 * 2^-140 = 2^-137
+    sub_in = _subnormal_case(vid, 2.0 ** -130, 2.0 ** 10)           # exact: 8 * 2^-120 = 2^-117
+    outs = {}
+    for label, got, exact in [("subnormal results", sub_out, 2.0 ** -137), ("subnormal inputs", sub_in, 2.0 ** -117)]:
+        vals = set(np.unique(got.astype(np.float64)).tolist())
+        assert vals <= {exact, 0.0}, (name, label, vals)
+        outs[label] = "kept" if vals == {exact} else ("flushed" if vals == {0.0} else "mixed")
+    _say(f"[subnormal] {name}: results {outs['subnormal results']}, inputs {outs['subnormal inputs']}")

@@ -340,3 +340,37 @@ def test_bad_arguments_rejected():
         oracle.ref_points(A, B, C, [3], [0], 1.0, 0.0)
     with pytest.raises(ValueError):
         oracle.ref_rows(A, np.zeros((5, 5), np.float32), C, 1.0, 0.0)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", ["square1024_beta", "ragged3001x5003x777", "skinny65536x64x1024"])
+def test_integer_workloads_exact_full(wname):
+    """Integer-valued inputs at the workloads' own sizes: the loop oracle equals an independent exact
+    path (float64 BLAS product of integer matrices: every partial sum is an integer far below 2^53,
+    so it is exact, as are alpha*s and beta*c for the dyadic alpha, beta)."""
+    from fp32_gemm_05_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[wname].as_int()
+    A, B, C = make_inputs(w)
+    ref, _ = oracle.ref_rows(A, B, C, w.alpha, w.beta)
+    exact = w.alpha * (A.astype(np.float64) @ B.astype(np.float64))
+    if w.beta != 0:
+        exact += w.beta * C.astype(np.float64)
+    assert np.array_equal(ref, exact)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", ["square4096", "square8192"])
+def test_integer_workloads_exact_sampled(wname):
+    """The large integer workloads, on sampled outputs: the loop oracle's points equal int64 dot
+    products of the sampled rows and columns."""
+    from fp32_gemm_05_amd.workloads import WORKLOADS, make_inputs, sample_points
+    w = WORKLOADS[wname].as_int()
+    A, B, C = make_inputs(w)
+    I, J = sample_points(w.M, w.N, n_random=512, seed=w.seed, tile=128)
+    ref, _ = oracle.ref_points(A, B, C, I, J, w.alpha, w.beta)
+    Ai = A.astype(np.int64)
+    Bi = B.astype(np.int64)
+    exact = np.array([w.alpha * float(Ai[i] @ Bi[:, j]) for i, j in zip(I, J)])
+    if w.beta != 0:
+        exact += w.beta * C[I, J].astype(np.float64)
+    assert np.array_equal(ref, exact)
