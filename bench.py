@@ -7,7 +7,7 @@ A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
                     [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline] [--cpu-full]
-                    [--cpu-threads N] [--cold] [--no-sclk]
+                    [--cpu-threads N] [--cold]
 
 ``--op`` other than NN stores A as K x M and/or B as N x K and times
 ``sgemm_op`` (op(A) * op(B)) on the same logical product.
@@ -109,45 +109,6 @@ def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0, full: bool = Fals
     return rec, parity
 
 
-def sample_sclk(step, stream, seconds: float = 1.5):
-    """Engine clock under this kernel's sustained load: keep launching `step` for `seconds` while
-    `amd-smi metric -c` reads the clock of every XCD.  Returns {"mean_mhz", "min_mhz", "max_mhz"}
-    over the XCDs, or None when amd-smi is unavailable or fails."""
-    import json as _json
-    import shutil
-    import subprocess
-
-    import torch
-
-    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
-    if exe is None:
-        return None
-    t_end = time.perf_counter() + seconds
-    for _ in range(20):  # get the queue busy before the query starts
-        step()
-    proc = subprocess.Popen([exe, "metric", "-g", "0", "-c", "--json"], stdout=subprocess.PIPE,
-                            stderr=subprocess.DEVNULL, text=True)
-    while time.perf_counter() < t_end or proc.poll() is None:
-        for _ in range(10):
-            step()
-        stream.synchronize() if hasattr(stream, "synchronize") else torch.cuda.synchronize()
-        if time.perf_counter() > t_end + 10:
-            proc.kill()
-            break
-    try:
-        out, _ = proc.communicate(timeout=10)
-        data = _json.loads(out)
-        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
-                  if k.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
-        clocks = [float(c) for c in clocks if isinstance(c, (int, float))]
-        if not clocks:
-            return None
-        return {"mean_mhz": round(sum(clocks) / len(clocks), 1), "min_mhz": min(clocks), "max_mhz": max(clocks)}
-    except Exception:  # a missing or differently shaped report: no clock figure
-        return None
-
-
 def cpu_blocked_baseline(A, B, C0, w, reps: int = 3):
     """Time the cache-blocked CPU SGEMM (cpu_blocked/) on the whole workload, on all host threads:
     one untimed call, then the best of `reps` timed calls."""
@@ -190,7 +151,6 @@ def main() -> int:
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 512 MiB buffer before every timed launch (evicts the caches, so the "
                          "operands come from HBM); each launch is then timed between its own two events")
-    ap.add_argument("--no-sclk", action="store_true", help="skip the engine-clock sample (amd-smi)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -289,9 +249,6 @@ def main() -> int:
     log(f"timed {args.steps} steps{' (cold)' if args.cold else ''}: {total_ms:.3f} ms events, "
         f"{wall * 1e3:.3f} ms wall; per launch mean {avg_launch_ms:.4f} ms, median "
         f"{float(np.median(per_launch)):.4f}, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
-    sclk = None if args.no_sclk else sample_sclk(step, stream)
-    if sclk is not None:
-        log(f"engine clock under this load (amd-smi, per XCD): {sclk}")
 
     is_mfma = info["kind"] == "mfma"
     peak = FP32_PEAK_TFLOPS if is_mfma else FP32_VALU_PEAK_TFLOPS
@@ -328,7 +285,6 @@ def main() -> int:
         "median_ms": round(float(np.median(per_launch)), 5),
         "min_ms": round(float(per_launch.min()), 5),
         "cold": bool(args.cold),
-        "sclk_mhz": sclk,
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pct_hbm_peak_alg": round(100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,

@@ -71,6 +71,19 @@ def _read_counters(path: str, kernel_substr: str):
     return out
 
 
+def _dispatches(path: str, kernel_substr: str):
+    """[(counters dict, duration ns)] per dispatch of the matching kernel, in dispatch order."""
+    per = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if kernel_substr not in row["Kernel_Name"]:
+                continue
+            d = per.setdefault(int(row["Dispatch_Id"]), [{}, 0])
+            d[0][row["Counter_Name"]] = float(row["Counter_Value"])
+            d[1] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    return [tuple(per[k]) for k in sorted(per)]
+
+
 def _mean(xs):
     return sum(xs) / len(xs) if xs else float("nan")
 
@@ -180,19 +193,26 @@ def cmd_report(args) -> None:
         128 * rd.get("TCC_EA0_RDREQ_128B_sum", 0.0)
     gui = sq.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
     mfma_util = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (N_SIMD * gui)
+    # the last dispatch of the counter run (after its warmup): engine clock = active cycles per XCD
+    # over the dispatch's duration, and that dispatch's MFMA busy fraction
+    last_c, last_ns = _dispatches(os.path.join(d, f"sq_{W}", "run_counter_collection.csv"), "sgemm")[-1]
+    last_gui = last_c.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
+    sclk_last = last_gui / last_ns if last_ns > 0 else float("nan")  # cycles per ns = GHz
+    mfma_last = last_c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (N_SIMD * last_gui)
     lds_conf = sq.get("SQ_LDS_BANK_CONFLICT", float("nan")) / (N_CU * gui)
     expect_mfma = w.M * w.N * w.K / 2048.0  # 32x32x2 MFMAs of the exact problem (no tile padding)
     tflops = flops / (avg_ns * 1e-9) / 1e12
     tflops_timed = flops / (timed_ns * 1e-9) / 1e12
     bench = "python -u bench.py --workload %s" % W
     trace_opt = f"--trace-args='{args.trace_args}' " if args.trace_args else ""
+    sq_warm = args.sq_warmup
     cmds = [
         f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} "
         f"{args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
         f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
-        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup {sq_warm} --no-cpu-baseline",
         "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE, then the three TCC_EA0_RDREQ_*_sum) --output-format csv -d <dir>/copy_fetch (copy_write, copy_rdreq) -o run -- python -u -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3",
         f"python -m fp32_gemm_05_amd.profiling report --dir <dir> --workload {W} --variant {variant} "
         f"{trace_opt}--out-dir profiles",
@@ -222,7 +242,12 @@ def cmd_report(args) -> None:
         "", "## Derived", "",
         f"* MFMA instructions: {sq.get('SQ_INSTS_MFMA', float('nan')):.6g} (the problem needs M*N*K/2048 = "
         f"{expect_mfma:.6g} v_mfma_f32_32x32x2_f32; the rest is tile padding at ragged edges)",
-        f"* MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) = {100 * mfma_util:.1f} %",
+        f"* MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) = {100 * mfma_util:.1f} % "
+        f"(mean over the counter run's dispatches); {100 * mfma_last:.1f} % in its last dispatch",
+        (f"* Engine clock in the counter run's last dispatch: GRBM_GUI_ACTIVE / 8 XCDs / duration = "
+         f"{sclk_last:.2f} GHz ({last_ns / 1e3:.1f} us under counter collection)" if last_ns >= 150_000 else
+         f"* Engine clock: not derived (a {last_ns / 1e3:.1f} us dispatch is too short: GRBM_GUI_ACTIVE also "
+         f"counts cycles of the counter collection around it, which also lowers the MFMA busy figure)"),
         f"* LDS bank-conflict cycles per CU-cycle: SQ_LDS_BANK_CONFLICT / (256 CUs x GRBM_GUI_ACTIVE / 8) = "
         f"{100 * lds_conf:.2f} %",
         f"* Copy calibration: a {copy_bytes / 2**20:.0f} MiB device copy reads FETCH_SIZE {cfetch:.6g} KiB "
@@ -243,7 +268,8 @@ def cmd_report(args) -> None:
            "FETCH_SIZE_KiB_per_launch": fetch, "WRITE_SIZE_KiB_per_launch": write,
            "fetch_scale": f_scale, "write_scale": w_scale, "hbm_bytes_per_launch": hbm,
            "l2_read_bytes_by_request_size": rd_bytes, "algorithmic_bytes_per_launch": alg_bytes,
-           "mfma_busy": mfma_util, "lds_bank_conflict_per_cu_cycle": lds_conf,
+           "mfma_busy": mfma_util, "mfma_busy_last_dispatch": mfma_last, "sclk_ghz_last_dispatch": sclk_last if last_ns >= 150_000 else None,
+           "lds_bank_conflict_per_cu_cycle": lds_conf,
            "kernel_source_hash": kernel_source_hash(), "commands": cmds}
     with open(os.path.join(args.out_dir, f"traffic_{variant}_{W}.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -287,6 +313,7 @@ def main(argv=None) -> int:
     p.add_argument("--workload", required=True)
     p.add_argument("--variant", required=True)
     p.add_argument("--steps", type=int, default=200, help="timed steps of the traced bench run")
+    p.add_argument("--sq-warmup", type=int, default=1, help="bench warmup of the SQ counter run")
     p.add_argument("--trace-args", default="", help="extra bench.py arguments of the traced run (e.g. a longer "
                    "warmup, so that short kernels are traced at the ramped-up engine clock)")
     p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
