@@ -439,3 +439,49 @@ def test_subnormal_behaviour_recorded(vid):
         assert vals <= {exact, 0.0}, (name, label, vals)
         outs[label] = "kept" if vals == {exact} else ("flushed" if vals == {0.0} else "mixed")
     _say(f"[subnormal] {name}: results {outs['subnormal results']}, inputs {outs['subnormal inputs']}")
+
+
+# ------------------------------------------------------------------------------------------
+# large extents: C beyond 4 GiB (64-bit element offsets in the epilogue), very tall and very
+# long operands, K = 1
+# ------------------------------------------------------------------------------------------
+
+LARGE = [
+    # (label, M, N, K, dist, alpha, beta)
+    ("c_over_4gib", 33000, 33003, 8, "int", 1.0, 0.0),
+    ("tall_n1", 1_000_003, 1, 64, "int", 0.5, 0.0),
+    ("long_k", 96, 80, 1_000_001, "int", 1.0, 0.0),
+    ("k1_wide", 4099, 20000, 1, "uniform", 2.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("label,M,N,K,dist,alpha,beta", LARGE, ids=[x[0] for x in LARGE])
+def test_large_extents_sampled(label, M, N, K, dist, alpha, beta):
+    """Default dispatch on extreme shapes; sampled outputs (random points plus tile-boundary rows
+    and columns) against the oracle's loop, integer data exactly."""
+    rng = np.random.default_rng(len(label) * 1000 + K)
+    if dist == "int":
+        A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+        B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+    else:
+        A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    assert beta == 0.0  # C is neither read by the library nor needed by the oracle
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    vid = sg.sgemm_select_variant(M, N, K, dA, K, dB, N, dC, N)
+    _say(f"[large] {label} {M}x{N}x{K} variant={sg.sgemm_variant_name(vid)}")
+    sg.sgemm(M, N, K, alpha, dA, K, dB, N, beta, dC, N)
+    torch.cuda.synchronize()
+    I, J = sample_points(M, N, n_random=1024, seed=K, tile=128)
+    I = np.concatenate([I, [M - 1, M - 1, 0]])
+    J = np.concatenate([J, [N - 1, 0, N - 1]])
+    got = dC[torch.from_numpy(I).cuda(), torch.from_numpy(J).cuda()].cpu().numpy()
+    ref, bound = oracle.ref_points(A, B, None, I, J, alpha, beta)
+    if dist == "int":
+        check_exact(got, ref, label)
+    else:
+        check_within_bound(got, ref, bound, label)
+    del dA, dB, dC
+    torch.cuda.empty_cache()
