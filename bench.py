@@ -227,28 +227,39 @@ def main() -> int:
         total_ms = float(per_launch.sum())
         del flush
     else:
-        # K + 1 events on the kernels' stream: event i before step i, event i + 1 after it.  One
-        # event between consecutive launches (not two) keeps the stream as close to back-to-back as
-        # timing every launch allows; launch i's duration is elapsed(ev[i], ev[i + 1]).
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        # Two events on the kernels' stream bracket the K back-to-back launches; the mean launch
+        # duration is the timed region over K (events between launches would add their own gaps).
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
-        ev[0].record(stream)
+        ev0.record(stream)
         for i in range(args.steps):
             step()
-            ev[i + 1].record(stream)
+        ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        total_ms = ev[0].elapsed_time(ev[args.steps])
-        per_launch = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+        total_ms = ev0.elapsed_time(ev1)
+        # the spread of single launches, from a separate pass after the timed region
+        n_spread = min(args.steps, 50)
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+        ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+        for i in range(n_spread):
+            ev_s[i].record(stream)
+            step()
+            ev_e[i].record(stream)
+        torch.cuda.synchronize()
+        per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
     ms_per_step = total_ms / args.steps
     flops = 2.0 * w.M * w.N * w.K
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    avg_launch_ms = float(per_launch.mean())
+    # cold: the mean of the individually timed launches (the fills between them are excluded);
+    # warm: the timed region over K
+    avg_launch_ms = float(per_launch.mean()) if args.cold else ms_per_step
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     log(f"timed {args.steps} steps{' (cold)' if args.cold else ''}: {total_ms:.3f} ms events, "
-        f"{wall * 1e3:.3f} ms wall; per launch mean {avg_launch_ms:.4f} ms, median "
-        f"{float(np.median(per_launch)):.4f}, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
+        f"{wall * 1e3:.3f} ms wall; mean launch {avg_launch_ms:.4f} ms; {len(per_launch)} single launches: "
+        f"median {float(np.median(per_launch)):.4f}, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
 
     is_mfma = info["kind"] == "mfma"
     peak = FP32_PEAK_TFLOPS if is_mfma else FP32_VALU_PEAK_TFLOPS
@@ -282,8 +293,8 @@ def main() -> int:
             "op": args.op, "variant": vname,
         },
         "pct_fp32_peak": round(100.0 * tflops / FP32_PEAK_TFLOPS, 2),
-        "median_ms": round(float(np.median(per_launch)), 5),
-        "min_ms": round(float(per_launch.min()), 5),
+        "launch_median_ms": round(float(np.median(per_launch)), 5),
+        "launch_min_ms": round(float(per_launch.min()), 5),
         "cold": bool(args.cold),
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pct_hbm_peak_alg": round(100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
