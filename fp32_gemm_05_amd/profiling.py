@@ -3,6 +3,9 @@
     python -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3
         a plain device-to-device copy of known size; run under `rocprofv3 --pmc FETCH_SIZE`
         (then WRITE_SIZE) it calibrates how many bytes one KiB of each counter stands for.
+    python -m fp32_gemm_05_amd.profiling read --mib 256 [--cold]
+        a streaming read of known size (torch's sum), warm or after evicting the caches: the
+        read bandwidth an HBM-bound kernel can expect under the same protocol.
     python -m fp32_gemm_05_amd.profiling stats <kernel_stats.csv> --command "..." --out X.md
         short text summary of a `rocprofv3 --kernel-trace --stats` run.
     python -m fp32_gemm_05_amd.profiling traffic --kernel SUBSTR --fetch F.csv --write W.csv
@@ -54,6 +57,34 @@ def run_copy(mib: int, reps: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"copy: {reps} x {mib} MiB device-to-device ({2 * mib} MiB of traffic each)", flush=True)
+
+
+def run_read(mib: int, reps: int, cold: bool) -> None:
+    """Read-bandwidth reference: torch's sum over `mib` MiB (a streaming read), timed between
+    events; with cold, a 512 MiB buffer is overwritten before every timed read (the protocol of
+    bench.py --cold), so the data comes from HBM."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if cold else None
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        torch.sum(x, dim=0, out=out)
+    times = []
+    for i in range(reps):
+        if cold:
+            flush.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(x, dim=0, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    med = times[len(times) // 2]
+    print(f"read: {mib} MiB {'cold' if cold else 'warm'}, median {med * 1e3:.1f} us over {reps} -> "
+          f"{mib * 1024 * 1024 / (med * 1e-3) / 1e12:.2f} TB/s", flush=True)
 
 
 def _read_counters(path: str, kernel_substr: str):
@@ -282,6 +313,10 @@ def main(argv=None) -> int:
     p = sub.add_parser("copy")
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=3)
+    p = sub.add_parser("read")
+    p.add_argument("--mib", type=int, default=256)
+    p.add_argument("--reps", type=int, default=50)
+    p.add_argument("--cold", action="store_true")
     p = sub.add_parser("stats")
     p.add_argument("csv")
     p.add_argument("--title", default="")
@@ -323,6 +358,8 @@ def main(argv=None) -> int:
         cmd_report(args)
     elif args.cmd == "copy":
         run_copy(args.mib, args.reps)
+    elif args.cmd == "read":
+        run_read(args.mib, args.reps, args.cold)
     elif args.cmd == "stats":
         cmd_stats(args)
     elif args.cmd == "traffic":
