@@ -1,0 +1,182 @@
+// sgemm_launch.hpp -- the kernel variants of libsgemm: how each is launched (grid, block,
+// workgroup-to-tile grouping) and the table of all variants with their tile parameters.
+// Included by sgemm.hip only, inside its anonymous namespace; the kernels themselves are in
+// sgemm_kernels.hpp.  Together these two files fix what runs on the GPU for a given variant;
+// which variant runs for a given call is decided in sgemm.hip and tuned_table.inc.
+#pragma once
+
+using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
+
+enum Kind { kMfma = 0, kValu = 1 };
+
+struct Variant {
+    const char* name;
+    int kind;
+    int bm, bn, bk, wm, wn;  // wm/wn: MFMA wave tile, or VALU microtile tm/tn
+    int threads;
+    int vec;
+    int lds_bytes;
+    LaunchFn launch;
+    int wide;  // 64-bit per-lane load offsets (no 4 GiB limit on one workgroup's operand span)
+    int ks;    // k-groups sharing one tile inside a workgroup (split-K); 0 means 1
+    int ta;    // op(A) = A^T: A stored K x M
+    int tb;    // op(B) = B^T: B stored N x K
+};
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Tile-rows per group of the workgroup -> tile map.  Measured on 4096^3 and 8192^3 with the
+// 128x128 tile over groups of 4, 8, 16 and 32 rows, with and without the XCD renumbering:
+// 4096^3 is insensitive (all within 0.3 %), 8192^3 is fastest with the renumbering and groups
+// of 4 (151.6 TFLOP/s against 148.5-150.4 for 8 and 16).
+int group_rows(int tiles_m, int tiles_n) {
+    (void)tiles_n;
+    return tiles_m < 4 ? tiles_m : 4;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false>
+hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
+hipError_t launch_mfma_pipe(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool VEC>
+hipError_t launch_mfma_splitk(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_splitk_kernel<BM, BN, BK, WM, WN, KS, VEC>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
+template <int BM, int BN, int BK, int TM, int TN, bool VEC, bool WIDE>
+hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_valu_kernel<BM, BN, BK, TM, TN, VEC, WIDE>),
+                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+}
+
+#define MFMA_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, NAME)                                       \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma<BM, BN, BK, WM, WN, VEC, OCC, false>, 0}
+#define WIDE_MFMA_VARIANT(BM, BN, BK, WM, WN, VEC, NAME)                                         \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, true>, 1}
+#define VALU_VARIANT(BM, BN, BK, TM, TN, VEC, SUFFIX)                                             \
+    {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN SUFFIX, kValu, BM, BN, BK, TM, TN,              \
+     ValuCfg<BM, BN, BK, TM, TN, VEC>::NT, VEC, ValuCfg<BM, BN, BK, TM, TN, VEC>::LDS_BYTES,     \
+     &launch_valu<BM, BN, BK, TM, TN, VEC, false>, 0}
+#define MFMA_NAME(BM, BN, BK, WM, WN) "mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
+#define BOTH_MFMA(BM, BN, BK, WM, WN)                                                       \
+    MFMA_VARIANT(BM, BN, BK, WM, WN, 0, true, MFMA_NAME(BM, BN, BK, WM, WN) "_vec"),        \
+        MFMA_VARIANT(BM, BN, BK, WM, WN, 0, false, MFMA_NAME(BM, BN, BK, WM, WN) "_scalar")
+// vector-load form only, with an occupancy target of OCC waves per SIMD
+#define VEC_MFMA_OCC(BM, BN, BK, WM, WN, OCC) \
+    MFMA_VARIANT(BM, BN, BK, WM, WN, OCC, true, MFMA_NAME(BM, BN, BK, WM, WN) "_o" #OCC "_vec")
+#define PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, NAME)                                       \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_pipe<BM, BN, BK, WM, WN, VEC, OCC, false>, 0}
+#define PIPE_NAME(BM, BN, BK, WM, WN, OCC) "mfma32p_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_o" #OCC
+#define BOTH_PIPE(BM, BN, BK, WM, WN, OCC)                                                      \
+    PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, true, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_vec"),     \
+        PIPE_VARIANT(BM, BN, BK, WM, WN, OCC, false, PIPE_NAME(BM, BN, BK, WM, WN, OCC) "_scalar")
+#define SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, VEC, NAME)                                     \
+    {NAME, kMfma, BM, BN, BK, WM, WN, SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>::NT, VEC,            \
+     SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>::LDS_BYTES, &launch_mfma_splitk<BM, BN, BK, WM, WN, KS, VEC>, 0, KS}
+#define SPLITK_NAME(BM, BN, BK, WM, WN, KS) "mfma32k" #KS "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
+#define BOTH_SPLITK(BM, BN, BK, WM, WN, KS)                                                     \
+    SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, true, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_vec"),   \
+        SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, false, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_scalar")
+#define TRANS_VARIANT(BM, BN, BK, WM, WN, VEC, WIDE, TA, TB, NAME)                              \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT, VEC,          \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::LDS_BYTES,                                         \
+     &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, WIDE, TA, TB>, WIDE, 0, TA, TB}
+// the variants of one transposition (TAG: "nt", "tn" or "tt"; first letter op(A), second op(B))
+#define TRANS_SET(TA, TB, TAG)                                                                     \
+    TRANS_VARIANT(128, 128, 16, 64, 64, true, false, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_vec"),     \
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, false, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_scalar"), \
+        TRANS_VARIANT(64, 64, 32, 32, 32, true, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_vec"),         \
+        TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
+        TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
+#define DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, NAME)                                             \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0>, 0}
+#define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
+#define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
+    DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
+        DEEP_VARIANT(BM, BN, BK, WM, WN, false, DEEP_NAME(BM, BN, BK, WM, WN) "_scalar")
+#define BOTH_VALU(BM, BN, BK, TM, TN) \
+    VALU_VARIANT(BM, BN, BK, TM, TN, true, "_vec"), VALU_VARIANT(BM, BN, BK, TM, TN, false, "_scalar")
+
+// The variant table.  Ids are positions in this table.
+const Variant kVariants[] = {
+    BOTH_MFMA(128, 128, 16, 64, 64),
+    BOTH_MFMA(128, 128, 32, 64, 64),
+    BOTH_MFMA(256, 128, 16, 128, 64),
+    BOTH_MFMA(128, 256, 16, 64, 128),
+    BOTH_MFMA(256, 64, 16, 64, 64),
+    BOTH_MFMA(64, 64, 16, 32, 32),
+    BOTH_MFMA(64, 64, 32, 32, 32),
+    VEC_MFMA_OCC(128, 128, 16, 64, 64, 4),
+    MFMA_VARIANT(128, 128, 16, 64, 64, 4, false, MFMA_NAME(128, 128, 16, 64, 64) "_o4_scalar"),
+    VEC_MFMA_OCC(128, 128, 32, 64, 64, 2),
+    PIPE_VARIANT(128, 128, 32, 64, 64, 2, true, PIPE_NAME(128, 128, 32, 64, 64, 2) "_vec"),
+    BOTH_PIPE(256, 128, 16, 64, 64, 2),
+    BOTH_PIPE(64, 64, 16, 32, 32, 4),
+    BOTH_PIPE(256, 64, 16, 64, 64, 2),
+    PIPE_VARIANT(128, 256, 16, 64, 128, 2, true, PIPE_NAME(128, 256, 16, 64, 128, 2) "_vec"),
+    PIPE_VARIANT(256, 128, 16, 128, 64, 2, true, PIPE_NAME(256, 128, 16, 128, 64, 2) "_vec"),
+    BOTH_SPLITK(64, 64, 32, 32, 32, 2),
+    BOTH_SPLITK(64, 64, 32, 32, 32, 4),
+    BOTH_MFMA(64, 64, 64, 32, 32),
+    BOTH_MFMA(128, 64, 32, 64, 64),
+    BOTH_MFMA(128, 64, 64, 64, 64),
+    BOTH_MFMA(64, 64, 32, 64, 32),
+    BOTH_VALU(128, 128, 8, 8, 8),
+    BOTH_VALU(64, 64, 16, 4, 4),
+    // 64-bit offsets: used whenever one workgroup's operand span does not fit 32-bit offsets
+    WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, true, MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec"),
+    WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, false, MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
+    // deep prefetch (one wave per SIMD)
+    BOTH_DEEP(64, 64, 32, 32, 32),
+    BOTH_DEEP(64, 64, 64, 32, 32),
+    // transposed operands (sgemm_op): op(A) x op(B) = N x T, T x N, T x T
+    TRANS_SET(false, true, "nt"),
+    TRANS_SET(true, false, "tn"),
+    TRANS_SET(true, true, "tt"),
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

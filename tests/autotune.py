@@ -43,13 +43,27 @@ CASES = [
     ("ragged2500x3500x1000", "shallow", "ragged3001x5003x777", 2500, 3500, 1000, None, None, None, False),
     ("shallow4096x4096x512", "shallow", "square4096", 4096, 4096, 512, None, None, None, True),
     ("shallow3072x3072x768", "shallow", "square1024_beta", 3072, 3072, 768, None, None, None, True),
+    ("medium2585x6716x2000", "medium", "square4096", 2585, 6716, 2000, None, None, None, True),
+    ("medium3000x3000x3000", "medium", "square4096", 3000, 3000, 3000, None, None, None, True),
+    ("medium2062x3171x3921", "medium", "ragged3001x5003x777", 2062, 3171, 3921, None, None, None, False),
+    ("medium5000x2001x2501", "medium", "ragged3001x5003x777", 5000, 2001, 2501, None, None, None, False),
+    ("tinyk5555x1124x68", "tiny_k", "square4096", 5555, 1124, 68, None, None, None, True),
+    ("tinyk1953x2052x72", "tiny_k", "square4096", 1953, 2052, 72, None, None, None, True),
+    ("tinyk8192x8192x32", "tiny_k", "square4096", 8192, 8192, 32, None, None, None, True),
+    ("tinyk3001x4001x101", "tiny_k", "ragged3001x5003x777", 3001, 4001, 101, None, None, None, False),
+    ("tinyk2048x2047x33", "tiny_k", "ragged3001x5003x777", 2048, 2047, 33, None, None, None, False),
+    ("longk1024x1024x4096", "small_longk", "square1024_beta", 1024, 1024, 4096, None, None, None, True),
+    ("longk1089x728x5752", "small_longk", "square4096", 1089, 728, 5752, None, None, None, True),
+    ("longk1751x907x5323", "small_longk", "ragged3001x5003x777", 1751, 907, 5323, None, None, None, False),
+    ("longk777x1501x3001", "small_longk", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
     ("square256", "small", "square256", None, None, None, None, None, None, True),
     ("square1024_beta", "small", "square1024_beta", None, None, None, None, None, None, True),
     ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
     ("skinny65536x64x1024", "skinny", "skinny65536x64x1024", None, None, None, None, None, None, True),
     ("skinny65536x61x1021", "skinny", "skinny65536x64x1024", 65536, 61, 1021, None, None, None, False),
 ]
-CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow"}
+CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
+             "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK"}
 
 
 def log(msg):
@@ -85,17 +99,65 @@ def write_table(winners):
     log(f"wrote {TABLE}")
 
 
+def regret_mode(args, sg, sweep) -> int:
+    """Dispatch regret on random shapes: for each, every variant is timed and the dispatched one
+    compared with the fastest (time of the dispatched variant / best time)."""
+    import numpy as np
+
+    rng = np.random.default_rng(args.regret_seed)
+    records, summary = [], []
+    for c in range(args.regret):
+        M = int(np.exp(rng.uniform(np.log(256), np.log(8192))))
+        N = int(np.exp(rng.uniform(np.log(64), np.log(8192))))
+        K = int(np.exp(rng.uniform(np.log(64), np.log(8192))))
+        aligned = bool(rng.integers(0, 2))
+        if aligned:
+            N, K = max(4, N - N % 4), max(4, K - K % 4)
+        elif N % 4 == 0 and K % 4 == 0:
+            K += 1
+        beta = float(rng.choice([0.0, 0.5]))
+        A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+        C0 = rng.uniform(-1, 1, (M, N)).astype(np.float32) if beta else np.zeros((M, N), np.float32)
+        label = f"random{c}_{M}x{N}x{K}"
+        # the variant sgemm would dispatch for these arguments (pointer alignment as torch gives it)
+        disp = sg.sgemm_variant_name(sg.sgemm_select_variant(M, N, K, 256, K, 512, N, 768, N))
+        recs = sweep(label, "random", A, B, C0, 1.0, beta, aligned, 4242 + c)
+        good = [r for r in recs if r["parity"]]
+        best = min(good, key=lambda r: r["ms_median"])
+        mine = [r for r in good if r["variant"] == disp]
+        regret = mine[0]["ms_median"] / best["ms_median"] if mine else float("nan")
+        summary.append({"case": label, "dispatched": disp, "best": best["variant"], "regret": regret,
+                        "best_tflops": best["tflops"]})
+        log(f"-- {label}: dispatched {disp}, best {best['variant']} ({best['tflops']:.1f} TFLOP/s), "
+            f"regret {regret:.3f}")
+        records += recs
+    rs = sorted(x["regret"] for x in summary if x["regret"] == x["regret"])
+    if rs:
+        log(f"regret over {len(rs)} shapes: median {rs[len(rs) // 2]:.3f}, p90 {rs[int(len(rs) * 0.9)]:.3f}, "
+            f"max {rs[-1]:.3f}")
+    os.makedirs(os.path.dirname(args.out), exist_ok=True)
+    with open(args.out, "w") as f:
+        json.dump({"time": time.strftime("%Y-%m-%d %H:%M:%S"), "results": records, "regret": summary}, f, indent=1)
+    log(f"wrote {args.out}")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
     ap.add_argument("--write-table", action="store_true")
-    ap.add_argument("--classes", default="large,huge,shallow,small,skinny")
+    ap.add_argument("--classes", default="large,huge,shallow,medium,tiny_k,small,small_longk,skinny")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,
                     help="seconds of untimed launches before timing a candidate (the engine clock ramps "
                          "up under sustained load; short kernels alone would be timed at a lower clock)")
     ap.add_argument("--table-from", default=None, help="write the table from a saved results file (no GPU)")
+    ap.add_argument("--regret", type=int, default=0,
+                    help="instead of tuning: time every variant on this many random shapes and report how far "
+                         "the dispatched variant is from the fastest")
+    ap.add_argument("--regret-seed", type=int, default=2024)
     args = ap.parse_args()
     if args.table_from:
         with open(args.table_from) as f:
@@ -111,22 +173,17 @@ def main() -> int:
     import oracle
     from fp32_gemm_05_amd.workloads import WORKLOADS, make_inputs, sample_points
 
-    classes = set(args.classes.split(","))
     nvar = sg.sgemm_num_variants()
     infos = [sg.sgemm_variant_info(v) for v in range(nvar)]
-    results = []
     stream = torch.cuda.current_stream()
-    for (label, cls, wname, M, N, K, dist, alpha, beta, vec_ok) in CASES:
-        if cls not in classes:
-            continue
-        w = WORKLOADS[wname]
-        M = M or w.M
-        N = N or w.N
-        K = K or w.K
-        alpha = w.alpha if alpha is None else alpha
-        beta = w.beta if beta is None else beta
-        A, B, C0 = make_inputs(w, M=M, N=N, K=K, dist=dist, beta=beta)
-        I, J = sample_points(M, N, args.points, seed=w.seed + 17, tile=64)
+
+    def sweep(label, cls, A, B, C0, alpha, beta, vec_ok, points_seed):
+        """Time every applicable plain-operand variant on one problem; parity-gate each on sampled
+        outputs.  Returns the result records."""
+        M, K = A.shape
+        N = B.shape[1]
+        out = []
+        I, J = sample_points(M, N, args.points, seed=points_seed, tile=64)
         ref, bound = oracle.ref_points(A, B, C0, I, J, alpha, beta)
         dA = torch.from_numpy(A).cuda()
         dB = torch.from_numpy(B).cuda()
@@ -174,11 +231,29 @@ def main() -> int:
             rec = {"case": label, "class": cls, "vec_class": int(vec_ok), "M": M, "N": N, "K": K,
                    "variant": info["name"], "variant_id": v, "parity": ok, "max_err_over_bound": ratio,
                    "ms_median": med, "ms_min": ts[0], "reps": reps, "tflops": flops / (med * 1e-3) / 1e12}
-            results.append(rec)
+            out.append(rec)
             log(f"   {info['name']:36s} {'ok ' if ok else 'BAD'} err/bound={ratio:.3g} "
                 f"median {med:.4f} ms  {rec['tflops']:.2f} TFLOP/s")
         del dA, dB, dC, dC0
         torch.cuda.empty_cache()
+        return out
+
+    if args.regret:
+        return regret_mode(args, sg, sweep)
+
+    classes = set(args.classes.split(","))
+    results = []
+    for (label, cls, wname, M, N, K, dist, alpha, beta, vec_ok) in CASES:
+        if cls not in classes:
+            continue
+        w = WORKLOADS[wname]
+        M = M or w.M
+        N = N or w.N
+        K = K or w.K
+        alpha = w.alpha if alpha is None else alpha
+        beta = w.beta if beta is None else beta
+        A, B, C0 = make_inputs(w, M=M, N=N, K=K, dist=dist, beta=beta)
+        results += sweep(label, cls, A, B, C0, alpha, beta, vec_ok, w.seed + 17)
 
     # choose winners
     winners = {}
