@@ -53,6 +53,7 @@ struct GemmArgs {
     long ldb;
     float* C;
     long ldc;
+    int drain_from;  // first workgroup of the grid's last round (no workgroup starts after it)
 };
 
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
@@ -296,7 +297,50 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false>
+// Drain ordering.  A SIMD issues from its highest-priority ready wave, oldest first among equals,
+// so of the workgroups sharing a CU the oldest runs nearly alone and finishes first; in a grid's
+// last round nothing refills the freed slots, and the last workgroup ends up alone on its CU, where
+// one wave per SIMD keeps the matrix pipe about two-thirds busy.  With FAIR, every wave starts at
+// priority 3 and, in the last round only, steps down at three points of its K loop (schedule
+// FAIR picks them): a wave ahead of the others on its SIMD drops below them until they catch up,
+// so the last round's workgroups end together.
+struct DrainPhases {
+    int next, after, last;  // slabs of the remaining steps down (even; INT_MAX: none)
+    int phase;              // 0..3
+    // drain_from: first workgroup of the last round; INT_MAX turns the ordering off (a grid with no
+    // more workgroups than CUs, where no two share a SIMD and priority changes only cost).
+    __device__ inline void init(int fair, int nslab, int drain_from) {
+        next = after = last = 0x7fffffff;
+        phase = 0;
+        if (drain_from == 0x7fffffff) return;
+        const bool last_round = (int)blockIdx.x >= drain_from;
+        // schedule 2: 1/2, 3/4, 7/8 of the K loop; 3: 3/4, 7/8, 15/16; 4: 7/8, 15/16, 31/32
+        const int n1 = fair == 4 ? 28 : (fair == 3 ? 24 : 16);
+        const int n2 = fair == 4 ? 30 : (fair == 3 ? 28 : 24);
+        const int n3 = fair == 4 ? 31 : (fair == 3 ? 30 : 28);
+        next = last_round ? (int)(((long)nslab * n1 / 32) & ~1L) : 0x7fffffff;
+        after = (int)(((long)nslab * n2 / 32) & ~1L);
+        last = (int)(((long)nslab * n3 / 32) & ~1L);
+        __builtin_amdgcn_s_setprio(3);
+    }
+    __device__ inline void step(int s) {
+        if (s >= next) {
+            ++phase;
+            if (phase == 1)
+                __builtin_amdgcn_s_setprio(2);
+            else if (phase == 2)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+            next = after;
+            after = last;
+            last = 0x7fffffff;
+        }
+    }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
+          int FAIR = 0>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -409,9 +453,12 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     };
     using Full = std::integral_constant<int, 1>;
     using Dyn = std::integral_constant<int, -1>;
+    DrainPhases drain;
+    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
     int s = 0;
     // main loop, two slabs per trip so that both LDS stage offsets are constants
     for (; s + 2 < nfull; s += 2) {
+        if (FAIR > 0) drain.step(s);
         slab(s, Full{}, std::integral_constant<int, 0>{});
         slab(s + 1, Full{}, std::integral_constant<int, 1>{});
     }
@@ -439,7 +486,7 @@ struct MfmaFrag {
     float b[FN][4];
 };
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, int FAIR = 0>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -545,8 +592,11 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         }
     };
     using Dyn = std::integral_constant<int, -1>;
+    DrainPhases drain;
+    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
     int s = 0;
     for (; s + 3 < nfull; s += 2) {  // two slabs per trip: constant LDS stage offsets
+        if (FAIR > 0) drain.step(s);
         slab(s, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
         slab(s + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     }
@@ -574,7 +624,7 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 // after the barrier of slab s-1, and every wave finished its reads of that stage (slab s-1)
 // before reaching that barrier (the barrier waits for outstanding LDS accesses).
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -692,8 +742,11 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Odd = std::integral_constant<int, 1>;
     using Full = std::integral_constant<bool, true>;
     using Checked = std::integral_constant<bool, false>;
+    DrainPhases drain;
+    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
     int s = 0;
     for (; s + 3 < nfull; s += 2) {  // two slabs per trip: the buffer and stage of each are constants
+        if (FAIR > 0) drain.step(s);
         slab(s, Even{}, Full{});
         slab(s + 1, Odd{}, Full{});
     }

@@ -34,37 +34,86 @@ int group_rows(int tiles_m, int tiles_n) {
     return tiles_m < 4 ? tiles_m : 4;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false>
+// Compute units of the current device (cached per device id).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// First workgroup of the last round of an nwg-workgroup grid of `kernel`: the workgroups from
+// there on start in slots that no later workgroup refills.  resident_per_cu is the kernel's
+// occupancy (workgroups per CU); 0 when unknown, which puts the whole grid in the last round.
+// INT_MAX (ordering off) when the grid has no more workgroups than the device has CUs.
+int drain_from(int nwg, int resident_per_cu) {
+    const int cus = device_cus();
+    if (cus > 0 && nwg <= cus) return INT_MAX;
+    const long resident = (long)resident_per_cu * cus;
+    return resident <= 0 || resident >= nwg ? 0 : (int)(nwg - resident);
+}
+
+template <typename Kernel>
+int occupancy(Kernel kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) n = 0;
+    return n;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
+          int FAIR = 0>
 hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
+    auto kernel = &sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB, FAIR>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
+    if (FAIR > 0) {
+        static const int per_cu = occupancy(kernel, Cfg::NT);
+        a.drain_from = drain_from(tiles_m * tiles_n, per_cu);
+    }
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB>),
-                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0,
+                           stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0>
 hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
+    if (FAIR > 0) {
+        static const int per_cu = occupancy(kernel, Cfg::NT);
+        a.drain_from = drain_from(tiles_m * tiles_n, per_cu);
+    }
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC>),
-                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0,
+                           stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, int FAIR = 0>
 hipError_t launch_mfma_pipe(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
+    auto kernel = &sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, FAIR>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
+    if (FAIR > 0) {
+        static const int per_cu = occupancy(kernel, Cfg::NT);
+        a.drain_from = drain_from(tiles_m * tiles_n, per_cu);
+    }
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_pipe_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE>),
-                           dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0,
+                           stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool VEC>
@@ -132,9 +181,19 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
         TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
         TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
         TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
+#define FAIR_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, P, NAME)                                    \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                                              \
+     &launch_mfma<BM, BN, BK, WM, WN, VEC, OCC, false, false, false, P>, 0}
 #define DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, NAME)                                             \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0>, 0}
+#define PIPE_FAIR_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, P, NAME)                                 \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_pipe<BM, BN, BK, WM, WN, VEC, OCC, false, P>, 0}
+#define DEEP_FAIR_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                      \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0, P>, 0}
 #define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
 #define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
     DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
@@ -171,6 +230,20 @@ const Variant kVariants[] = {
     // 64-bit offsets: used whenever one workgroup's operand span does not fit 32-bit offsets
     WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, true, MFMA_NAME(128, 128, 16, 64, 64) "_wide_vec"),
     WIDE_MFMA_VARIANT(128, 128, 16, 64, 64, false, MFMA_NAME(128, 128, 16, 64, 64) "_wide_scalar"),
+    // drain ordering in the last round (schedules 3 and 4)
+    FAIR_VARIANT(128, 128, 16, 64, 64, 0, true, 3, MFMA_NAME(128, 128, 16, 64, 64) "_d3_vec"),
+    FAIR_VARIANT(128, 128, 16, 64, 64, 0, true, 4, MFMA_NAME(128, 128, 16, 64, 64) "_d4_vec"),
+    FAIR_VARIANT(128, 128, 16, 64, 64, 4, true, 3, MFMA_NAME(128, 128, 16, 64, 64) "_o4_d3_vec"),
+    FAIR_VARIANT(128, 128, 16, 64, 64, 4, false, 3, MFMA_NAME(128, 128, 16, 64, 64) "_o4_d3_scalar"),
+    FAIR_VARIANT(128, 128, 16, 64, 64, 4, false, 4, MFMA_NAME(128, 128, 16, 64, 64) "_o4_d4_scalar"),
+    FAIR_VARIANT(64, 64, 16, 32, 32, 0, true, 3, MFMA_NAME(64, 64, 16, 32, 32) "_d3_vec"),
+    FAIR_VARIANT(64, 64, 16, 32, 32, 0, false, 3, MFMA_NAME(64, 64, 16, 32, 32) "_d3_scalar"),
+    FAIR_VARIANT(64, 64, 32, 32, 32, 0, true, 3, MFMA_NAME(64, 64, 32, 32, 32) "_d3_vec"),
+    FAIR_VARIANT(64, 64, 32, 32, 32, 0, false, 3, MFMA_NAME(64, 64, 32, 32, 32) "_d3_scalar"),
+    PIPE_FAIR_VARIANT(64, 64, 16, 32, 32, 4, true, 3, PIPE_NAME(64, 64, 16, 32, 32, 4) "_d3_vec"),
+    PIPE_FAIR_VARIANT(64, 64, 16, 32, 32, 4, false, 3, PIPE_NAME(64, 64, 16, 32, 32, 4) "_d3_scalar"),
+    DEEP_FAIR_VARIANT(64, 64, 32, 32, 32, true, 3, DEEP_NAME(64, 64, 32, 32, 32) "_d3_vec"),
+    DEEP_FAIR_VARIANT(64, 64, 32, 32, 32, false, 3, DEEP_NAME(64, 64, 32, 32, 32) "_d3_scalar"),
     // deep prefetch (one wave per SIMD)
     BOTH_DEEP(64, 64, 32, 32, 32),
     BOTH_DEEP(64, 64, 64, 32, 32),
