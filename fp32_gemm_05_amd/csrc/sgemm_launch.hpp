@@ -169,18 +169,19 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define BOTH_SPLITK(BM, BN, BK, WM, WN, KS)                                                     \
     SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, true, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_vec"),   \
         SPLITK_VARIANT(BM, BN, BK, WM, WN, KS, false, SPLITK_NAME(BM, BN, BK, WM, WN, KS) "_scalar")
-#define TRANS_VARIANT(BM, BN, BK, WM, WN, VEC, WIDE, TA, TB, NAME)                              \
+#define TRANS_VARIANT(BM, BN, BK, WM, WN, VEC, WIDE, TA, TB, FAIR, NAME)                        \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT, VEC,          \
      MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::LDS_BYTES,                                         \
-     &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, WIDE, TA, TB>, WIDE, 0, TA, TB}
-// the variants of one transposition (TAG: "nt", "tn" or "tt"; first letter op(A), second op(B))
+     &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, WIDE, TA, TB, FAIR>, WIDE, 0, TA, TB}
+// the variants of one transposition (TAG: "nt", "tn" or "tt"; first letter op(A), second op(B));
+// the 128x128 ones with drain ordering (schedule 4)
 #define TRANS_SET(TA, TB, TAG)                                                                     \
-    TRANS_VARIANT(128, 128, 16, 64, 64, true, false, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_vec"),     \
-        TRANS_VARIANT(128, 128, 16, 64, 64, false, false, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_scalar"), \
-        TRANS_VARIANT(64, 64, 32, 32, 32, true, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_vec"),         \
-        TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
-        TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
-        TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
+    TRANS_VARIANT(128, 128, 16, 64, 64, true, false, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_vec"),     \
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, false, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_scalar"), \
+        TRANS_VARIANT(64, 64, 32, 32, 32, true, false, TA, TB, 0, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_vec"),         \
+        TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, 0, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
+        TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
 #define FAIR_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, P, NAME)                                    \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                                              \
