@@ -34,9 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FP32_PEAK_TFLOPS = 157.3       # MI355X dense FP32 matrix (MFMA): 256 CUs x 2.4 GHz x 256 FLOP/clk
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X FP32 vector: 256 CUs x 2.4 GHz x 256 FLOP/clk
-HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+from fp32_gemm_05_amd.roofline import (FP32_PEAK_TFLOPS, FP32_VALU_PEAK_TFLOPS, HBM_PEAK_GBS,  # noqa: E402
+                                       algorithmic_bytes, gemm_flops)
 
 
 def log(msg: str) -> None:
@@ -251,7 +250,7 @@ def main() -> int:
         torch.cuda.synchronize()
         per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
     ms_per_step = total_ms / args.steps
-    flops = 2.0 * w.M * w.N * w.K
+    flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     # cold: the mean of the individually timed launches (the fills between them are excluded);
     # warm: the timed region over K
@@ -272,7 +271,7 @@ def main() -> int:
         "frac": round(achieved / peak, 4),
         "traffic": traffic,
     }
-    alg_bytes = 4.0 * (w.M * w.K + w.K * w.N + (2 if w.beta != 0 else 1) * w.M * w.N)
+    alg_bytes = algorithmic_bytes(w.M, w.N, w.K, w.beta)
     line = {
         "metric": "SGEMM TFLOP/s and % of FP32 peak at M=N=K=4096 on 1 MI355X",
         "value": round(tflops, 3),

@@ -35,6 +35,8 @@ import os
 import sys
 from collections import defaultdict
 
+from .roofline import FP32_PEAK_TFLOPS, algorithmic_bytes, gemm_flops, panel_read_bytes
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -193,9 +195,17 @@ def _mean_counter(path, substr, name):
 def _workload_figures(workload):
     from fp32_gemm_05_amd.workloads import WORKLOADS
     w = WORKLOADS[workload]
-    flops = 2.0 * w.M * w.N * w.K
-    alg_bytes = 4.0 * (w.M * w.K + w.K * w.N + (2 if w.beta != 0 else 1) * w.M * w.N)
-    return w, flops, alg_bytes
+    return w, gemm_flops(w.M, w.N, w.K), algorithmic_bytes(w.M, w.N, w.K, w.beta)
+
+
+def _variant_tile(name):
+    """(BM, BN) of the named kernel variant in the built library, or None."""
+    from . import _binding as sg
+    for i in range(sg.sgemm_num_variants()):
+        if sg.sgemm_variant_name(i) == name:
+            info = sg.sgemm_variant_info(i)
+            return info["BM"], info["BN"]
+    return None
 
 
 def cmd_report(args) -> None:
@@ -240,6 +250,8 @@ def cmd_report(args) -> None:
     expect_mfma = w.M * w.N * w.K / 2048.0  # 32x32x2 MFMAs of the exact problem (no tile padding)
     tflops = flops / (avg_ns * 1e-9) / 1e12
     tflops_timed = flops / (timed_ns * 1e-9) / 1e12
+    tile = _variant_tile(variant)
+    panel = panel_read_bytes(w.M, w.N, w.K, *tile) if tile else float("nan")
     bench = "python -u bench.py --workload %s" % W
     trace_opt = f"--trace-args='{args.trace_args}' " if args.trace_args else ""
     sq_warm = args.sq_warmup
@@ -259,11 +271,11 @@ def cmd_report(args) -> None:
         f"Workload: {w.describe()}; {flops / 1e9:.2f} GFLOP and {alg_bytes / 1e6:.1f} MB of algorithmic traffic per call.",
         f"Kernel: `{name}`", "",
         "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
-        "| Dispatches | Mean duration | TFLOP/s | % of 157.3 |", "|---|---|---|---|",
+        f"| Dispatches | Mean duration | TFLOP/s | % of {FP32_PEAK_TFLOPS} |", "|---|---|---|---|",
         f"| all {k['Calls']} (first call + warmup + timed; the --stats average) | {avg_ns / 1e3:.1f} us | "
-        f"{tflops:.1f} | {100 * tflops / 157.3:.1f} % |",
+        f"{tflops:.1f} | {100 * tflops / FP32_PEAK_TFLOPS:.1f} % |",
         f"| the last {len(timed)} (the bench's timed region) | {timed_ns / 1e3:.1f} us | {tflops_timed:.1f} | "
-        f"{100 * tflops_timed / 157.3:.1f} % |", "",
+        f"{100 * tflops_timed / FP32_PEAK_TFLOPS:.1f} % |", "",
         f"Min {float(k['MinNs']) / 1e3:.1f} us, max {float(k['MaxNs']) / 1e3:.1f} us over all dispatches.", "",
         "## Counters (means per dispatch)", "",
         "| Counter | Value |", "|---|---|",
@@ -292,6 +304,9 @@ def cmd_report(args) -> None:
         f"* HBM-side traffic per launch (copy-calibrated FETCH_SIZE + WRITE_SIZE): {hbm / 1e6:.1f} MB "
         f"= {hbm / alg_bytes:.2f} x the algorithmic {alg_bytes / 1e6:.1f} MB",
         f"* L2 read requests by size: {rd_bytes / 1e6:.1f} MB read (32/64/128 B requests counted at their size)",
+        (f"* Panel reads of the {tile[0]}x{tile[1]} tiling, K*(1/BM + 1/BN) values per output: {panel / 1e6:.1f} MB "
+         f"per launch; the L2 serves all but the L2->fabric traffic above" if tile else
+         "* Panel reads: variant not found in this build"),
         "", "## Commands", "", "```", *cmds, "```", "",
     ]
     if args.note:
