@@ -7,7 +7,7 @@ A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
                     [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline] [--cpu-full]
-                    [--cpu-threads N] [--cold]
+                    [--cpu-threads N] [--cold | --cold-dirty]
 
 ``--op`` other than NN stores A as K x M and/or B as N x K and times
 ``sgemm_op`` (op(A) * op(B)) on the same logical product.
@@ -148,8 +148,12 @@ def main() -> int:
                     help="time the oracle on the whole workload instead of a bounded sample of rows")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: all host threads)")
     ap.add_argument("--cold", action="store_true",
-                    help="overwrite a 512 MiB buffer before every timed launch (evicts the caches, so the "
-                         "operands come from HBM); each launch is then timed between its own two events")
+                    help="read a 512 MiB buffer before every timed launch (evicts the operands from the L2s "
+                         "and the Infinity Cache, leaving clean lines, so the operands come from HBM); each "
+                         "launch is then timed between its own two events")
+    ap.add_argument("--cold-dirty", action="store_true",
+                    help="as --cold, but overwrite the 512 MiB buffer instead: the caches then hold dirty lines "
+                         "whose write-back competes with the timed launch")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -207,16 +211,21 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    if args.cold:
-        # 512 MiB > the 256 MB Infinity Cache and every L2: the fill before each launch evicts the
-        # operands.  Launch i is timed between its own events (the fill is outside them).
-        flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+    cold = args.cold or args.cold_dirty
+    if cold:
+        # 512 MiB > the 256 MB Infinity Cache and every L2: the flush before each launch evicts the
+        # operands.  Launch i is timed between its own events (the flush is outside them).
+        flush = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+        flush_out = torch.empty((), dtype=torch.float32, device=dev)
         ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         for i in range(args.steps):
-            flush.fill_(float(i))
+            if args.cold_dirty:
+                flush.fill_(float(i))
+            else:
+                torch.sum(flush, dim=0, out=flush_out)
             ev_s[i].record(stream)
             step()
             ev_e[i].record(stream)
@@ -224,7 +233,7 @@ def main() -> int:
         wall = time.perf_counter() - wall0
         per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
         total_ms = float(per_launch.sum())
-        del flush
+        del flush, flush_out
     else:
         # Two events on the kernels' stream bracket the K back-to-back launches; the mean launch
         # duration is the timed region over K (events between launches would add their own gaps).
@@ -252,11 +261,11 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
     flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    # cold: the mean of the individually timed launches (the fills between them are excluded);
+    # cold: the mean of the individually timed launches (the flushes between them are excluded);
     # warm: the timed region over K
-    avg_launch_ms = float(per_launch.mean()) if args.cold else ms_per_step
+    avg_launch_ms = float(per_launch.mean()) if cold else ms_per_step
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    log(f"timed {args.steps} steps{' (cold)' if args.cold else ''}: {total_ms:.3f} ms events, "
+    log(f"timed {args.steps} steps{' (cold)' if cold else ''}: {total_ms:.3f} ms events, "
         f"{wall * 1e3:.3f} ms wall; mean launch {avg_launch_ms:.4f} ms; {len(per_launch)} single launches: "
         f"median {float(np.median(per_launch)):.4f}, min {per_launch.min():.4f}, max {per_launch.max():.4f}")
 
@@ -294,7 +303,7 @@ def main() -> int:
         "pct_fp32_peak": round(100.0 * tflops / FP32_PEAK_TFLOPS, 2),
         "launch_median_ms": round(float(np.median(per_launch)), 5),
         "launch_min_ms": round(float(per_launch.min()), 5),
-        "cold": bool(args.cold),
+        "cold": "dirty" if args.cold_dirty else bool(args.cold),
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pct_hbm_peak_alg": round(100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,

@@ -23,10 +23,23 @@ FLAGS = [
 ]
 
 
+# The read-bandwidth reference of the profiling summaries (not part of libsgemm).
+HBM_READ_LIB = os.path.join(HERE, "libhbm_read.so")
+HBM_READ_SOURCES = [os.path.join(CSRC, "hbm_read.hip")]
+
+
 def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
-    out = out or LIB
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *SOURCES, "-o", out + ".tmp"]
+    """Compile libsgemm's HIP sources into one shared library; returns its path."""
+    return _compile(SOURCES, out or LIB, verbose, extra_flags)
+
+
+def build_hbm_read(verbose: bool = False) -> str:
+    """Compile the streaming-read reference kernel (libhbm_read.so); returns its path."""
+    return _compile(HBM_READ_SOURCES, HBM_READ_LIB, verbose, None)
+
+
+def _compile(sources, out: str, verbose: bool, extra_flags) -> str:
+    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *sources, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

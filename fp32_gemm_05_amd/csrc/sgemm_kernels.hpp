@@ -94,8 +94,9 @@ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
 // covers 4 consecutive columns (needs ld % 4 == 0, ncols % 4 == 0 and a
 // 16-byte aligned base, which also make every 4-column group wholly inside or
 // outside K).  Per-lane offsets are 32-bit unless WIDE (64-bit, for leading
-// dimensions so large that one workgroup's panel spans 4 GiB or more).
-template <int ROWS, int COLS, int NT, bool VEC, bool KROWS, bool WIDE, int NBUF = 1>
+// dimensions so large that one workgroup's panel spans 4 GiB or more).  NTL marks
+// the loads nontemporal (streamed: no other workgroup reads this operand's panel).
+template <int ROWS, int COLS, int NT, bool VEC, bool KROWS, bool WIDE, int NBUF = 1, bool NTL = false>
 struct PanelLoader {
     using OffT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
     static constexpr int W = VEC ? 4 : 1;             // floats per load
@@ -150,9 +151,10 @@ struct PanelLoader {
             const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + off[l]);
             if (VEC) {
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                v[BUF][l] = ok ? *reinterpret_cast<const f32x4*>(p) : z;
+                const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
+                v[BUF][l] = ok ? (NTL ? __builtin_nontemporal_load(p4) : *p4) : z;
             } else {
-                v[BUF][l].x = ok ? *p : 0.f;
+                v[BUF][l].x = ok ? (NTL ? __builtin_nontemporal_load(p) : *p) : 0.f;
             }
         }
     }
@@ -340,7 +342,7 @@ struct DrainPhases {
 };
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
-          int FAIR = 0>
+          int FAIR = 0, bool NTA = false>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -362,8 +364,8 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int K = g.K;
     // A slab: BM rows x BK columns of A, or (TA) BK rows x BM columns of the stored A^T.
     // B slab: BK rows x BN columns of B, or (TB) BN rows x BK columns of the stored B^T.
-    using LoaderA = typename std::conditional<TA, PanelLoader<BK, BM, NT, VEC, true, WIDE>,
-                                              PanelLoader<BM, BK, NT, VEC, false, WIDE>>::type;
+    using LoaderA = typename std::conditional<TA, PanelLoader<BK, BM, NT, VEC, true, WIDE, 1, NTA>,
+                                              PanelLoader<BM, BK, NT, VEC, false, WIDE, 1, NTA>>::type;
     using LoaderB = typename std::conditional<TB, PanelLoader<BN, BK, NT, VEC, false, WIDE>,
                                               PanelLoader<BK, BN, NT, VEC, true, WIDE>>::type;
     LoaderA la;
@@ -624,7 +626,7 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 // after the barrier of slab s-1, and every wave finished its reads of that stage (slab s-1)
 // before reaching that barrier (the barrier waits for outstanding LDS accesses).
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -646,7 +648,7 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int li = lane & 31, lh = lane >> 5;
 
     const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false, false, 2> la;
+    PanelLoader<BM, BK, NT, VEC, false, false, 2, NTA> la;
     PanelLoader<BK, BN, NT, VEC, true, false, 2> lb;
     la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
     lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);

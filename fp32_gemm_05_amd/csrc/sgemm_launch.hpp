@@ -68,10 +68,10 @@ int occupancy(Kernel kernel, int threads) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
-          int FAIR = 0>
+          int FAIR = 0, bool NTA = false>
 hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
-    auto kernel = &sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB, FAIR>;
+    auto kernel = &sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB, FAIR, NTA>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -84,10 +84,10 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
                            stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false>
 hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR>;
+    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR, NTA>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -195,6 +195,15 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define DEEP_FAIR_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                      \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0, P>, 0}
+// nontemporal loads of A (the skinny class: with one tile column, no two workgroups read the
+// same rows of A)
+#define NTA_FAIR_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                      \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                                              \
+     &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, false, false, false, P, true>, 0}
+#define NTA_DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                      \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0, P, true>, 0}
 #define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
 #define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
     DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
@@ -248,6 +257,14 @@ const Variant kVariants[] = {
     // deep prefetch (one wave per SIMD)
     BOTH_DEEP(64, 64, 32, 32, 32),
     BOTH_DEEP(64, 64, 64, 32, 32),
+    // nontemporal A (skinny class)
+    NTA_FAIR_VARIANT(64, 64, 32, 32, 32, true, 3, MFMA_NAME(64, 64, 32, 32, 32) "_d3_nta_vec"),
+    NTA_FAIR_VARIANT(64, 64, 32, 32, 32, false, 3, MFMA_NAME(64, 64, 32, 32, 32) "_d3_nta_scalar"),
+    NTA_DEEP_VARIANT(64, 64, 32, 32, 32, true, 0, DEEP_NAME(64, 64, 32, 32, 32) "_nta_vec"),
+    NTA_DEEP_VARIANT(64, 64, 32, 32, 32, false, 0, DEEP_NAME(64, 64, 32, 32, 32) "_nta_scalar"),
+    NTA_DEEP_VARIANT(64, 64, 32, 32, 32, true, 3, DEEP_NAME(64, 64, 32, 32, 32) "_d3_nta_vec"),
+    NTA_DEEP_VARIANT(64, 64, 32, 32, 32, false, 3, DEEP_NAME(64, 64, 32, 32, 32) "_d3_nta_scalar"),
+    NTA_FAIR_VARIANT(128, 64, 32, 64, 64, true, 0, MFMA_NAME(128, 64, 32, 64, 64) "_nta_vec"),
     // transposed operands (sgemm_op): op(A) x op(B) = N x T, T x N, T x T
     TRANS_SET(false, true, "nt"),
     TRANS_SET(true, false, "tn"),

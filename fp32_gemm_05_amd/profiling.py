@@ -3,9 +3,9 @@
     python -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3
         a plain device-to-device copy of known size; run under `rocprofv3 --pmc FETCH_SIZE`
         (then WRITE_SIZE) it calibrates how many bytes one KiB of each counter stands for.
-    python -m fp32_gemm_05_amd.profiling read --mib 256 [--cold]
-        a streaming read of known size (torch's sum), warm or after evicting the caches: the
-        read bandwidth an HBM-bound kernel can expect under the same protocol.
+    python -m fp32_gemm_05_amd.profiling read --mib 256 [--mode warm|cold|cold-dirty]
+        a streaming read of known size (a hand-written read kernel, libhbm_read.so), warm or after
+        evicting the caches: the read bandwidth an HBM-bound kernel can expect under the same protocol.
     python -m fp32_gemm_05_amd.profiling stats <kernel_stats.csv> --command "..." --out X.md
         short text summary of a `rocprofv3 --kernel-trace --stats` run.
     python -m fp32_gemm_05_amd.profiling traffic --kernel SUBSTR --fetch F.csv --write W.csv
@@ -67,32 +67,58 @@ def run_copy(mib: int, reps: int) -> None:
     print(f"copy: {reps} x {mib} MiB device-to-device ({2 * mib} MiB of traffic each)", flush=True)
 
 
-def run_read(mib: int, reps: int, cold: bool) -> None:
-    """Read-bandwidth reference: torch's sum over `mib` MiB (a streaming read), timed between
-    events; with cold, a 512 MiB buffer is overwritten before every timed read (the protocol of
-    bench.py --cold), so the data comes from HBM."""
+def _hbm_read_lib():
+    import ctypes
+    from .build import HBM_READ_LIB, build_hbm_read
+    if not os.path.exists(HBM_READ_LIB):
+        build_hbm_read()
+    lib = ctypes.CDLL(HBM_READ_LIB)
+    lib.hbm_read_workgroups.restype = ctypes.c_long
+    lib.hbm_read_workgroups.argtypes = [ctypes.c_long, ctypes.c_int]
+    lib.hbm_read.restype = ctypes.c_int
+    lib.hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def run_read(mib: int, reps: int, mode: str, chunk_kib: int = 1024) -> None:
+    """Read-bandwidth reference: a hand-written streaming read (csrc/hbm_read.hip: each workgroup
+    reads one contiguous chunk with eight 128-bit loads in flight per thread) over `mib` MiB, each
+    read timed between its own events.  mode: "warm" (back-to-back), "cold" (a 512 MiB buffer is
+    read before every timed read: the operands leave the L2s and the Infinity Cache, which then
+    hold clean lines) or "cold-dirty" (the 512 MiB buffer is overwritten instead: dirty lines are
+    written back while the timed read runs) -- the protocols of bench.py, --cold and --cold-dirty."""
     import torch
-    n = mib * 1024 * 1024 // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda")
-    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if cold else None
-    out = torch.empty((), dtype=torch.float32, device="cuda")
-    for _ in range(5):
-        torch.sum(x, dim=0, out=out)
-    times = []
-    for i in range(reps):
-        if cold:
+    lib = _hbm_read_lib()
+    nbytes = mib * 1024 * 1024
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    nwg = lib.hbm_read_workgroups(nbytes, chunk_kib)
+    out = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+    flush = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if mode != "warm" else None
+    fout = torch.empty(lib.hbm_read_workgroups(flush.numel() * 4, chunk_kib) * 256, dtype=torch.float32,
+                       device="cuda") if flush is not None else None
+    stream = torch.cuda.current_stream()
+
+    def read(buf, o):
+        rc = lib.hbm_read(buf.data_ptr(), buf.numel() * 4, chunk_kib, o.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hbm_read returned {rc}")
+
+    for _ in range(200):  # the engine clock ramps up under sustained load
+        read(x, out)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
+        if mode == "cold":
+            read(flush, fout)
+        elif mode == "cold-dirty":
             flush.fill_(float(i))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        torch.sum(x, dim=0, out=out)
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    times.sort()
+        e0.record(stream)
+        read(x, out)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     med = times[len(times) // 2]
-    print(f"read: {mib} MiB {'cold' if cold else 'warm'}, median {med * 1e3:.1f} us over {reps} -> "
-          f"{mib * 1024 * 1024 / (med * 1e-3) / 1e12:.2f} TB/s", flush=True)
+    print(f"read: {mib} MiB {mode}, median {med * 1e3:.1f} us (min {times[0] * 1e3:.1f}) over {reps} -> "
+          f"{nbytes / (med * 1e-3) / 1e12:.2f} TB/s", flush=True)
 
 
 def _read_counters(path: str, kernel_substr: str):
@@ -337,7 +363,8 @@ def main(argv=None) -> int:
     p = sub.add_parser("read")
     p.add_argument("--mib", type=int, default=256)
     p.add_argument("--reps", type=int, default=50)
-    p.add_argument("--cold", action="store_true")
+    p.add_argument("--mode", default="warm", choices=["warm", "cold", "cold-dirty"])
+    p.add_argument("--chunk-kib", type=int, default=1024)
     p = sub.add_parser("stats")
     p.add_argument("csv")
     p.add_argument("--title", default="")
@@ -380,7 +407,7 @@ def main(argv=None) -> int:
     elif args.cmd == "copy":
         run_copy(args.mib, args.reps)
     elif args.cmd == "read":
-        run_read(args.mib, args.reps, args.cold)
+        run_read(args.mib, args.reps, args.mode, args.chunk_kib)
     elif args.cmd == "stats":
         cmd_stats(args)
     elif args.cmd == "traffic":

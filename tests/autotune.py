@@ -61,7 +61,17 @@ CASES = [
     ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
     ("skinny65536x64x1024", "skinny", "skinny65536x64x1024", None, None, None, None, None, None, True),
     ("skinny65536x61x1021", "skinny", "skinny65536x64x1024", 65536, 61, 1021, None, None, None, False),
+    ("skinny262144x32x512", "skinny", "skinny65536x64x1024", 262144, 32, 512, None, None, None, True),
+    ("skinny100003x47x777", "skinny", "ragged3001x5003x777", 100003, 47, 777, None, None, None, False),
 ]
+# Classes timed in three cache states, each state scored as a case of its own: "warm"
+# (back-to-back launches), "cold" (each timed launch follows a read of a 512 MiB buffer, which
+# evicts the operands from the L2s and the 256 MB Infinity Cache and leaves clean lines) and
+# "dirty" (the 512 MiB buffer is overwritten instead, so dirty lines are written back while the
+# launch runs).  The skinny class streams A from HBM: warm launches alone would time it partly
+# out of the Infinity Cache, and cold ones alone would miss what evicting dirty lines costs.
+COLD_CLASSES = {"skinny"}
+STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK"}
 
@@ -76,7 +86,7 @@ def read_table():
     out = {}
     if os.path.exists(TABLE):
         ids = {v: k for k, v in CLASS_IDS.items()}
-        for m in re.finditer(r'\{(k\w+), (\d), "([\w]+)"\},\s*//[^\n]*?([\d.]+)\s*$', open(TABLE).read(), re.M):
+        for m in re.finditer(r'\{(k\w+), (\d), "([\w]+)"\},\s*//[^\n]*?best ([\d.]+)[^\n]*$', open(TABLE).read(), re.M):
             out[(ids[m.group(1)], int(m.group(2)))] = (m.group(3), float(m.group(4)))
     return out
 
@@ -92,7 +102,8 @@ def write_table(winners):
              "// over that class's representative workloads.",
              "const TableEntry kTunedTable[] = {"]
     for (cls, vclass), (win, sc) in sorted(winners.items()):
-        lines.append(f'    {{{CLASS_IDS[cls]}, {vclass}, "{win}"}},  // slowdown vs per-case best {sc:.3f}')
+        states = " (warm, cold, dirty)" if cls in COLD_CLASSES else ""
+        lines.append(f'    {{{CLASS_IDS[cls]}, {vclass}, "{win}"}},  // slowdown vs per-case best {sc:.3f}{states}')
     lines.append("};")
     with open(TABLE, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -177,9 +188,15 @@ def main() -> int:
     infos = [sg.sgemm_variant_info(v) for v in range(nvar)]
     stream = torch.cuda.current_stream()
 
+    flush = {}
+
     def sweep(label, cls, A, B, C0, alpha, beta, vec_ok, points_seed):
         """Time every applicable plain-operand variant on one problem; parity-gate each on sampled
         outputs.  Returns the result records."""
+        states = STATES if cls in COLD_CLASSES else ("warm",)
+        if len(states) > 1 and not flush:
+            flush["buf"] = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+            flush["out"] = torch.empty((), dtype=torch.float32, device="cuda")
         M, K = A.shape
         N = B.shape[1]
         out = []
@@ -217,23 +234,30 @@ def main() -> int:
             e1.record(stream)
             torch.cuda.synchronize()
             est = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
-            for _ in range(int(min(20000, args.warm_time / est))):
-                call()
-            reps = int(max(5, min(500, args.min_time / est)))
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for s, e in evs:
-                s.record(stream)
-                call()
-                e.record(stream)
-            torch.cuda.synchronize()
-            ts = sorted(s.elapsed_time(e) for s, e in evs)
-            med = ts[len(ts) // 2]
-            rec = {"case": label, "class": cls, "vec_class": int(vec_ok), "M": M, "N": N, "K": K,
-                   "variant": info["name"], "variant_id": v, "parity": ok, "max_err_over_bound": ratio,
-                   "ms_median": med, "ms_min": ts[0], "reps": reps, "tflops": flops / (med * 1e-3) / 1e12}
-            out.append(rec)
-            log(f"   {info['name']:36s} {'ok ' if ok else 'BAD'} err/bound={ratio:.3g} "
-                f"median {med:.4f} ms  {rec['tflops']:.2f} TFLOP/s")
+            for state in states:
+                for _ in range(int(min(20000, args.warm_time / est))):
+                    call()
+                reps = int(max(5, min(500 if state == "warm" else 60, args.min_time / est)))
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for i, (s, e) in enumerate(evs):
+                    if state == "cold":
+                        torch.sum(flush["buf"], dim=0, out=flush["out"])
+                    elif state == "dirty":
+                        flush["buf"].fill_(float(i))
+                    s.record(stream)
+                    call()
+                    e.record(stream)
+                torch.cuda.synchronize()
+                ts = sorted(s.elapsed_time(e) for s, e in evs)
+                med = ts[len(ts) // 2]
+                case = label if len(states) == 1 else f"{label}@{state}"
+                rec = {"case": case, "class": cls, "vec_class": int(vec_ok), "state": state, "M": M, "N": N,
+                       "K": K, "variant": info["name"], "variant_id": v, "parity": ok, "max_err_over_bound": ratio,
+                       "ms_median": med, "ms_min": ts[0], "reps": reps, "tflops": flops / (med * 1e-3) / 1e12}
+                out.append(rec)
+                log(f"   {info['name']:36s} {'ok ' if ok else 'BAD'} err/bound={ratio:.3g} "
+                    f"median {med:.4f} ms {state:5s}  {rec['tflops']:.2f} TFLOP/s")
         del dA, dB, dC, dC0
         torch.cuda.empty_cache()
         return out
