@@ -127,6 +127,16 @@ hipError_t launch_mfma_splitk(const GemmArgs& g, hipStream_t stream) {
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
+template <bool VEC, int D>
+hipError_t launch_mfma_direct(const GemmArgs& g, hipStream_t stream) {
+    int tiles_m = ceil_div(g.M, 32), tiles_n = ceil_div(g.N, 32);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_direct_kernel<VEC, D>),
+                           dim3(tiles_m * tiles_n), dim3(64), args, 0, stream);
+}
+
 template <int BM, int BN, int BK, int TM, int TN, bool VEC, bool WIDE>
 hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
@@ -269,5 +279,11 @@ const Variant kVariants[] = {
     TRANS_SET(false, true, "nt"),
     TRANS_SET(true, false, "tn"),
     TRANS_SET(true, true, "tt"),
+    // LDS-free: one wave per 32x32 tile, operands loaded straight into registers D groups ahead
+    // (BK = 16 D: the K span of the loads in flight, which bounds the 32-bit per-lane offsets)
+    {"mfma32r_32x32x128_w32x32_g8_vec", kMfma, 32, 32, 128, 32, 32, 64, 1, 0, &launch_mfma_direct<true, 8>, 0},
+    {"mfma32r_32x32x128_w32x32_g8_scalar", kMfma, 32, 32, 128, 32, 32, 64, 0, 0, &launch_mfma_direct<false, 8>, 0},
+    {"mfma32r_32x32x96_w32x32_g6_vec", kMfma, 32, 32, 96, 32, 32, 64, 1, 0, &launch_mfma_direct<true, 6>, 0},
+    {"mfma32r_32x32x96_w32x32_g6_scalar", kMfma, 32, 32, 96, 32, 32, 64, 0, 0, &launch_mfma_direct<false, 6>, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

@@ -56,9 +56,16 @@ CASES = [
     ("longk1089x728x5752", "small_longk", "square4096", 1089, 728, 5752, None, None, None, True),
     ("longk1751x907x5323", "small_longk", "ragged3001x5003x777", 1751, 907, 5323, None, None, None, False),
     ("longk777x1501x3001", "small_longk", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
-    ("square256", "small", "square256", None, None, None, None, None, None, True),
+    ("square256", "tiny", "square256", None, None, None, None, None, None, True),
     ("square1024_beta", "small", "square1024_beta", None, None, None, None, None, None, True),
     ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
+    ("small512x512x512", "tiny", "square256", 512, 512, 512, None, None, None, True),
+    ("tiny333x555x777", "tiny", "ragged3001x5003x777", 333, 555, 777, None, None, None, False),
+    ("tiny600x200x1000", "tiny", "ragged3001x5003x777", 600, 200, 1000, None, None, None, False),
+    ("tiny640x384x1536", "tiny", "square1024_beta", 640, 384, 1536, None, None, None, True),
+    ("small768x1280x1024", "small", "square1024_beta", 768, 1280, 1024, None, None, None, True),
+    ("small2048x512x1536", "small", "square256", 2048, 512, 1536, None, None, None, True),
+    ("ragged700x900x1301", "small", "ragged3001x5003x777", 700, 900, 1301, None, None, None, False),
     ("skinny65536x64x1024", "skinny", "skinny65536x64x1024", None, None, None, None, None, None, True),
     ("skinny65536x61x1021", "skinny", "skinny65536x64x1024", 65536, 61, 1021, None, None, None, False),
     ("skinny262144x32x512", "skinny", "skinny65536x64x1024", 262144, 32, 512, None, None, None, True),
@@ -73,7 +80,7 @@ CASES = [
 COLD_CLASSES = {"skinny"}
 STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
-             "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK"}
+             "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny"}
 
 
 def log(msg):
@@ -158,7 +165,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
     ap.add_argument("--write-table", action="store_true")
-    ap.add_argument("--classes", default="large,huge,shallow,medium,tiny_k,small,small_longk,skinny")
+    ap.add_argument("--classes", default="large,huge,shallow,medium,tiny_k,small,tiny,small_longk,skinny")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,

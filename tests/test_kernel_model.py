@@ -134,8 +134,16 @@ SHAPES = [(1, 1, 1), (1, 4, 4), (4, 1, 4), (33, 65, 9), (128, 128, 16), (129, 13
           (132, 132, 20), (68, 260, 36)]
 
 
+def is_direct(v):
+    """The LDS-free kernel (one wave per 32x32 tile, operands loaded straight into registers):
+    its loads follow the MFMA operand layout, not the panel loader's, and have their own model."""
+    return v["name"].startswith("mfma32r_")
+
+
 @pytest.mark.parametrize("v", VARIANTS, ids=[v["name"] for v in VARIANTS])
 def test_loads_in_bounds(v):
+    if is_direct(v):
+        pytest.skip("covered by test_direct_kernel_loads_in_bounds")
     for (M, N, K) in SHAPES:
         a_len = M if v["trans_a"] else K   # stored row lengths
         b_len = K if v["trans_b"] else N
@@ -172,3 +180,50 @@ def test_mfma_k_mapping_covers_slab_once(BK):
     """Group kk, step t, half h uses k = 8*kk + 4*h + t for both operands: each k in the slab once."""
     ks = [8 * kk + 4 * h + t for kk in range(BK // 8) for t in range(4) for h in range(2)]
     assert sorted(ks) == list(range(BK))
+
+
+DIRECT = [v for v in VARIANTS if is_direct(v)]
+
+
+@pytest.mark.parametrize("v", DIRECT, ids=[v["name"] for v in DIRECT])
+def test_direct_kernel_loads_in_bounds(v):
+    """sgemm_mfma_direct_kernel's addressing, restated: lane (i, h) of the wave owning tile
+    (m0, n0) reads A(min(m0+i, M-1), k) and B(k, min(n0+i, N-1)) for k = 8q + 4h + t of every
+    group q < ceil(K/8) (in the ring's last trips, groups past the end too); in the tail, k past
+    K is read at k = K-1 (K-4 for the 128-bit A load) and the value replaced by zero.  Every
+    element read must lie inside the operand; every k < K must be read for every row/column."""
+    D = v["BK"] // 16
+    vec = bool(v["vec"])
+    for (M, N, K) in SHAPES + [(64, 64, 8 * D), (33, 35, 16 * D + 5), (40, 64, 24 * D + 4)]:
+        if vec and (N % 4 or K % 4):
+            continue
+        ngroups, nfull = -(-K // 8), K // 8
+        # groups loaded: the prologue's D, then D per trip while q + D < ngroups
+        loaded = set(range(D))
+        q = 0
+        while q + 2 * D <= nfull:
+            loaded |= set(range(q + D, q + 2 * D))
+            q += D
+        while q + D < ngroups:
+            loaded |= set(range(q + D, q + 2 * D))
+            q += D
+        consumed = set(range(q + D))  # every trip's slots, and the final D
+        assert set(range(ngroups)) <= consumed <= loaded
+        ks_a, ks_b = [], []
+        for g in sorted(loaded):
+            for h in range(2):
+                kb = 8 * g + 4 * h
+                if vec:
+                    ka = min(kb, K - 4) if kb >= K or g >= nfull else kb
+                    ks_a += [ka + t for t in range(4)]
+                    ok = kb < K
+                    assert ok or all(kb + t >= K for t in range(4))
+                else:
+                    ks_a += [min(kb + t, K - 1) if g >= nfull else kb + t for t in range(4)]
+                ks_b += [min(kb + t, K - 1) if g >= nfull else kb + t for t in range(4)]
+        ks_a, ks_b = np.array(ks_a), np.array(ks_b)
+        assert ks_a.min() >= 0 and ks_a.max() < K and ks_b.min() >= 0 and ks_b.max() < K
+        assert set(range(K)) <= set(ks_a.tolist()) and set(range(K)) <= set(ks_b.tolist())
+        rows = np.minimum(np.arange(-(-M // 32) * 32), M - 1)
+        cols = np.minimum(np.arange(-(-N // 32) * 32), N - 1)
+        assert rows.max() < M and cols.max() < N
