@@ -56,7 +56,12 @@ CASES = [
     ("longk1089x728x5752", "small_longk", "square4096", 1089, 728, 5752, None, None, None, True),
     ("longk1751x907x5323", "small_longk", "ragged3001x5003x777", 1751, 907, 5323, None, None, None, False),
     ("longk777x1501x3001", "small_longk", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
-    ("square256", "tiny", "square256", None, None, None, None, None, None, True),
+    ("square256", "small_shortk", "square256", None, None, None, None, None, None, True),
+    ("shortk822x124x88", "small_shortk", "square256", 822, 124, 88, None, None, None, True),
+    ("shortk2664x180x284", "small_shortk", "square256", 2664, 180, 284, None, None, None, True),
+    ("shortk7195x426x167", "small_shortk", "ragged3001x5003x777", 7195, 426, 167, None, None, None, False),
+    ("shortk516x1306x236", "small_shortk", "ragged3001x5003x777", 516, 1306, 236, None, None, None, False),
+    ("tiny1554x64x5093", "tiny", "ragged3001x5003x777", 1554, 64, 5093, None, None, None, False),
     ("square1024_beta", "small", "square1024_beta", None, None, None, None, None, None, True),
     ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
     ("small512x512x512", "tiny", "square256", 512, 512, 512, None, None, None, True),
@@ -80,7 +85,8 @@ CASES = [
 COLD_CLASSES = {"skinny"}
 STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
-             "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny"}
+             "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
+             "small_shortk": "kSmallShortK"}
 
 
 def log(msg):
@@ -165,7 +171,8 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
     ap.add_argument("--write-table", action="store_true")
-    ap.add_argument("--classes", default="large,huge,shallow,medium,tiny_k,small,tiny,small_longk,skinny")
+    ap.add_argument("--classes",
+                    default="large,huge,shallow,medium,tiny_k,small,tiny,small_shortk,small_longk,skinny")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,
