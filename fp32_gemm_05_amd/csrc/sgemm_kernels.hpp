@@ -912,66 +912,100 @@ sgemm_mfma_splitk_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 // LDS-free MFMA kernel for small grids.  One wave per workgroup owns a 32x32 tile of C and loads
 // its MFMA operands from global memory straight into registers, in the layout the 32x32x2
 // instruction takes: for each 8-deep group of K, lane (i, h) needs A(m0+i, k) and B(k, n0+i) for
-// k = 4h + t, t = 0..3.  A's four values are one 128-bit load (VEC) or four 32-bit loads; each of
-// B's four is a 32-bit load whose 32 lanes read 128 contiguous bytes of one row.  There is no LDS
-// and no barrier; the loads run D groups ahead of the MFMAs in a ring of registers.  Rows past M
-// and columns past N are clamped (they feed outputs that are never stored); k past K is zero.
-// Byte offsets per lane are 32-bit from a per-tile base: the caller guarantees
-// (31 * lda + 16 D) * 4 < 2^32 and (16 D * ldb + 32) * 4 < 2^32 (the variant's BK is 16 D).
+// k = 4h + t, t = 0..3.  There is no LDS and no barrier; the loads run D groups ahead of the
+// MFMAs in a ring of registers.  Rows past M and columns past N are clamped (they feed outputs
+// that are never stored); k past K is zero.
 // ---------------------------------------------------------------------------------
-template <bool VEC, int D>
+
+// One operand of the LDS-free kernel, X(r, k) with r = r0 + i along the tile (m for A, n for B).
+// KC: k runs along the stored rows (A, or B^T): a lane's four k values are contiguous, one
+// 128-bit load (VEC) or four 32-bit loads from row min(r0+i, R-1).  Otherwise (B, or A^T) each k
+// is a stored row and the lane reads column min(r0+i, R-1) of it: four 32-bit loads whose 32
+// lanes read 128 contiguous bytes.  Addressing: a workgroup-uniform base moved D groups per
+// trip, plus loop-invariant 32-bit per-lane byte offsets (KC: one, the group's step being an
+// immediate; otherwise one per (slot, t)).  The base starts D groups before the matrix, so the
+// prologue is a trip of loads without MFMAs.  The caller guarantees the offsets fit 32 bits:
+// KC: (31 * ld + 16 D) * 4 < 2^32, otherwise ((16 D - 1) * ld + 32) * 4 < 2^32.
+template <bool KC, bool VEC, int D>
+struct DirectOperand {
+    static constexpr int NO = KC ? 1 : 4 * D;
+    const char* base;
+    long step;
+    long ld4;
+    uint32_t off[NO];
+
+    __device__ inline void init(const float* X, long ld, int r0, int R, int li, int lh) {
+        ld4 = ld * 4;
+        const long r = imin(r0 + li, R - 1) - r0;
+        if (KC) {
+            base = reinterpret_cast<const char*>(X + (long)r0 * ld) - (long)D * 32;
+            step = (long)D * 32;
+            off[0] = (uint32_t)((r * ld + lh * 4) * 4);
+        } else {
+            base = reinterpret_cast<const char*>(X + r0) - (long)D * 8 * ld4;
+            step = (long)D * 8 * ld4;
+            const long o = ((long)(lh * 4) * ld + r) * 4;
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) off[d * 4 + t] = (uint32_t)(o + ((long)(D + d) * 8 + t) * ld4);
+        }
+    }
+
+    __device__ inline void advance() { base += step; }
+
+    // Slot d's values for k = kb + t (kb = 8 * group + 4h).  With TAIL, k >= K gives zero: such
+    // elements are loaded from k = K - 1 (always in bounds) and then replaced, so that no load is
+    // conditional (a branch around a load would stop the compiler from counting the loads in
+    // flight across the loop, and it would wait for all of them at the top of every trip).
+    template <bool TAIL>
+    __device__ inline void load(f32x4& v, int d, int kb, int K) {
+        if (KC) {
+            asm volatile("" : "+v"(off[0]));
+            const char* q = base + off[0] + (D + d) * 32;
+            if (VEC) {  // K % 4 == 0: the four k are all below K or all at or past it
+                const int back = TAIL ? kb - imin(kb, K - 4) : 0;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(q - back * 4);
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                v = (!TAIL || kb < K) ? x : z;
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int back = TAIL ? kb + t - imin(kb + t, K - 1) : 0;
+                    const float x = reinterpret_cast<const float*>(q)[t - back];
+                    v[t] = (!TAIL || kb + t < K) ? x : 0.f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                asm volatile("" : "+v"(off[d * 4 + t]));
+                const int back = TAIL ? kb + t - imin(kb + t, K - 1) : 0;
+                const float x = *reinterpret_cast<const float*>(base + off[d * 4 + t] - (long)back * ld4);
+                v[t] = (!TAIL || kb + t < K) ? x : 0.f;
+            }
+        }
+    }
+};
+
+template <bool VEC, int D, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * 32, n0 = tn * 32;
     const int lane = threadIdx.x, li = lane & 31, lh = lane >> 5;
     const int K = g.K;
-    const long ldb4 = g.ldb * 4;
-    // Addressing: a workgroup-uniform base per operand, moved D groups per trip, plus 32-bit
-    // per-lane byte offsets that are the same every trip: A's include the group's 32-byte step
-    // as an immediate, B's one offset per (slot, t) row.  The bases start D groups before the
-    // matrices so that the prologue is a trip of loads without MFMAs.
-    const char* pa = reinterpret_cast<const char*>(g.A + (long)m0 * g.lda) - (long)D * 32;
-    const char* pb = reinterpret_cast<const char*>(g.B + n0) - (long)D * 8 * ldb4;
-    uint32_t offA = (uint32_t)(((long)(imin(m0 + li, g.M - 1) - m0) * g.lda + lh * 4) * 4);
-    const uint32_t offB = (uint32_t)(((long)(lh * 4) * g.ldb + (imin(n0 + li, g.N - 1) - n0)) * 4);
-    uint32_t ob[D][4];
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ob[d][t] = offB + (uint32_t)(((long)(D + d) * 8 + t) * ldb4);
+    DirectOperand<!TA, VEC, D> oa;  // A (M x K): k along its rows; A^T (K x M): k down its rows
+    DirectOperand<TB, VEC, D> ob;   // B (K x N): k down its rows; B^T (N x K): k along its rows
+    oa.init(g.A, g.lda, m0, g.M, li, lh);
+    ob.init(g.B, g.ldb, n0, g.N, li, lh);
 
     f32x4 ra[D], rb[D];
-    // Load group q + D + d into slot d (q: the trip's first group).  With TAIL, k >= K gives
-    // zero: such elements are loaded from k = K - 1 (always in bounds) and then replaced, so
-    // that no load is conditional (branches around loads would stop the compiler from
-    // counting the loads in flight across the loop, and it would wait for all of them).
-    auto load = [&](int d, int q, auto tail) {
+    auto load = [&](int d, int q, auto tail) {  // group q + D + d into slot d
         constexpr bool TAIL = decltype(tail)::value;
         const int kb = 8 * (q + D + d) + 4 * lh;
-        // keep the offsets 32-bit and in VGPRs, folded into the loads' base + offset form
-        asm volatile("" : "+v"(offA));
-        const char* qa = pa + offA + (D + d) * 32;
-        if (VEC) {  // K % 4 == 0: the four k values are all below K or all at or past it
-            const int back = TAIL ? kb - imin(kb, K - 4) : 0;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(qa - back * 4);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            ra[d] = (!TAIL || kb < K) ? v : z;
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int back = TAIL ? kb + t - imin(kb + t, K - 1) : 0;
-                const float v = reinterpret_cast<const float*>(qa)[t - back];
-                ra[d][t] = (!TAIL || kb + t < K) ? v : 0.f;
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            asm volatile("" : "+v"(ob[d][t]));
-            const int back = TAIL ? kb + t - imin(kb + t, K - 1) : 0;
-            const float v = *reinterpret_cast<const float*>(pb + ob[d][t] - (long)back * ldb4);
-            rb[d][t] = (!TAIL || kb + t < K) ? v : 0.f;
-        }
+        oa.template load<TAIL>(ra[d], d, kb, K);
+        ob.template load<TAIL>(rb[d], d, kb, K);
     };
     f32x16 acc[1][1];
 #pragma unroll
@@ -981,8 +1015,8 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
         for (int t = 0; t < 4; ++t) acc[0][0] = mfma_step<VEC>(ra[d][t], rb[d][t], acc[0][0]);
     };
     auto advance = [&]() {
-        pa += D * 32;
-        pb += D * 8 * ldb4;
+        oa.advance();
+        ob.advance();
     };
     using Tail = std::integral_constant<bool, true>;
     using Full = std::integral_constant<bool, false>;

@@ -127,13 +127,13 @@ hipError_t launch_mfma_splitk(const GemmArgs& g, hipStream_t stream) {
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
-template <bool VEC, int D>
+template <bool VEC, int D, bool TA = false, bool TB = false>
 hipError_t launch_mfma_direct(const GemmArgs& g, hipStream_t stream) {
     int tiles_m = ceil_div(g.M, 32), tiles_n = ceil_div(g.N, 32);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_direct_kernel<VEC, D>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_direct_kernel<VEC, D, TA, TB>),
                            dim3(tiles_m * tiles_n), dim3(64), args, 0, stream);
 }
 
@@ -183,15 +183,19 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT, VEC,          \
      MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::LDS_BYTES,                                         \
      &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, WIDE, TA, TB, FAIR>, WIDE, 0, TA, TB}
+#define DIRECT_TRANS(D, BK, VEC, TA, TB, NAME) \
+    {NAME, kMfma, 32, 32, BK, 32, 32, 64, VEC, 0, &launch_mfma_direct<VEC, D, TA, TB>, 0, 0, TA, TB}
 // the variants of one transposition (TAG: "nt", "tn" or "tt"; first letter op(A), second op(B));
-// the 128x128 ones with drain ordering (schedule 4)
+// the 128x128 ones with drain ordering (schedule 4); the LDS-free ones (BK = 16 D)
 #define TRANS_SET(TA, TB, TAG)                                                                     \
     TRANS_VARIANT(128, 128, 16, 64, 64, true, false, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_vec"),     \
         TRANS_VARIANT(128, 128, 16, 64, 64, false, false, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_scalar"), \
         TRANS_VARIANT(64, 64, 32, 32, 32, true, false, TA, TB, 0, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_vec"),         \
         TRANS_VARIANT(64, 64, 32, 32, 32, false, false, TA, TB, 0, MFMA_NAME(64, 64, 32, 32, 32) "_" TAG "_scalar"),     \
         TRANS_VARIANT(128, 128, 16, 64, 64, true, true, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_vec"), \
-        TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar")
+        TRANS_VARIANT(128, 128, 16, 64, 64, false, true, TA, TB, 4, MFMA_NAME(128, 128, 16, 64, 64) "_" TAG "_wide_scalar"), \
+        DIRECT_TRANS(8, 128, true, TA, TB, "mfma32r_32x32x128_w32x32_g8_" TAG "_vec"),                                 \
+        DIRECT_TRANS(6, 96, false, TA, TB, "mfma32r_32x32x96_w32x32_g6_" TAG "_scalar")
 #define FAIR_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, P, NAME)                                    \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                                              \
