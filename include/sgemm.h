@@ -26,7 +26,10 @@
  *
  * Streams: work is enqueued on `stream` (0 = the null stream) and the call
  * returns without waiting for it; the usual stream ordering applies.  There is
- * no implicit synchronisation.  Calls are thread-safe (no global mutable state).
+ * no implicit synchronisation.  Calls are thread-safe: the only global state is
+ * read-only after its first use (the dispatch table, each kernel's occupancy and
+ * the device's compute-unit count, computed once).  The library records no
+ * memset and allocates nothing, so calls may be captured into a HIP graph.
  *
  * Semantics of the special cases:
  *   - M == 0 or N == 0: nothing is done (returns 0).
@@ -50,10 +53,11 @@
  * A^T(i, k) = A[k * lda + i], lda >= max(1, M); with op(B) = B^T the stored B
  * is N x K, B^T(k, j) = B[j * ldb + k], ldb >= max(1, K).  A row-major K x M
  * array read as its transpose is the column-major M x K matrix, so these entry
- * points also serve column-major callers.  The kernels read both stored forms
- * with coalesced global loads and transpose while staging into LDS, the staging
- * transpose of "SGEMM CUDA kernel (First Half)", "Part 5: Reduced bank
- * conflict (v3)" (the A tile is written k-major into shared memory).
+ * points also serve column-major callers.  The LDS kernels read both stored
+ * forms with coalesced global loads and transpose while staging into LDS, the
+ * staging transpose of "SGEMM CUDA kernel (First Half)", "Part 5: Reduced bank
+ * conflict (v3)" (the A tile is written k-major into shared memory); the
+ * LDS-free kernel of small grids loads either form straight into registers.
  *
  * Return codes (never aborts, never prints):
  *    0   success (work enqueued, or a valid quick return);
@@ -138,7 +142,8 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   info[0] kind (0 = MFMA 32x32x2 f32, 1 = vector FMA), info[1] BM, info[2] BN,
  *   info[3] BK, info[4] WM (MFMA wave tile rows) or TM (VALU microtile rows),
  *   info[5] WN or TN, info[6] threads per workgroup, info[7] vector loads (0/1),
- *   info[8] LDS bytes per workgroup; when n >= 10, info[9] 64-bit offsets (0/1); when
+ *   info[8] LDS bytes per workgroup (0 for the LDS-free variants "mfma32r_", whose BK
+ *   is the K span of the loads they keep in flight); when n >= 10, info[9] 64-bit offsets (0/1); when
  *   n >= 11, info[10] the number of k-groups splitting K inside one workgroup (1 = none);
  *   when n >= 13, info[11] and info[12]: the variant reads A, resp. B, transposed (0/1).
  *   Variants with info[11] or info[12] set serve only sgemm_op / sgemm_op_ex.
