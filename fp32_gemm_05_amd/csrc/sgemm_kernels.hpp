@@ -921,68 +921,83 @@ sgemm_mfma_splitk_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 // KC: k runs along the stored rows (A, or B^T): a lane's four k values are contiguous, one
 // 128-bit load (VEC) or four 32-bit loads from row min(r0+i, R-1).  Otherwise (B, or A^T) each k
 // is a stored row and the lane reads column min(r0+i, R-1) of it: four 32-bit loads whose 32
-// lanes read 128 contiguous bytes.  Addressing: a workgroup-uniform base moved D groups per
-// trip, plus loop-invariant 32-bit per-lane byte offsets (KC: one, the group's step being an
-// immediate; otherwise one per (slot, t)).  The base starts D groups before the matrix, so the
-// prologue is a trip of loads without MFMAs.  The caller guarantees the offsets fit 32 bits:
-// KC: (31 * ld + 16 D) * 4 < 2^32, otherwise ((16 D - 1) * ld + 32) * 4 < 2^32.
+// lanes read 128 contiguous bytes.  Addressing of the full groups of the main loop: the tile's
+// origin plus a workgroup-uniform byte position that moves D groups per trip, plus
+// loop-invariant 32-bit per-lane byte offsets (KC: one, the group's step being an immediate;
+// otherwise one per (slot, t)), so each load is a scalar base plus a vector offset.  The
+// prologue's and the last trips' groups, which may reach past K, are addressed from the origin
+// with k clamped to K - 1, so no address outside the operand is ever formed.  The caller
+// guarantees the offsets fit 32 bits: KC: (31 * ld + 16 D) * 4 < 2^32, otherwise
+// ((16 D - 1) * ld + 32) * 4 < 2^32.
 template <bool KC, bool VEC, int D>
 struct DirectOperand {
     static constexpr int NO = KC ? 1 : 4 * D;
-    const char* base;
-    long step;
-    long ld4;
+    const char* origin;  // X(r0, 0)
+    long pos;            // byte position of the current trip's first group from the origin
+    long step;           // bytes per trip
+    long ld;
+    int r;               // this lane's clamped row (KC) or column, relative to r0
     uint32_t off[NO];
 
-    __device__ inline void init(const float* X, long ld, int r0, int R, int li, int lh) {
-        ld4 = ld * 4;
-        const long r = imin(r0 + li, R - 1) - r0;
+    __device__ inline void init(const float* X, long ld_, int r0, int R, int li, int lh) {
+        ld = ld_;
+        r = imin(r0 + li, R - 1) - r0;
+        pos = 0;
         if (KC) {
-            base = reinterpret_cast<const char*>(X + (long)r0 * ld) - (long)D * 32;
+            origin = reinterpret_cast<const char*>(X + (long)r0 * ld);
             step = (long)D * 32;
-            off[0] = (uint32_t)((r * ld + lh * 4) * 4);
+            off[0] = (uint32_t)(((long)r * ld + lh * 4) * 4);
         } else {
-            base = reinterpret_cast<const char*>(X + r0) - (long)D * 8 * ld4;
-            step = (long)D * 8 * ld4;
+            origin = reinterpret_cast<const char*>(X + r0);
+            step = (long)D * 8 * ld * 4;
             const long o = ((long)(lh * 4) * ld + r) * 4;
 #pragma unroll
             for (int d = 0; d < D; ++d)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) off[d * 4 + t] = (uint32_t)(o + ((long)(D + d) * 8 + t) * ld4);
+                for (int t = 0; t < 4; ++t) off[d * 4 + t] = (uint32_t)(o + ((long)(D + d) * 8 + t) * ld * 4);
         }
     }
 
-    __device__ inline void advance() { base += step; }
+    __device__ inline void advance() { pos += step; }
 
-    // Slot d's values for k = kb + t (kb = 8 * group + 4h).  With TAIL, k >= K gives zero: such
-    // elements are loaded from k = K - 1 (always in bounds) and then replaced, so that no load is
-    // conditional (a branch around a load would stop the compiler from counting the loads in
-    // flight across the loop, and it would wait for all of them at the top of every trip).
+    // Slot d's values for k = kb + t, kb = 8 g + 4h.  Without TAIL, group g is the trip's
+    // (D + d)-th group from its position and lies wholly below K.  With TAIL (any group), k >= K
+    // gives zero: such elements are read at k = K - 1 (K - 4 for the 128-bit load) and then
+    // replaced, so that no load is conditional (a branch around a load would stop the compiler
+    // from counting the loads in flight across the loop, and it would wait for all of them at
+    // the top of every trip).
     template <bool TAIL>
     __device__ inline void load(f32x4& v, int d, int kb, int K) {
         if (KC) {
-            asm volatile("" : "+v"(off[0]));
-            const char* q = base + off[0] + (D + d) * 32;
-            if (VEC) {  // K % 4 == 0: the four k are all below K or all at or past it
-                const int back = TAIL ? kb - imin(kb, K - 4) : 0;
-                const f32x4 x = *reinterpret_cast<const f32x4*>(q - back * 4);
+            if (!TAIL) {
+                asm volatile("" : "+v"(off[0]));
+                const char* q = origin + pos + off[0] + (D + d) * 32;
+                if (VEC)
+                    v = *reinterpret_cast<const f32x4*>(q);
+                else
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = reinterpret_cast<const float*>(q)[t];
+            } else if (VEC) {  // K % 4 == 0: the four k are all below K or all at or past it
+                const f32x4 x = *reinterpret_cast<const f32x4*>(origin + ((long)r * ld + imin(kb, K - 4)) * 4);
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                v = (!TAIL || kb < K) ? x : z;
+                v = kb < K ? x : z;
             } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const int back = TAIL ? kb + t - imin(kb + t, K - 1) : 0;
-                    const float x = reinterpret_cast<const float*>(q)[t - back];
-                    v[t] = (!TAIL || kb + t < K) ? x : 0.f;
+                    const float x = *reinterpret_cast<const float*>(origin + ((long)r * ld + imin(kb + t, K - 1)) * 4);
+                    v[t] = kb + t < K ? x : 0.f;
                 }
             }
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                asm volatile("" : "+v"(off[d * 4 + t]));
-                const int back = TAIL ? kb + t - imin(kb + t, K - 1) : 0;
-                const float x = *reinterpret_cast<const float*>(base + off[d * 4 + t] - (long)back * ld4);
-                v[t] = (!TAIL || kb + t < K) ? x : 0.f;
+                if (!TAIL) {
+                    asm volatile("" : "+v"(off[d * 4 + t]));
+                    v[t] = *reinterpret_cast<const float*>(origin + pos + off[d * 4 + t]);
+                } else {
+                    const float x = *reinterpret_cast<const float*>(origin + ((long)imin(kb + t, K - 1) * ld + r) * 4);
+                    v[t] = kb + t < K ? x : 0.f;
+                }
             }
         }
     }
@@ -1001,9 +1016,9 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
     ob.init(g.B, g.ldb, n0, g.N, li, lh);
 
     f32x4 ra[D], rb[D];
-    auto load = [&](int d, int q, auto tail) {  // group q + D + d into slot d
+    auto load = [&](int d, int grp, auto tail) {  // group grp into slot d
         constexpr bool TAIL = decltype(tail)::value;
-        const int kb = 8 * (q + D + d) + 4 * lh;
+        const int kb = 8 * grp + 4 * lh;
         oa.template load<TAIL>(ra[d], d, kb, K);
         ob.template load<TAIL>(rb[d], d, kb, K);
     };
@@ -1022,16 +1037,15 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
     using Full = std::integral_constant<bool, false>;
 
     const int ngroups = (K + 7) / 8, nfull = K / 8;
-    // at the top of each trip, slot d holds group q + d (zeros for groups past K)
+    // at the top of the trip at group q, slot d holds group q + d (zeros for groups past K)
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(d, -D, Tail{});
-    advance();
+    for (int d = 0; d < D; ++d) load(d, d, Tail{});
     int q = 0;
     for (; q + 2 * D <= nfull; q += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             mfma(d);
-            load(d, q, Full{});
+            load(d, q + D + d, Full{});
         }
         advance();
     }
@@ -1039,9 +1053,8 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             mfma(d);
-            load(d, q, Tail{});
+            load(d, q + D + d, Tail{});
         }
-        advance();
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) mfma(d);
