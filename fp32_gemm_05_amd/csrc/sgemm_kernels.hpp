@@ -278,17 +278,21 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
             }
         }
     } else {
+        // register r holds row 8*(r/4) + 4*lh + r%4 of the block: one per-lane pointer per block,
+        // and a wave-uniform row step (8*(r/4) + r%4) * ldc per register
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            const int lrow = m_base + i * 32 + lh * 4;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int col = n_base + j * 32 + li;
                 if (col >= N) continue;
+                float* pl = C + (long)lrow * ldc + col;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m_base + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                    if (row < M) {
-                        float* pc = C + (long)row * ldc + col;
+                    const int dr = (r >> 2) * 8 + (r & 3);
+                    if (lrow + dr < M) {
+                        float* pc = pl + dr * ldc;
                         float x = alpha * acc[i][j][r];
                         if (beta != 0.f) x += beta * *pc;
                         *pc = x;
