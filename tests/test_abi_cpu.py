@@ -123,6 +123,52 @@ def test_select_variant_classes():
     assert sg.sgemm_select_variant(0, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4) == -1
 
 
+def _name(v):
+    return sg.sgemm_variant_name(v)
+
+
+@pytest.mark.parametrize("M,N,K,ld_odd,family", [
+    (256, 256, 256, False, "lds"),        # small_shortk: K < 512 keeps the LDS kernels
+    (822, 124, 88, False, "lds"),
+    (512, 512, 512, False, "direct"),     # tiny: under 128 64x64 tiles
+    (333, 555, 777, True, "direct"),
+    (1554, 64, 5093, True, "direct"),     # skinny with few tiles joins the small classes
+    (1024, 1024, 1024, False, "lds"),     # small, aligned: 64x64 workgroups fill the CUs
+    (1001, 1003, 777, True, "direct"),    # small, unaligned
+    (1089, 728, 5752, False, "direct"),   # small_longk, aligned
+    (4096, 4096, 4096, False, "lds"),
+    (65536, 64, 1024, False, "lds"),      # skinny
+])
+def test_dispatch_families(M, N, K, ld_odd, family):
+    """Which kernel family the shape classes pick: the LDS-free kernel (mfma32r_) for tiny grids,
+    unaligned small ones and long-K small aligned ones; LDS kernels elsewhere."""
+    lda, ldb = (K | 1, N | 1) if ld_odd else (K, N)
+    v = sg.sgemm_select_variant(M, N, K, FAKE_A, lda, FAKE_B, ldb, FAKE_C, ldb)
+    assert v >= 0
+    assert _name(v).startswith("mfma32r_") == (family == "direct"), _name(v)
+    assert bool(sg.sgemm_variant_info(v)["vec"]) == (not ld_odd) or family == "lds"
+
+
+@pytest.mark.parametrize("ta,tb,M,N,K,odd,direct", [
+    ("T", "N", 333, 555, 777, True, True),     # tiny: every transposition
+    ("N", "T", 333, 555, 777, True, True),
+    ("T", "T", 512, 512, 512, False, True),
+    ("T", "N", 1001, 1003, 777, True, True),   # small: only with A transposed
+    ("N", "T", 1001, 1003, 777, True, False),
+    ("T", "T", 4096, 4096, 4096, False, False),
+])
+def test_op_dispatch_families(ta, tb, M, N, K, odd, direct):
+    lda = M if ta == "T" else K
+    ldb = K if tb == "T" else N
+    ldc = N
+    if odd:
+        lda, ldb, ldc = lda | 1, ldb | 1, ldc | 1
+    v = sg.sgemm_op_select_variant(ta, tb, M, N, K, FAKE_A, lda, FAKE_B, ldb, FAKE_C, ldc)
+    info = sg.sgemm_variant_info(v)
+    assert (info["trans_a"], info["trans_b"]) == (int(ta == "T"), int(tb == "T"))
+    assert _name(v).startswith("mfma32r_") == direct, _name(v)
+
+
 @pytest.mark.parametrize("tiles_m,tiles_n,group_m", [
     (1, 1, 8), (1, 7, 8), (7, 1, 8), (32, 32, 8), (24, 40, 8), (3, 5, 2), (512, 1, 8), (17, 9, 4),
     (64, 64, 8), (2, 2, 8), (9, 33, 16)])
