@@ -485,3 +485,40 @@ def test_large_extents_sampled(label, M, N, K, dist, alpha, beta):
         check_within_bound(got, ref, bound, label)
     del dA, dB, dC
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------------------
+# the LDS-free kernel at its 32-bit offset limits: leading dimensions just under the limit run
+# it, just over fall back to the 64-bit-offset variant; both exact on integer data
+# ------------------------------------------------------------------------------------------
+
+OFFSET_LIMITS = [
+    # (label, lda, ldb, expected family): M, N, K = 40, 36, 600 (the tiny class)
+    ("lda_under_limit", 33_000_000, 36, "mfma32r_"),    # (31*lda + 128)*4 < 2^32
+    ("lda_over_limit", 35_000_000, 36, "_wide"),
+    ("ldb_under_limit", 600, 8_000_000, "mfma32r_"),    # (127*ldb + 32)*4 < 2^32
+    ("ldb_over_limit", 600, 8_500_000, "_wide"),
+]
+
+
+@pytest.mark.parametrize("label,lda,ldb,family", OFFSET_LIMITS, ids=[x[0] for x in OFFSET_LIMITS])
+def test_direct_kernel_offset_limits(label, lda, ldb, family):
+    M, N, K = 40, 36, 600
+    rng = np.random.default_rng(lda + ldb)
+    A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+    B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+    C = np.zeros((M, N), np.float32)
+    bufA, vA, lda_ = device_matrix(A, pad_cols=lda - K)
+    bufB, vB, ldb_ = device_matrix(B, pad_cols=ldb - N)
+    bufC, vC, ldc = device_matrix(C, fill=SENTINEL)
+    assert (lda_, ldb_) == (lda, ldb)
+    vid = sg.sgemm_select_variant(M, N, K, vA.data_ptr(), lda, vB.data_ptr(), ldb, vC.data_ptr(), ldc)
+    name = sg.sgemm_variant_name(vid)
+    _say(f"[offset limits] {label}: lda={lda} ldb={ldb} variant={name}")
+    assert family in name
+    sg.sgemm(M, N, K, 1.0, vA.data_ptr(), lda, vB.data_ptr(), ldb, 0.0, vC.data_ptr(), ldc)
+    torch.cuda.synchronize()
+    ref, _ = oracle.ref_rows(A, B, C, 1.0, 0.0)
+    check_exact(vC.cpu().numpy(), ref, label)
+    del bufA, bufB, bufC, vA, vB, vC
+    torch.cuda.empty_cache()
