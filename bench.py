@@ -7,7 +7,7 @@ A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
                     [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline] [--cpu-full]
-                    [--cpu-threads N] [--cold | --cold-dirty]
+                    [--cpu-threads N] [--cold | --cold-dirty] [--shard-rows G]
 
 ``--op`` other than NN stores A as K x M and/or B as N x K and times
 ``sgemm_op`` (op(A) * op(B)) on the same logical product.
@@ -151,6 +151,9 @@ def main() -> int:
                     help="read a 512 MiB buffer before every timed launch (evicts the operands from the L2s "
                          "and the Infinity Cache, leaving clean lines, so the operands come from HBM); each "
                          "launch is then timed between its own two events")
+    ap.add_argument("--shard-rows", type=int, default=1, metavar="G",
+                    help="time one GPU's share of the workload split by rows over G GPUs (the first "
+                         "ceil(M/G) rows of A and C, all of B) on this GPU; no collective is run")
     ap.add_argument("--cold-dirty", action="store_true",
                     help="as --cold, but overwrite the 512 MiB buffer instead: the caches then hold dirty lines "
                          "whose write-back competes with the timed launch")
@@ -176,6 +179,9 @@ def main() -> int:
         return 1
 
     w = WORKLOADS[args.workload or HEADLINE]
+    if args.shard_rows > 1:
+        from dataclasses import replace
+        w = replace(w, name=f"{w.name}_rows1of{args.shard_rows}", M=-(-w.M // args.shard_rows))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload: {w.describe()}")
@@ -296,7 +302,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": (f"sgemm{'' if args.op == 'NN' else '_op ' + args.op} {w.M}x{w.N}x{w.K} "
-                         f"alpha={w.alpha:g} beta={w.beta:g} {w.dist} seed={w.seed}"),
+                         f"alpha={w.alpha:g} beta={w.beta:g} {w.dist} seed={w.seed}"
+                         + (f" (one GPU's row share of a {args.shard_rows}-GPU split)" if args.shard_rows > 1 else "")),
             "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
             "op": args.op, "variant": vname,
         },

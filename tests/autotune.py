@@ -45,6 +45,11 @@ CASES = [
     ("shallow3072x3072x768", "shallow", "square1024_beta", 3072, 3072, 768, None, None, None, True),
     ("medium2585x6716x2000", "medium", "square4096", 2585, 6716, 2000, None, None, None, True),
     ("medium3000x3000x3000", "medium", "square4096", 3000, 3000, 3000, None, None, None, True),
+    ("shard1024x4096x4096", "medium", "square4096", 1024, 4096, 4096, None, None, None, True),
+    ("shard2048x4096x4096", "long_k", "square4096", 2048, 4096, 4096, None, None, None, True),
+    ("shard1024x8192x8192", "long_k", "square8192", 1024, 8192, 8192, None, None, None, True),
+    ("longk2047x4095x4097", "long_k", "ragged3001x5003x777", 2047, 4095, 4097, None, None, None, False),
+    ("longk1500x6000x6000", "long_k", "ragged3001x5003x777", 1500, 6000, 6001, None, None, None, False),
     ("medium2062x3171x3921", "medium", "ragged3001x5003x777", 2062, 3171, 3921, None, None, None, False),
     ("medium5000x2001x2501", "medium", "ragged3001x5003x777", 5000, 2001, 2501, None, None, None, False),
     ("tinyk5555x1124x68", "tiny_k", "square4096", 5555, 1124, 68, None, None, None, True),
@@ -53,8 +58,9 @@ CASES = [
     ("tinyk3001x4001x101", "tiny_k", "ragged3001x5003x777", 3001, 4001, 101, None, None, None, False),
     ("tinyk2048x2047x33", "tiny_k", "ragged3001x5003x777", 2048, 2047, 33, None, None, None, False),
     ("longk1024x1024x4096", "small_longk", "square1024_beta", 1024, 1024, 4096, None, None, None, True),
+    ("shard512x4096x4096", "medium", "square4096", 512, 4096, 4096, None, None, None, True),
     ("longk1089x728x5752", "small_longk", "square4096", 1089, 728, 5752, None, None, None, True),
-    ("longk1751x907x5323", "small_longk", "ragged3001x5003x777", 1751, 907, 5323, None, None, None, False),
+    ("longk1751x907x5323", "medium", "ragged3001x5003x777", 1751, 907, 5323, None, None, None, False),
     ("longk777x1501x3001", "small_longk", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
     ("square256", "small_shortk", "square256", None, None, None, None, None, None, True),
     ("shortk822x124x88", "small_shortk", "square256", 822, 124, 88, None, None, None, True),
@@ -86,7 +92,7 @@ COLD_CLASSES = {"skinny"}
 STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
-             "small_shortk": "kSmallShortK"}
+             "small_shortk": "kSmallShortK", "long_k": "kLongK"}
 
 
 def log(msg):
@@ -172,7 +178,7 @@ def main() -> int:
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
-                    default="large,huge,shallow,medium,tiny_k,small,tiny,small_shortk,small_longk,skinny")
+                    default="large,huge,long_k,shallow,medium,tiny_k,small,tiny,small_shortk,small_longk,skinny")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,
