@@ -70,6 +70,11 @@ CASES = [
     ("tiny1554x64x5093", "tiny", "ragged3001x5003x777", 1554, 64, 5093, None, None, None, False),
     ("square1024_beta", "small", "square1024_beta", None, None, None, None, None, None, True),
     ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
+    ("full1111x1113x1001", "small_full", "ragged3001x5003x777", 1111, 1113, 1001, None, None, None, False),
+    ("full900x1500x833", "small_full", "ragged3001x5003x777", 900, 1500, 833, None, None, None, False),
+    ("full1200x1300x700", "small_full", "square1024_beta", 1200, 1300, 700, None, None, None, True),
+    ("small892x1083x609", "small", "ragged3001x5003x777", 892, 1083, 609, None, None, None, False),
+    ("small1000x800x1000", "small", "square1024_beta", 1000, 800, 1000, None, None, None, True),
     ("small512x512x512", "tiny", "square256", 512, 512, 512, None, None, None, True),
     ("tiny333x555x777", "tiny", "ragged3001x5003x777", 333, 555, 777, None, None, None, False),
     ("tiny600x200x1000", "tiny", "ragged3001x5003x777", 600, 200, 1000, None, None, None, False),
@@ -92,7 +97,7 @@ COLD_CLASSES = {"skinny"}
 STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
-             "small_shortk": "kSmallShortK", "long_k": "kLongK"}
+             "small_shortk": "kSmallShortK", "long_k": "kLongK", "small_full": "kSmallFull"}
 
 
 def log(msg):
@@ -178,7 +183,8 @@ def main() -> int:
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
-                    default="large,huge,long_k,shallow,medium,tiny_k,small,tiny,small_shortk,small_longk,skinny")
+                    default="large,huge,long_k,shallow,medium,tiny_k,small,small_full,tiny,small_shortk,small_longk,"
+                            "skinny")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,

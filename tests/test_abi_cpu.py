@@ -135,6 +135,7 @@ def _name(v):
     (1554, 64, 5093, True, "direct"),     # skinny with few tiles joins the small classes
     (1024, 1024, 1024, False, "lds"),     # small, aligned: 64x64 workgroups fill the CUs
     (1001, 1003, 777, True, "direct"),    # small, unaligned
+    (1111, 1113, 1001, True, "lds"),      # small_full: more than one 64x64 tile per CU
     (1089, 728, 5752, False, "direct"),   # small_longk, aligned
     (4096, 4096, 4096, False, "lds"),
     (65536, 64, 1024, False, "lds"),      # skinny
