@@ -13,6 +13,9 @@
         HBM bytes per launch of one kernel from two --pmc runs, each scaled by the copy calibration.
     python -m fp32_gemm_05_amd.profiling counters <counter_collection.csv> --kernel SUBSTR --out X.md
         per-dispatch means of any collected counters for one kernel.
+    python -m fp32_gemm_05_amd.profiling collect --dir D --workload W [--warmup N] [--out-dir profiles]
+        runs every rocprofv3 pass below (each as a child process with its own time limit) and then
+        `report`: the one command behind each committed summary.
     python -m fp32_gemm_05_amd.profiling report --dir D --workload W --out-dir profiles
         one summary per (kernel, workload) from the runs the profiling commands below leave in D:
           D/trace_W   rocprofv3 --kernel-trace --stats ... -- python bench.py --workload W --no-cpu-baseline
@@ -282,6 +285,9 @@ def cmd_report(args) -> None:
     trace_opt = f"--trace-args='{args.trace_args}' " if args.trace_args else ""
     sq_warm = args.sq_warmup
     cmds = [
+        f"python -m fp32_gemm_05_amd.profiling collect --dir <dir> --workload {W} "
+        f"{'--warmup ' + args.trace_args.split()[-1] + ' ' if args.trace_args.startswith('--warmup') else ''}"
+        f"(runs all of the following)",
         f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} "
         f"{args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
@@ -354,6 +360,59 @@ def cmd_report(args) -> None:
     print("\n".join(lines))
 
 
+# Counter passes of one summary: each rocprofv3 --pmc run stays within one pass's limits
+# (at most 8 SQ counters and 4 TCC counters; FETCH_SIZE alone takes 3 TCC counters).
+PMC_PASSES = [
+    ("fetch", ["FETCH_SIZE"]),
+    ("write", ["WRITE_SIZE"]),
+    ("rdreq", ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]),
+    ("sq", ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "SQ_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "GRBM_GUI_ACTIVE"]),
+]
+
+
+def _run(cmd, log, timeout):
+    """Run one profiler command as a child process (this process never touches the GPU)."""
+    import subprocess
+    print("+ " + " ".join(cmd), flush=True)
+    with open(log, "w") as f:
+        res = subprocess.run(cmd, stdout=f, stderr=subprocess.STDOUT, timeout=timeout)
+    if res.returncode != 0:
+        raise SystemExit(f"command failed ({res.returncode}), see {log}: {' '.join(cmd)}")
+
+
+def cmd_collect(args) -> None:
+    """All the runs one summary needs, then the summary: the copy calibration (once per directory),
+    the kernel trace of the bench (with --warmup so that the clock has ramped up), the four counter
+    passes, and `report`.  Each profiler run is a child process with its own time limit."""
+    d, W = args.dir, args.workload
+    os.makedirs(d, exist_ok=True)
+    py = sys.executable
+    rp = ["rocprofv3", "--output-format", "csv"]
+    copy = [py, "-u", "-m", "fp32_gemm_05_amd.profiling", "copy", "--mib", "1024", "--reps", "3"]
+    for tag, counters in (("copy_fetch", ["FETCH_SIZE"]), ("copy_write", ["WRITE_SIZE"]),
+                          ("copy_rdreq", PMC_PASSES[2][1])):
+        if not os.path.isdir(os.path.join(d, tag)):
+            _run(rp + ["--pmc", *counters, "-d", os.path.join(d, tag), "-o", "run", "--", *copy],
+                 os.path.join(d, tag + ".log"), 120)
+    bench = [py, "-u", os.path.join(ROOT, "bench.py"), "--workload", W]
+    _run(rp + ["--kernel-trace", "--stats", "-d", os.path.join(d, f"trace_{W}"), "-o", "run", "--", *bench,
+               "--warmup", str(args.warmup), "--no-cpu-baseline"], os.path.join(d, f"trace_{W}.log"), 300)
+    variant = None
+    with open(os.path.join(d, f"trace_{W}.log")) as f:
+        for line in f:
+            if line.startswith("variant: "):
+                variant = line.split()[1]
+    if variant is None:
+        raise SystemExit("the bench did not report its variant")
+    for tag, counters in PMC_PASSES:
+        _run(rp + ["--pmc", *counters, "-d", os.path.join(d, f"{tag}_{W}"), "-o", "run", "--", *bench,
+                   "--steps", "3", "--warmup", "1", "--no-cpu-baseline"], os.path.join(d, f"{tag}_{W}.log"), 120)
+    report = argparse.Namespace(dir=d, workload=W, variant=variant, steps=200, sq_warmup=1,
+                                trace_args=f"--warmup {args.warmup}", out_dir=args.out_dir, note="")
+    cmd_report(report)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -391,6 +450,11 @@ def main(argv=None) -> int:
     p.add_argument("--command", required=True)
     p.add_argument("--note", default="")
     p.add_argument("--out", required=True)
+    p = sub.add_parser("collect", help="run every profiler pass of one workload and write its summary")
+    p.add_argument("--dir", required=True, help="where the raw rocprofv3 output goes")
+    p.add_argument("--workload", required=True)
+    p.add_argument("--warmup", type=int, default=100, help="bench warmup of the traced run")
+    p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     p = sub.add_parser("report")
     p.add_argument("--dir", required=True)
     p.add_argument("--workload", required=True)
@@ -404,6 +468,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.cmd == "report":
         cmd_report(args)
+    elif args.cmd == "collect":
+        cmd_collect(args)
     elif args.cmd == "copy":
         run_copy(args.mib, args.reps)
     elif args.cmd == "read":
