@@ -50,7 +50,7 @@ def stored_traffic(workload: str, variant: str):
     with open(path) as f:
         rec = json.load(f)
     from fp32_gemm_05_amd.profiling import kernel_source_hash
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(variant):
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -289,5 +289,7 @@ const Variant kVariants[] = {
     {"mfma32r_32x32x128_w32x32_g8_scalar", kMfma, 32, 32, 128, 32, 32, 64, 0, 0, &launch_mfma_direct<false, 8>, 0},
     {"mfma32r_32x32x96_w32x32_g6_vec", kMfma, 32, 32, 96, 32, 32, 64, 1, 0, &launch_mfma_direct<true, 6>, 0},
     {"mfma32r_32x32x96_w32x32_g6_scalar", kMfma, 32, 32, 96, 32, 32, 64, 0, 0, &launch_mfma_direct<false, 6>, 0},
+    // skinny streams: four 64x32 wave tiles per 128x64 workgroup (the B panel stays in L2)
+    NTA_FAIR_VARIANT(128, 64, 32, 64, 32, true, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_vec"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

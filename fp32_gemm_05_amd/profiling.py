@@ -49,12 +49,28 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ("sgemm_kernels.hpp", "sgemm_launch.hpp")
 
 
-def kernel_source_hash() -> str:
+def _strip_variant_table(text: bytes) -> bytes:
+    """The launch source without the body of its variant table: appending or editing other
+    variants' rows leaves every kernel's own code, and so its counters, unchanged."""
+    start = text.find(b"const Variant kVariants[] = {")
+    if start < 0:
+        return text
+    end = text.find(b"\n};", start)
+    return text[:start] + text[end:] if end >= 0 else text
+
+
+def kernel_source_hash(variant: str) -> str:
+    """Hash of the kernel code a variant runs: the kernel templates, the launch code (without the
+    variant table) and the variant's name, which spells out its template configuration."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp32_gemm_05_amd", "csrc")
     for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+            text = f.read()
+        if name == "sgemm_launch.hpp":
+            text = _strip_variant_table(text)
+        h.update(name.encode() + b"\0" + text)
+    h.update(b"variant\0" + variant.encode())
     return h.hexdigest()[:16]
 
 
@@ -187,7 +203,7 @@ def cmd_traffic(args) -> None:
         "copy_bytes": args.copy_bytes, "copy_FETCH_SIZE_KiB": cfetch, "copy_WRITE_SIZE_KiB": cwrite,
         "fetch_scale": f_scale, "write_scale": w_scale,
         "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": args.alg_bytes,
-        "kernel_source_hash": kernel_source_hash(), "commands": args.commands,
+        "kernel_source_hash": kernel_source_hash(args.variant), "commands": args.commands,
     }
     with open(args.out, "w") as f:
         json.dump(rec, f, indent=1)
@@ -354,7 +370,7 @@ def cmd_report(args) -> None:
            "l2_read_bytes_by_request_size": rd_bytes, "algorithmic_bytes_per_launch": alg_bytes,
            "mfma_busy": mfma_util, "mfma_busy_last_dispatch": mfma_last, "sclk_ghz_last_dispatch": sclk_last if last_ns >= 150_000 else None,
            "lds_bank_conflict_per_cu_cycle": lds_conf,
-           "kernel_source_hash": kernel_source_hash(), "commands": cmds}
+           "kernel_source_hash": kernel_source_hash(variant), "commands": cmds}
     with open(os.path.join(args.out_dir, f"traffic_{variant}_{W}.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print("\n".join(lines))
