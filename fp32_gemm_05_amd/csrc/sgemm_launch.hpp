@@ -291,5 +291,9 @@ const Variant kVariants[] = {
     {"mfma32r_32x32x96_w32x32_g6_scalar", kMfma, 32, 32, 96, 32, 32, 64, 0, 0, &launch_mfma_direct<false, 6>, 0},
     // skinny streams: four 64x32 wave tiles per 128x64 workgroup (the B panel stays in L2)
     NTA_FAIR_VARIANT(128, 64, 32, 64, 32, true, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_vec"),
+    // N <= 32 streams: 32-wide workgroups (64-wide ones would compute half padding)
+    NTA_FAIR_VARIANT(128, 32, 32, 32, 32, true, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_vec"),
+    NTA_FAIR_VARIANT(128, 32, 32, 32, 32, false, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_scalar"),
+    NTA_FAIR_VARIANT(256, 32, 32, 64, 32, true, 0, MFMA_NAME(256, 32, 32, 64, 32) "_nta_vec"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

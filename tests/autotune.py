@@ -84,8 +84,12 @@ CASES = [
     ("ragged700x900x1301", "small", "ragged3001x5003x777", 700, 900, 1301, None, None, None, False),
     ("skinny65536x64x1024", "skinny", "skinny65536x64x1024", None, None, None, None, None, None, True),
     ("skinny65536x61x1021", "skinny", "skinny65536x64x1024", 65536, 61, 1021, None, None, None, False),
-    ("skinny262144x32x512", "skinny", "skinny65536x64x1024", 262144, 32, 512, None, None, None, True),
     ("skinny100003x47x777", "skinny", "ragged3001x5003x777", 100003, 47, 777, None, None, None, False),
+    ("narrow262144x32x512", "narrow", "skinny65536x64x1024", 262144, 32, 512, None, None, None, True),
+    ("narrow131072x16x1024", "narrow", "skinny65536x64x1024", 131072, 16, 1024, None, None, None, True),
+    ("narrow65536x24x2048", "narrow", "skinny65536x64x1024", 65536, 24, 2048, None, None, None, True),
+    ("narrow100003x29x777", "narrow", "ragged3001x5003x777", 100003, 29, 777, None, None, None, False),
+    ("narrow200003x7x333", "narrow", "ragged3001x5003x777", 200003, 7, 333, None, None, None, False),
 ]
 # Classes timed in three cache states, each state scored as a case of its own: "warm"
 # (back-to-back launches), "cold" (each timed launch follows a read of a 512 MiB buffer, which
@@ -93,11 +97,12 @@ CASES = [
 # "dirty" (the 512 MiB buffer is overwritten instead, so dirty lines are written back while the
 # launch runs).  The skinny class streams A from HBM: warm launches alone would time it partly
 # out of the Infinity Cache, and cold ones alone would miss what evicting dirty lines costs.
-COLD_CLASSES = {"skinny"}
+COLD_CLASSES = {"skinny", "narrow"}
 STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
-             "small_shortk": "kSmallShortK", "long_k": "kLongK", "small_full": "kSmallFull"}
+             "small_shortk": "kSmallShortK", "long_k": "kLongK", "small_full": "kSmallFull",
+             "narrow": "kNarrow"}
 
 
 def log(msg):
@@ -184,7 +189,7 @@ def main() -> int:
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
                     default="large,huge,long_k,shallow,medium,tiny_k,small,small_full,tiny,small_shortk,small_longk,"
-                            "skinny")
+                            "skinny,narrow")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,

@@ -118,6 +118,9 @@ def test_select_variant_classes():
     assert 0 <= ragged < n and sg.sgemm_variant_info(ragged)["vec"] == 0
     skinny = sg.sgemm_select_variant(65536, 64, 1024, FAKE_A, 1024, FAKE_B, 64, FAKE_C, 64)
     assert 0 <= skinny < n and sg.sgemm_variant_info(skinny)["BN"] <= 64
+    # N <= 32 streams: an aligned one gets 32-wide workgroups, not half-padded 64-wide ones
+    narrow = sg.sgemm_select_variant(262144, 32, 512, FAKE_A, 512, FAKE_B, 32, FAKE_C, 32)
+    assert 0 <= narrow < n and sg.sgemm_variant_info(narrow)["BN"] == 32
     mis = sg.sgemm_select_variant(4096, 4096, 4096, FAKE_A + 4, 4096, FAKE_B, 4096, FAKE_C, 4096)
     assert sg.sgemm_variant_info(mis)["vec"] == 0
     assert sg.sgemm_select_variant(0, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4) == -1

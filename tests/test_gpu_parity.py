@@ -96,6 +96,7 @@ REDUCED = [
     ("square1024_beta", "square1024_beta", 1024, 1024, 1024),
     ("ragged_reduced", "ragged3001x5003x777", 301, 503, 77),
     ("skinny_reduced", "skinny65536x64x1024", 4099, 64, 136),
+    ("narrow_reduced", "skinny65536x64x1024", 4101, 28, 140),
     ("square_tail", "square4096", 389, 260, 300),
 ]
 
@@ -452,6 +453,8 @@ LARGE = [
     ("tall_n1", 1_000_003, 1, 64, "int", 0.5, 0.0),
     ("long_k", 96, 80, 1_000_001, "int", 1.0, 0.0),
     ("k1_wide", 4099, 20000, 1, "uniform", 2.0, 0.0),
+    ("narrow_stream", 262144, 32, 512, "uniform", 1.0, 0.0),
+    ("narrow_unaligned", 100003, 29, 777, "int", 1.0, 0.0),
 ]
 
 
