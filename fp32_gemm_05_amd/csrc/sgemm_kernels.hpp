@@ -250,12 +250,68 @@ __device__ __attribute__((always_inline)) inline f32x16 mfma_step(float a, float
 // upright (32 lanes along a row: coalesced 32-bit stores).
 // (Scalars are passed by value: taking the argument struct by reference makes the compiler
 // keep an addressable copy of it, which it may place in LDS.)
+// The C values a wave's output blocks need for the beta term, in the accumulators' layout
+// (entries outside the matrix are left unset; the epilogue skips them).  Kernels of one-round
+// grids read them at the start of the tile, after their first operand loads, so that the
+// read's latency hides under the K loop instead of stalling the epilogue.
 template <int FM, int FN, bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma_load_c(int M, int N, const float* __restrict__ C,
+                                                                  long ldc, f32x16 (&cv)[FM][FN], int m_base,
+                                                                  int n_base, int li, int lh) {
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = m_base + i * 32 + li;
+            if (row >= M) continue;
+            const float* prow = C + (long)row * ldc;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n_base + j * 32 + q * 8 + lh * 4;
+                    if (col >= N) continue;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(prow + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cv[i][j][4 * q + e] = v[e];
+                }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int lrow = m_base + i * 32 + lh * 4;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n_base + j * 32 + li;
+                if (col >= N) continue;
+                const float* pl = C + (long)lrow * ldc + col;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dr = (r >> 2) * 8 + (r & 3);
+                    if (lrow + dr < M) cv[i][j][r] = pl[dr * ldc];
+                }
+            }
+        }
+    }
+}
+
+// C := alpha * acc + beta * C over a wave's output blocks.  With beta != 0 the C values of a
+// block are loaded before its first store: the row stride is a run-time value, so the compiler
+// cannot tell a later load from an earlier store's address and would otherwise wait out one
+// memory round trip per loaded value.  (The 128-bit path's loads of one row differ by constant
+// offsets and already issue together; with several blocks per wave it keeps them that way,
+// which needs no extra registers.)  With PRE the C values come from cv instead, filled by
+// mfma_load_c at the start of the tile.
+template <int FM, int FN, bool VEC, bool PRE = false>
 __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N, float alpha, float beta,
                                                                     float* __restrict__ C, long ldc,
                                                                     const f32x16 (&acc)[FM][FN], int m_base,
-                                                                    int n_base, int li, int lh) {
+                                                                    int n_base, int li, int lh,
+                                                                    const f32x16 (*cv)[FN] = nullptr) {
     if (VEC) {
+        constexpr bool BATCH = PRE || FM * FN == 1;  // C values taken from registers
+        f32x16 cl[FM][FN];
+        if (BATCH && !PRE && beta != 0.f) mfma_load_c<FM, FN, VEC>(M, N, C, ldc, cl, m_base, n_base, li, lh);
+        const f32x16 (*cs)[FN] = PRE ? cv : cl;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int row = m_base + i * 32 + li;
@@ -272,7 +328,15 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
                                acc[i][j][4 * q + 3]};
                     v *= alpha;
                     f32x4* pc = reinterpret_cast<f32x4*>(prow + col);
-                    if (beta != 0.f) v += beta * *pc;
+                    if (beta != 0.f) {
+                        if (BATCH) {
+                            const f32x4 c = {cs[i][j][4 * q + 0], cs[i][j][4 * q + 1], cs[i][j][4 * q + 2],
+                                             cs[i][j][4 * q + 3]};
+                            v += beta * c;
+                        } else {
+                            v += beta * *pc;
+                        }
+                    }
                     *pc = v;
                 }
             }
@@ -288,14 +352,23 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
                 const int col = n_base + j * 32 + li;
                 if (col >= N) continue;
                 float* pl = C + (long)lrow * ldc + col;
+                f32x16 c;
+                if (PRE) {
+                    c = cv[i][j];
+                } else if (beta != 0.f) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int dr = (r >> 2) * 8 + (r & 3);
+                        if (lrow + dr < M) c[r] = pl[dr * ldc];
+                    }
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int dr = (r >> 2) * 8 + (r & 3);
                     if (lrow + dr < M) {
-                        float* pc = pl + dr * ldc;
                         float x = alpha * acc[i][j][r];
-                        if (beta != 0.f) x += beta * *pc;
-                        *pc = x;
+                        if (beta != 0.f) x += beta * c[r];
+                        pl[dr * ldc] = x;
                     }
                 }
             }
@@ -630,7 +703,8 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 // after the barrier of slab s-1, and every wave finished its reads of that stage (slab s-1)
 // before reaching that barrier (the barrier waits for outstanding LDS accesses).
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false,
+          bool CPRE = false>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -701,6 +775,8 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         la.template fetch_slab<1>(BK, BK, K);
         lb.template fetch_slab<1>(BK, BK, K);
     }
+    f32x16 cv[FM][FN];  // CPRE: C for the beta term, read after the first operand loads
+    if (CPRE && g.beta != 0.f) mfma_load_c<FM, FN, VEC>(g.M, g.N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
     __syncthreads();
     MfmaFrag<FM, FN> F[2];
     read_frag(F[0], lds_a, lds_b, 0);
@@ -763,7 +839,7 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         ++s;
     }
 
-    mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
+    mfma_epilogue<FM, FN, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1007,7 +1083,7 @@ struct DirectOperand {
     }
 };
 
-template <bool VEC, int D, bool TA = false, bool TB = false>
+template <bool VEC, int D, bool TA = false, bool TB = false, bool CPRE = false>
 __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -1044,6 +1120,8 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
     // at the top of the trip at group q, slot d holds group q + d (zeros for groups past K)
 #pragma unroll
     for (int d = 0; d < D; ++d) load(d, d, Tail{});
+    f32x16 cv[1][1];  // CPRE: C for the beta term, read after the ring's first loads
+    if (CPRE && g.beta != 0.f) mfma_load_c<1, 1, VEC>(g.M, g.N, g.C, g.ldc, cv, m0, n0, li, lh);
     int q = 0;
     for (; q + 2 * D <= nfull; q += D) {
 #pragma unroll
@@ -1063,7 +1141,7 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
 #pragma unroll
     for (int d = 0; d < D; ++d) mfma(d);
 
-    mfma_epilogue<1, 1, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0, n0, li, lh);
+    mfma_epilogue<1, 1, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0, n0, li, lh, cv);
 }
 
 // ---------------------------------------------------------------------------------

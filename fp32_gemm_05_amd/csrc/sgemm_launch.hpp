@@ -84,10 +84,11 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
                            stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false,
+          bool CPRE = false>
 hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR, NTA>;
+    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR, NTA, CPRE>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -127,13 +128,13 @@ hipError_t launch_mfma_splitk(const GemmArgs& g, hipStream_t stream) {
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
-template <bool VEC, int D, bool TA = false, bool TB = false>
+template <bool VEC, int D, bool TA = false, bool TB = false, bool CPRE = false>
 hipError_t launch_mfma_direct(const GemmArgs& g, hipStream_t stream) {
     int tiles_m = ceil_div(g.M, 32), tiles_n = ceil_div(g.N, 32);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_direct_kernel<VEC, D, TA, TB>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_mfma_direct_kernel<VEC, D, TA, TB, CPRE>),
                            dim3(tiles_m * tiles_n), dim3(64), args, 0, stream);
 }
 
@@ -218,6 +219,9 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define NTA_DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                      \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0, P, true>, 0}
+#define CP_DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                       \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0, P, false, true>, 0}
 #define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
 #define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
     DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
@@ -295,5 +299,16 @@ const Variant kVariants[] = {
     NTA_FAIR_VARIANT(128, 32, 32, 32, 32, true, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_vec"),
     NTA_FAIR_VARIANT(128, 32, 32, 32, 32, false, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_scalar"),
     NTA_FAIR_VARIANT(256, 32, 32, 64, 32, true, 0, MFMA_NAME(256, 32, 32, 64, 32) "_nta_vec"),
+    // C for the beta term read at the start of the tile ("_cp"): one-round grids
+    CP_DEEP_VARIANT(64, 64, 32, 32, 32, true, 0, DEEP_NAME(64, 64, 32, 32, 32) "_cp_vec"),
+    CP_DEEP_VARIANT(64, 64, 32, 32, 32, false, 0, DEEP_NAME(64, 64, 32, 32, 32) "_cp_scalar"),
+    CP_DEEP_VARIANT(64, 64, 32, 32, 32, true, 3, DEEP_NAME(64, 64, 32, 32, 32) "_d3_cp_vec"),
+    CP_DEEP_VARIANT(64, 64, 32, 32, 32, false, 3, DEEP_NAME(64, 64, 32, 32, 32) "_d3_cp_scalar"),
+    {"mfma32r_32x32x128_w32x32_g8_cp_vec", kMfma, 32, 32, 128, 32, 32, 64, 1, 0,
+     &launch_mfma_direct<true, 8, false, false, true>, 0},
+    {"mfma32r_32x32x96_w32x32_g6_cp_scalar", kMfma, 32, 32, 96, 32, 32, 64, 0, 0,
+     &launch_mfma_direct<false, 6, false, false, true>, 0},
+    {"mfma32r_32x32x96_w32x32_g6_cp_vec", kMfma, 32, 32, 96, 32, 32, 64, 1, 0,
+     &launch_mfma_direct<true, 6, false, false, true>, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

@@ -120,6 +120,40 @@ def read_table():
     return out
 
 
+def choose_winners(results, keep_margin):
+    """Per (class, vector-load class): the variant with the smallest geometric-mean slowdown
+    against the per-case best, among those that ran and passed parity on every case.  The table's
+    current entry is kept unless it is slower than that winner by more than keep_margin (run-to-run
+    variation of these scores is about 1 %)."""
+    incumbent = read_table()
+    winners = {}
+    for cls in sorted({r["class"] for r in results}):
+        for vclass in (0, 1):
+            recs = [r for r in results if r["class"] == cls and r["vec_class"] == vclass]
+            if not recs:
+                continue
+            cases = sorted({r["case"] for r in recs})
+            best = {c: min(r["ms_median"] for r in recs if r["case"] == c and r["parity"]) for c in cases}
+            score = {}
+            for name in sorted({r["variant"] for r in recs}):
+                rs = {r["case"]: r for r in recs if r["variant"] == name}
+                if set(rs) != set(cases) or not all(r["parity"] for r in rs.values()):
+                    continue
+                # a vector-load class may also be served by a scalar-load variant, never the reverse
+                score[name] = math.exp(sum(math.log(rs[c]["ms_median"] / best[c]) for c in cases) / len(cases))
+            if not score:
+                continue
+            win = min(score, key=score.get)
+            old = incumbent.get((cls, vclass), (None, 0.0))[0]
+            if old in score and old != win and score[old] <= score[win] * (1.0 + keep_margin):
+                log(f"keep {cls}/{'vec' if vclass else 'scalar'}: {old} ({score[old]:.3f}; "
+                    f"{win} {score[win]:.3f} is within the margin)")
+                win = old
+            winners[(cls, vclass)] = (win, score[win])
+            log(f"winner {cls}/{'vec' if vclass else 'scalar'}: {win} (geo-mean slowdown {score[win]:.3f})")
+    return winners
+
+
 def write_table(winners):
     """Write the table: the new winners replace the entries of their classes, others are kept."""
     merged = read_table()
@@ -196,6 +230,8 @@ def main() -> int:
                     help="seconds of untimed launches before timing a candidate (the engine clock ramps "
                          "up under sustained load; short kernels alone would be timed at a lower clock)")
     ap.add_argument("--table-from", default=None, help="write the table from a saved results file (no GPU)")
+    ap.add_argument("--keep-margin", type=float, default=0.01,
+                    help="keep the table's entry unless the winner's score beats it by more than this fraction")
     ap.add_argument("--regret", type=int, default=0,
                     help="instead of tuning: time every variant on this many random shapes and report how far "
                          "the dispatched variant is from the fastest")
@@ -204,8 +240,7 @@ def main() -> int:
     if args.table_from:
         with open(args.table_from) as f:
             saved = json.load(f)
-        winners = {tuple(k.split("/")): v for k, v in saved["winners"].items()}
-        write_table({(c, int(v)): tuple(w) for (c, v), w in winners.items()})
+        write_table(choose_winners(saved["results"], args.keep_margin))
         return 0
 
     import numpy as np
@@ -310,26 +345,7 @@ def main() -> int:
         A, B, C0 = make_inputs(w, M=M, N=N, K=K, dist=dist, beta=beta)
         results += sweep(label, cls, A, B, C0, alpha, beta, vec_ok, w.seed + 17)
 
-    # choose winners
-    winners = {}
-    for cls in classes:
-        for vclass in (0, 1):
-            recs = [r for r in results if r["class"] == cls and r["vec_class"] == vclass]
-            if not recs:
-                continue
-            cases = sorted({r["case"] for r in recs})
-            best = {c: min(r["ms_median"] for r in recs if r["case"] == c and r["parity"]) for c in cases}
-            score = {}
-            for name in sorted({r["variant"] for r in recs}):
-                rs = {r["case"]: r for r in recs if r["variant"] == name}
-                if set(rs) != set(cases) or not all(r["parity"] for r in rs.values()):
-                    continue
-                # a vector-load class may also be served by a scalar-load variant, never the reverse
-                score[name] = math.exp(sum(math.log(rs[c]["ms_median"] / best[c]) for c in cases) / len(cases))
-            if score:
-                win = min(score, key=score.get)
-                winners[(cls, vclass)] = (win, score[win])
-                log(f"winner {cls}/{'vec' if vclass else 'scalar'}: {win} (geo-mean slowdown {score[win]:.3f})")
+    winners = choose_winners(results, args.keep_margin)
     os.makedirs(os.path.dirname(args.out), exist_ok=True)
     with open(args.out, "w") as f:
         json.dump({"time": time.strftime("%Y-%m-%d %H:%M:%S"), "results": results,
