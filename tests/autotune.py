@@ -13,7 +13,8 @@ instance is one variant of the library, and the sweep runs over all of them.
 
 Selection: within a (shape class, vector-load class) pair, a variant must pass
 the oracle check on every representative workload; the winner minimises the
-geometric mean of (time / best time) over those workloads.  This file imports
+geometric mean of (time / best time) over those workloads, and replaces the
+table's current entry only when it beats it by more than --keep-margin (1 %).  This file imports
 the oracle, so it lives with the tests; the library never runs it.
 """
 from __future__ import annotations

@@ -1,0 +1,89 @@
+"""The autotuner's selection rule and the dispatch table it writes, checked on the CPU.
+
+The rule: per (shape class, vector-load class), among the variants that ran and passed the
+oracle check on every representative case, the one with the smallest geometric mean of
+(time / per-case best); the table's current entry stays unless that winner beats it by more than
+the keep margin.  The table must name only variants the library has, and a vector-load variant
+never serves the scalar class.
+"""
+import math
+import re
+
+import pytest
+
+import autotune
+import fp32_gemm_05_amd as sg
+
+
+def _rec(case, variant, ms, parity=True, cls="large", vec=1):
+    return {"case": case, "class": cls, "vec_class": vec, "variant": variant, "ms_median": ms,
+            "parity": parity}
+
+
+@pytest.fixture
+def incumbent(monkeypatch):
+    table = {}
+    monkeypatch.setattr(autotune, "read_table", lambda: dict(table))
+    return table
+
+
+def test_geo_mean_winner(incumbent):
+    res = [_rec("a", "x", 1.0), _rec("b", "x", 2.3),
+           _rec("a", "y", 1.1), _rec("b", "y", 2.0)]
+    # x: sqrt(1.0 * 1.15) = 1.072, y: sqrt(1.1 * 1.0) = 1.049
+    win = autotune.choose_winners(res, 0.01)
+    assert win[("large", 1)][0] == "y"
+    assert math.isclose(win[("large", 1)][1], math.sqrt(1.1))
+
+
+def test_incumbent_kept_within_margin(incumbent):
+    incumbent[("large", 1)] = ("old", 1.0)
+    res = [_rec("a", "old", 1.005), _rec("a", "new", 1.0)]
+    assert autotune.choose_winners(res, 0.01)[("large", 1)][0] == "old"
+    res = [_rec("a", "old", 1.02), _rec("a", "new", 1.0)]
+    assert autotune.choose_winners(res, 0.01)[("large", 1)][0] == "new"
+    # an incumbent that failed parity is never kept
+    res = [_rec("a", "old", 1.0, parity=False), _rec("a", "new", 1.004)]
+    assert autotune.choose_winners(res, 0.01)[("large", 1)][0] == "new"
+
+
+def test_parity_failure_or_missing_case_disqualifies(incumbent):
+    res = [_rec("a", "fast_wrong", 0.5, parity=False), _rec("b", "fast_wrong", 0.5),
+           _rec("a", "partial", 0.6),  # never ran on case b
+           _rec("a", "ok", 1.0), _rec("b", "ok", 1.0)]
+    win = autotune.choose_winners(res, 0.01)
+    assert win[("large", 1)][0] == "ok"
+    # the per-case best counts every passing run: 0.6 on case a ("partial"), 0.5 on case b
+    # ("fast_wrong" passed there)
+    assert math.isclose(win[("large", 1)][1], math.sqrt(1.0 / 0.6 * 1.0 / 0.5))
+
+
+def test_table_round_trip(tmp_path, monkeypatch):
+    path = tmp_path / "table.inc"
+    monkeypatch.setattr(autotune, "TABLE", str(path))
+    winners = {("large", 1): ("mfma32_128x128x16_w64x64_d4_vec", 1.0),
+               ("skinny", 0): ("mfma32_64x64x32_w32x32_d3_scalar", 1.0614)}
+    autotune.write_table(winners)
+    text = path.read_text()
+    assert '{kLarge, 1, "mfma32_128x128x16_w64x64_d4_vec"}' in text
+    assert "(warm, cold, dirty)" in text  # the skinny class is scored over three cache states
+    back = autotune.read_table()
+    assert back[("large", 1)][0] == "mfma32_128x128x16_w64x64_d4_vec"
+    assert back[("skinny", 0)] == ("mfma32_64x64x32_w32x32_d3_scalar", 1.061)
+
+
+def test_committed_table_names_real_variants():
+    """Every entry of the committed table names a variant of this build, of its vector-load class
+    (a scalar-load variant may serve the vector class, never the reverse) and with untransposed
+    operands; every class has both entries."""
+    text = open(autotune.TABLE).read()
+    entries = re.findall(r'\{(k\w+), (\d), "([\w]+)"\}', text)
+    names = {sg.sgemm_variant_name(v): v for v in range(sg.sgemm_num_variants())}
+    seen = set()
+    for cls, vec, name in entries:
+        assert name in names, name
+        info = sg.sgemm_variant_info(names[name])
+        assert not (info["vec"] and vec == "0"), name
+        assert info["trans_a"] == 0 and info["trans_b"] == 0, name
+        seen.add((cls, vec))
+    assert seen == {(c, v) for c in autotune.CLASS_IDS.values() for v in ("0", "1")}
