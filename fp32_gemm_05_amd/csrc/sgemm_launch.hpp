@@ -299,6 +299,9 @@ const Variant kVariants[] = {
     NTA_FAIR_VARIANT(128, 32, 32, 32, 32, true, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_vec"),
     NTA_FAIR_VARIANT(128, 32, 32, 32, 32, false, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_scalar"),
     NTA_FAIR_VARIANT(256, 32, 32, 64, 32, true, 0, MFMA_NAME(256, 32, 32, 64, 32) "_nta_vec"),
+    NTA_DEEP_VARIANT(128, 64, 32, 64, 32, true, 3, DEEP_NAME(128, 64, 32, 64, 32) "_d3_nta_vec"),
+    NTA_DEEP_VARIANT(128, 32, 32, 32, 32, true, 3, DEEP_NAME(128, 32, 32, 32, 32) "_d3_nta_vec"),
+    NTA_DEEP_VARIANT(128, 32, 32, 32, 32, false, 3, DEEP_NAME(128, 32, 32, 32, 32) "_d3_nta_scalar"),
     // C for the beta term read at the start of the tile ("_cp"): one-round grids
     CP_DEEP_VARIANT(64, 64, 32, 32, 32, true, 0, DEEP_NAME(64, 64, 32, 32, 32) "_cp_vec"),
     CP_DEEP_VARIANT(64, 64, 32, 32, 32, false, 0, DEEP_NAME(64, 64, 32, 32, 32) "_cp_scalar"),
