@@ -33,6 +33,7 @@ class Workload:
     beta: float
     dist: str          # "uniform" | "normal" | "int"
     seed: int
+    roofline: str = "compute"  # the roof the workload is reported against: "compute" or "hbm"
 
     def as_int(self) -> "Workload":
         """The integer-valued variant of this workload (same shape and scalars)."""
@@ -50,7 +51,8 @@ WORKLOADS = {
     "square4096": Workload("square4096", 4096, 4096, 4096, 1.0, 0.0, "uniform", 1004),
     "ragged3001x5003x777": Workload("ragged3001x5003x777", 3001, 5003, 777, 0.5, -1.5, "normal", 1005),
     "square8192": Workload("square8192", 8192, 8192, 8192, 1.0, 0.0, "uniform", 1006),
-    "skinny65536x64x1024": Workload("skinny65536x64x1024", 65536, 64, 1024, 1.0, 0.0, "uniform", 1007),
+    # tall-skinny: one pass over a 256 MiB A, reported against the HBM roofline
+    "skinny65536x64x1024": Workload("skinny65536x64x1024", 65536, 64, 1024, 1.0, 0.0, "uniform", 1007, "hbm"),
 }
 
 # The headline workload that the bench times.
