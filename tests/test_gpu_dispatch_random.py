@@ -1,0 +1,112 @@
+"""Default dispatch on seeded random shapes drawn region by region over the shape classes
+(narrow, skinny, tiny, small with short, medium and long K, shallow / medium / large grids and
+tiny K), with random scalars, alignment, pointer offsets and transpositions, checked against
+the float64 oracle on sampled outputs: integer-valued inputs exactly, random floats within
+1e-5*(|alpha|*sum|a*b| + |beta*c|) + 1e-6.  Every call also checks that nothing outside C's
+M x N window was written.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from fp32_gemm_05_amd.workloads import sample_points
+from tests.gemm_cases import SENTINEL, check_exact, check_within_bound, device_matrix
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import fp32_gemm_05_amd as sg  # noqa: E402
+
+# (region, M range, N range, K range): each drawn log-uniformly
+REGIONS = [
+    ("narrow", (8200, 40000), (1, 32), (64, 1500)),
+    ("skinny", (8200, 40000), (33, 64), (64, 1500)),
+    ("tiny", (40, 700), (40, 700), (512, 3000)),
+    ("small_shortk", (100, 1500), (100, 1500), (8, 511)),
+    ("small", (600, 1900), (600, 1900), (512, 4000)),
+    ("grid", (2000, 5000), (2000, 5000), (128, 2500)),
+    ("tiny_k", (2000, 4000), (2000, 4000), (1, 127)),
+]
+PER_REGION = 10
+
+
+def _loguniform(rng, lo, hi):
+    return int(round(np.exp(rng.uniform(np.log(lo), np.log(hi)))))
+
+
+def _cases():
+    rng = np.random.default_rng(20260)
+    out = []
+    for region, mr, nr, kr in REGIONS:
+        for i in range(PER_REGION):
+            M, N, K = _loguniform(rng, *mr), _loguniform(rng, *nr), _loguniform(rng, *kr)
+            aligned = bool(rng.integers(0, 2))
+            if aligned:  # 128-bit eligible: row lengths and strides multiples of 4
+                N, K = max(4, N - N % 4), max(4, K - K % 4)
+                if region == "narrow":
+                    N = min(N, 32)
+            ta, tb = ("T" if rng.random() < 0.25 else "N"), ("T" if rng.random() < 0.25 else "N")
+            alpha = float(rng.choice([1.0, 0.5, -2.0]))
+            beta = float(rng.choice([0.0, 0.5, -1.5]))
+            dist = "int" if rng.random() < 0.5 else "uniform"
+            out.append((f"{region}{i}_{ta}{tb}_{M}x{N}x{K}", M, N, K, ta, tb, alpha, beta, dist, aligned,
+                        int(rng.integers(0, 1 << 30))))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("label,M,N,K,ta,tb,alpha,beta,dist,aligned,seed", CASES, ids=[c[0] for c in CASES])
+def test_dispatch_random_shape(label, M, N, K, ta, tb, alpha, beta, dist, aligned, seed):
+    rng = np.random.default_rng(seed)
+    if dist == "int":
+        A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+        B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+        C = rng.integers(-2, 3, (M, N)).astype(np.float32)
+    else:
+        A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+        C = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    As = np.ascontiguousarray(A.T) if ta == "T" else A
+    Bs = np.ascontiguousarray(B.T) if tb == "T" else B
+    # aligned: 16-byte aligned starts and strides; otherwise odd pads and one-float offsets
+    pads = (0, 0, 0) if aligned else tuple(int(x) for x in rng.choice([1, 3, 5], 3))
+    offs = (0, 0, 0) if aligned else tuple(int(x) for x in rng.choice([0, 1], 3))
+    bufA, vA, lda = device_matrix(As, pad_cols=pads[0], offset=offs[0])
+    bufB, vB, ldb = device_matrix(Bs, pad_cols=pads[1], offset=offs[1])
+    bufC, vC, ldc = device_matrix(C, pad_cols=pads[2], pad_rows=2, offset=offs[2], fill=SENTINEL)
+    vid = sg.sgemm_op_select_variant(ta, tb, M, N, K, vA.data_ptr(), lda, vB.data_ptr(), ldb,
+                                     vC.data_ptr(), ldc)
+    print(f"[dispatch] {label} alpha={alpha} beta={beta} {dist} aligned={aligned} "
+          f"variant={sg.sgemm_variant_name(vid)}", flush=True)
+    sys.stdout.flush()
+    sg.sgemm_op(ta, tb, M, N, K, alpha, vA.data_ptr(), lda, vB.data_ptr(), ldb, beta, vC.data_ptr(), ldc)
+    torch.cuda.synchronize()
+
+    I, J = sample_points(M, N, n_random=1024, seed=seed % 100000, tile=32)
+    got = vC[torch.from_numpy(I).cuda(), torch.from_numpy(J).cuda()].cpu().numpy()
+    ref, bound = oracle.ref_points(A, B, C, I, J, alpha, beta)
+    if dist == "int":
+        check_exact(got, ref, label)
+    else:
+        check_within_bound(got, ref, bound, label)
+    host = bufC.cpu().numpy()
+    mask = np.ones(host.shape[0], dtype=bool)
+    for r in range(M):
+        mask[offs[2] + r * ldc: offs[2] + r * ldc + N] = False
+    assert np.all(host[mask] == SENTINEL), f"{label}: write outside C's M x N window"
+    del bufA, bufB, bufC, vA, vB, vC
