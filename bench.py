@@ -7,7 +7,7 @@ A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
                     [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline] [--cpu-full]
-                    [--cpu-threads N] [--cold | --cold-dirty] [--shard-rows G]
+                    [--cpu-threads N] [--cold | --cold-dirty] [--shard-rows G] [--no-sclk]
 
 ``--op`` other than NN stores A as K x M and/or B as N x K and times
 ``sgemm_op`` (op(A) * op(B)) on the same logical product.
@@ -59,6 +59,74 @@ def stored_traffic(workload: str, variant: str):
     if rec.get("kernel_source_hash") != kernel_source_hash(variant):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def host_cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def sample_sclk(step, record_event, step_ms: float, n_samples: int = 3, settle_s: float = 1.5,
+                spacing_s: float = 1.0, cap_s: float = 15.0):
+    """The engine clock under this workload's sustained load: amd-smi's per-XCD gfx clocks, read
+    n_samples times, spacing_s apart, after settle_s of back-to-back launches (the reading is a
+    snapshot the driver refreshes about once a second, so it needs seconds of steady load).  The
+    launch loop keeps about two 20 ms batches queued.  Returns (median over samples of the mean
+    over XCDs in MHz, samples), or None when amd-smi is missing or reports no gfx clocks."""
+    import shutil
+    import subprocess
+    import threading
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    vals, done = [], threading.Event()
+
+    def poll():
+        try:
+            time.sleep(settle_s)
+            for i in range(n_samples):
+                if i:
+                    time.sleep(spacing_s)
+                r = subprocess.run([exe, "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=8)
+                d = json.loads(r.stdout)
+                gpu = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                xs = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                      if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                      and isinstance(v["clk"].get("value"), (int, float))]
+                if xs:
+                    vals.append(sum(xs) / len(xs))
+        except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+            pass
+        finally:
+            done.set()
+
+    batch = max(1, int(20.0 / max(step_ms, 1e-3)))
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    prev = None
+    t0 = time.perf_counter()
+    while not done.is_set() and time.perf_counter() - t0 < cap_s:
+        for _ in range(batch):
+            step()
+        ev = record_event()
+        if prev is not None:
+            prev.synchronize()
+        prev = ev
+    if prev is not None:
+        prev.synchronize()
+    th.join(timeout=1.0)
+    if not vals:
+        return None
+    vals.sort()
+    return vals[len(vals) // 2], len(vals)
 
 
 def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0, full: bool = False, threads: int = 0):
@@ -142,6 +210,8 @@ def cpu_blocked_baseline(A, B, C0, w, reps: int = 3):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip reading the engine clock with amd-smi under about 4 s of sustained load")
     ap.add_argument("--steps", type=int, default=200)
     # the engine clock ramps up over the first tens of milliseconds of sustained MFMA work
     ap.add_argument("--warmup", type=int, default=100)
@@ -271,6 +341,12 @@ def main() -> int:
         torch.cuda.synchronize()
         per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
     ms_per_step = total_ms / args.steps
+    def record_event():
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        return ev
+
+    sclk = None if args.no_sclk else sample_sclk(step, record_event, ms_per_step)
     flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     # cold: the mean of the individually timed launches (the flushes between them are excluded);
@@ -327,6 +403,12 @@ def main() -> int:
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pct_hbm_peak_alg": round(100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,
+        # amd-smi's gfx clock (mean over XCDs) while this step ran back to back, and the share of
+        # the FP32 MFMA peak at that clock (the 157.3 figure assumes 2.4 GHz)
+        "sclk_mhz": round(sclk[0], 1) if sclk else None,
+        "pct_fp32_peak_at_sclk": round(100.0 * achieved / (FP32_PEAK_TFLOPS * sclk[0] / 2400.0), 2)
+        if sclk else None,
+        "host_cpu": host_cpu_model(),
     }
     if roofline is not compute_roof:
         line["roofline_compute"] = compute_roof

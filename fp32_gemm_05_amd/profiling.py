@@ -18,8 +18,8 @@
         `report`: the one command behind each committed summary.
     python -m fp32_gemm_05_amd.profiling report --dir D --workload W --out-dir profiles
         one summary per (kernel, workload) from the runs the profiling commands below leave in D:
-          D/trace_W   rocprofv3 --kernel-trace --stats ... -- python bench.py --workload W --no-cpu-baseline
-          D/fetch_W   rocprofv3 --pmc FETCH_SIZE ...        -- python bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline
+          D/trace_W   rocprofv3 --kernel-trace --stats ... -- python bench.py --workload W --no-cpu-baseline --no-sclk
+          D/fetch_W   rocprofv3 --pmc FETCH_SIZE ...        -- python bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --no-sclk
           D/write_W   rocprofv3 --pmc WRITE_SIZE ...        (same bench command)
           D/rdreq_W   rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum ...
           D/sq_W      rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT
@@ -263,11 +263,13 @@ def cmd_report(args) -> None:
     k = kern[0]
     name = k["Name"]
     avg_ns = float(k["AverageNs"])
-    # the bench's timed region is its last `steps` launches (after the first call and the warmup)
+    # the bench's launches: the first call, the warmup, the timed region (`steps` back-to-back
+    # launches) and a pass of min(steps, 50) individually timed launches
     with open(os.path.join(d, f"trace_{W}", "run_kernel_trace.csv")) as f:
         disp = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in csv.DictReader(f)
                 if r["Kernel_Name"] == name]
-    timed = disp[-args.steps:]
+    spread = min(args.steps, 50)
+    timed = disp[-(args.steps + spread):-spread]
     timed_ns = _mean(timed)
     # variant name from the kernel signature is not unique; take it from the bench log
     variant = args.variant
@@ -305,11 +307,11 @@ def cmd_report(args) -> None:
         f"{'--warmup ' + args.trace_args.split()[-1] + ' ' if args.trace_args.startswith('--warmup') else ''}"
         f"(runs all of the following)",
         f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} "
-        f"{args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline",
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
-        f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline",
-        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup {sq_warm} --no-cpu-baseline",
+        f"{args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup {sq_warm} --no-cpu-baseline --no-sclk",
         "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE, then the three TCC_EA0_RDREQ_*_sum) --output-format csv -d <dir>/copy_fetch (copy_write, copy_rdreq) -o run -- python -u -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3",
         f"python -m fp32_gemm_05_amd.profiling report --dir <dir> --workload {W} --variant {variant} "
         f"{trace_opt}--out-dir profiles",
@@ -320,9 +322,9 @@ def cmd_report(args) -> None:
         f"Kernel: `{name}`", "",
         "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
         f"| Dispatches | Mean duration | TFLOP/s | % of {FP32_PEAK_TFLOPS} |", "|---|---|---|---|",
-        f"| all {k['Calls']} (first call + warmup + timed; the --stats average) | {avg_ns / 1e3:.1f} us | "
+        f"| all {k['Calls']} (first call, warmup, timed region, 50 single launches; the --stats average) | {avg_ns / 1e3:.1f} us | "
         f"{tflops:.1f} | {100 * tflops / FP32_PEAK_TFLOPS:.1f} % |",
-        f"| the last {len(timed)} (the bench's timed region) | {timed_ns / 1e3:.1f} us | {tflops_timed:.1f} | "
+        f"| the {len(timed)} of the bench's timed region | {timed_ns / 1e3:.1f} us | {tflops_timed:.1f} | "
         f"{100 * tflops_timed / FP32_PEAK_TFLOPS:.1f} % |", "",
         f"Min {float(k['MinNs']) / 1e3:.1f} us, max {float(k['MaxNs']) / 1e3:.1f} us over all dispatches.", "",
         "## Counters (means per dispatch)", "",
@@ -413,7 +415,7 @@ def cmd_collect(args) -> None:
                  os.path.join(d, tag + ".log"), 120)
     bench = [py, "-u", os.path.join(ROOT, "bench.py"), "--workload", W]
     _run(rp + ["--kernel-trace", "--stats", "-d", os.path.join(d, f"trace_{W}"), "-o", "run", "--", *bench,
-               "--warmup", str(args.warmup), "--no-cpu-baseline"], os.path.join(d, f"trace_{W}.log"), 300)
+               "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-sclk"], os.path.join(d, f"trace_{W}.log"), 300)
     variant = None
     with open(os.path.join(d, f"trace_{W}.log")) as f:
         for line in f:
@@ -423,7 +425,7 @@ def cmd_collect(args) -> None:
         raise SystemExit("the bench did not report its variant")
     for tag, counters in PMC_PASSES:
         _run(rp + ["--pmc", *counters, "-d", os.path.join(d, f"{tag}_{W}"), "-o", "run", "--", *bench,
-                   "--steps", "3", "--warmup", "1", "--no-cpu-baseline"], os.path.join(d, f"{tag}_{W}.log"), 120)
+                   "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-sclk"], os.path.join(d, f"{tag}_{W}.log"), 120)
     report = argparse.Namespace(dir=d, workload=W, variant=variant, steps=200, sq_warmup=1,
                                 trace_args=f"--warmup {args.warmup}", out_dir=args.out_dir, note="")
     cmd_report(report)
