@@ -52,6 +52,8 @@ def test_bench_line_headline_fields():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["unit"] == "TFLOP/s"
     assert d["parity"]["pass"] is True
+    # the engine clock read with amd-smi under sustained load (None where amd-smi is missing)
+    assert "sclk_mhz" in d and (d["sclk_mhz"] is None or 100.0 <= d["sclk_mhz"] <= 2500.0)
 
 
 @pytest.mark.gpu
