@@ -353,13 +353,15 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
                 if (col >= N) continue;
                 float* pl = C + (long)lrow * ldc + col;
                 f32x16 c;
-                if (PRE) {
-                    c = cv[i][j];
-                } else if (beta != 0.f) {
+                if (beta != 0.f) {
+                    if (PRE) {
+                        c = cv[i][j];
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int dr = (r >> 2) * 8 + (r & 3);
-                        if (lrow + dr < M) c[r] = pl[dr * ldc];
+                        for (int r = 0; r < 16; ++r) {
+                            const int dr = (r >> 2) * 8 + (r & 3);
+                            if (lrow + dr < M) c[r] = pl[dr * ldc];
+                        }
                     }
                 }
 #pragma unroll
