@@ -62,7 +62,9 @@ CASES = [
     ("shard512x4096x4096", "medium", "square4096", 512, 4096, 4096, None, None, None, True),
     ("longk1089x728x5752", "small_longk", "square4096", 1089, 728, 5752, None, None, None, True),
     ("longk1751x907x5323", "medium", "ragged3001x5003x777", 1751, 907, 5323, None, None, None, False),
-    ("longk777x1501x3001", "small_longk", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
+    ("longk777x1501x3001", "small_full", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
+    ("longk1199x587x3229", "small_longk", "ragged3001x5003x777", 1199, 587, 3229, None, None, None, False),
+    ("longk1003x777x2503", "small_longk", "ragged3001x5003x777", 1003, 777, 2503, None, None, None, False),
     ("square256", "small_shortk", "square256", None, None, None, None, None, None, True),
     ("shortk822x124x88", "small_shortk", "square256", 822, 124, 88, None, None, None, True),
     ("shortk2664x180x284", "small_shortk", "square256", 2664, 180, 284, None, None, None, True),
