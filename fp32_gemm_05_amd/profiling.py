@@ -356,7 +356,7 @@ def cmd_report(args) -> None:
         f"* L2 read requests by size: {rd_bytes / 1e6:.1f} MB read (32/64/128 B requests counted at their size)",
         (f"* Panel reads of the {tile[0]}x{tile[1]} tiling, K*(1/BM + 1/BN) values per output: {panel / 1e6:.1f} MB "
          f"per launch; the L2 serves all but the L2->fabric traffic above" if tile else
-         "* Panel reads: variant not found in this build"),
+         "* Panel reads: variant not found in the library"),
         "", "## Commands", "", "```", *cmds, "```", "",
     ]
     if args.note:

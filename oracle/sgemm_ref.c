@@ -20,7 +20,7 @@
  *   - "1D Register Tiling: One Thread, TM Outputs" (maxxfuu), section "The
  *     Kernel": the epilogue alpha * acc + beta * C.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - Accumulation is in float64, not in the pages' float: every product of two
  *     fp32 values is exact in double (24 + 24 <= 53 significand bits), and the
  *     k-order is ascending and fixed, so the result does not depend on the

@@ -24,6 +24,7 @@ import json
 import math
 import os
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -222,7 +223,7 @@ def regret_mode(args, sg, sweep) -> int:
 
 def main() -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "autotune.json"))
+    ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "libsgemm_autotune.json"))
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
                     default="large,huge,long_k,shallow,medium,tiny_k,small,small_full,tiny,small_shortk,small_longk,"

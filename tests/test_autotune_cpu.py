@@ -73,7 +73,7 @@ def test_table_round_trip(tmp_path, monkeypatch):
 
 
 def test_committed_table_names_real_variants():
-    """Every entry of the committed table names a variant of this build, of its vector-load class
+    """Every entry of the committed table names a variant of the library, of its vector-load class
     (a scalar-load variant may serve the vector class, never the reverse) and with untransposed
     operands; every class has both entries."""
     text = open(autotune.TABLE).read()
