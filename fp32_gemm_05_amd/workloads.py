@@ -53,6 +53,8 @@ WORKLOADS = {
     "square8192": Workload("square8192", 8192, 8192, 8192, 1.0, 0.0, "uniform", 1006),
     # tall-skinny: one pass over a 256 MiB A, reported against the HBM roofline
     "skinny65536x64x1024": Workload("skinny65536x64x1024", 65536, 64, 1024, 1.0, 0.0, "uniform", 1007, "hbm"),
+    # narrower still (N <= 32): a 512 MiB A streamed once; the 32-wide-tile class
+    "narrow262144x32x512": Workload("narrow262144x32x512", 262144, 32, 512, 1.0, 0.0, "uniform", 1008, "hbm"),
 }
 
 # The headline workload that the bench times.
