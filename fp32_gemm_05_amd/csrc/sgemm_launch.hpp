@@ -184,6 +184,11 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT, VEC,          \
      MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::LDS_BYTES,                                         \
      &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, WIDE, TA, TB, FAIR>, WIDE, 0, TA, TB}
+// streamed A with B transposed (op(B) = B^T): the skinny and narrow workgroups, nontemporal A loads
+#define NT_STREAM_VARIANT(BM, BN, BK, WM, WN, VEC, FAIR, NAME)                                    \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC, false, true>::NT, VEC,       \
+     MfmaCfg<BM, BN, BK, WM, WN, VEC, false, true>::LDS_BYTES,                                      \
+     &launch_mfma<BM, BN, BK, WM, WN, VEC, 0, false, false, true, FAIR, true>, 0, 0, false, true}
 #define DIRECT_TRANS(D, BK, VEC, TA, TB, NAME) \
     {NAME, kMfma, 32, 32, BK, 32, 32, 64, VEC, 0, &launch_mfma_direct<VEC, D, TA, TB>, 0, 0, TA, TB}
 // the variants of one transposition (TAG: "nt", "tn" or "tt"; first letter op(A), second op(B));
@@ -313,5 +318,9 @@ const Variant kVariants[] = {
      &launch_mfma_direct<false, 6, false, false, true>, 0},
     {"mfma32r_32x32x96_w32x32_g6_cp_vec", kMfma, 32, 32, 96, 32, 32, 64, 1, 0,
      &launch_mfma_direct<true, 6, false, false, true>, 0},
+    NT_STREAM_VARIANT(128, 64, 32, 64, 32, true, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_nt_vec"),
+    NT_STREAM_VARIANT(128, 64, 32, 64, 32, false, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_nt_scalar"),
+    NT_STREAM_VARIANT(128, 32, 32, 32, 32, true, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_nt_vec"),
+    NT_STREAM_VARIANT(128, 32, 32, 32, 32, false, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_nt_scalar"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

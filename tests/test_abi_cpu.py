@@ -160,6 +160,8 @@ def test_dispatch_families(M, N, K, ld_odd, family):
     ("T", "N", 1001, 1003, 777, True, True),   # small: only with A transposed
     ("N", "T", 1001, 1003, 777, True, False),
     ("T", "T", 4096, 4096, 4096, False, False),
+    ("N", "T", 262144, 32, 512, False, False),    # narrow stream, B transposed
+    ("N", "T", 65536, 64, 1024, True, False),     # skinny stream, B transposed, unaligned
 ])
 def test_op_dispatch_families(ta, tb, M, N, K, odd, direct):
     lda = M if ta == "T" else K
@@ -171,6 +173,8 @@ def test_op_dispatch_families(ta, tb, M, N, K, odd, direct):
     info = sg.sgemm_variant_info(v)
     assert (info["trans_a"], info["trans_b"]) == (int(ta == "T"), int(tb == "T"))
     assert _name(v).startswith("mfma32r_") == direct, _name(v)
+    if ta == "N" and tb == "T" and N <= 64 and M >= 65536:
+        assert "_nta_nt_" in _name(v) and info["BN"] == (32 if N <= 32 else 64), _name(v)
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n,group_m", [

@@ -259,12 +259,17 @@ def test_trans_huge_leading_dimension_wide_variant():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("ta,tb", COMBOS[:3], ids=["".join(c) for c in COMBOS[:3]])
+FULL_TRANS = [("square4096", "N", "T"), ("square4096", "T", "N"), ("square4096", "T", "T"),
+              ("skinny65536x64x1024", "N", "T"), ("narrow262144x32x512", "N", "T")]
+
+
+@pytest.mark.parametrize("wname,ta,tb", FULL_TRANS, ids=[f"{w}_{a}{b}" for w, a, b in FULL_TRANS])
 @pytest.mark.parametrize("kind", ["float", "int"])
-def test_trans_full_size_sampled(ta, tb, kind):
-    """4096^3 in each transposition, default dispatch, sampled outputs (random points plus tile
-    boundary rows/columns) computed one by one by the oracle."""
-    w = WORKLOADS["square4096"] if kind == "float" else WORKLOADS["square4096"].as_int()
+def test_trans_full_size_sampled(wname, ta, tb, kind):
+    """4096^3 in each transposition and the skinny and narrow streams with B transposed, default
+    dispatch, sampled outputs (random points plus tile boundary rows/columns) computed one by one
+    by the oracle."""
+    w = WORKLOADS[wname] if kind == "float" else WORKLOADS[wname].as_int()
     _say(f"[trans-full] {ta}{tb} {w.describe()}")
     A, B, C = make_inputs(w)
     As, Bs = stored(A, B, ta, tb)
