@@ -149,6 +149,8 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
                            dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0, stream);
 }
 
+// ---- The variant table: the macros that spell out its rows, then the rows.  A row's name
+// encodes its template configuration (tile, wave tile, loads, schedule, flags). ----
 #define MFMA_VARIANT(BM, BN, BK, WM, WN, OCC, VEC, NAME)                                       \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma<BM, BN, BK, WM, WN, VEC, OCC, false>, 0}

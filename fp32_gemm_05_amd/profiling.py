@@ -50,12 +50,16 @@ KERNEL_SOURCES = ("sgemm_kernels.hpp", "sgemm_launch.hpp")
 
 
 def _strip_variant_table(text: bytes) -> bytes:
-    """The launch source without the body of its variant table: appending or editing other
-    variants' rows leaves every kernel's own code, and so its counters, unchanged."""
-    start = text.find(b"const Variant kVariants[] = {")
+    """The launch source without its variant table (the row macros and the rows, from the table's
+    header comment to the end of the array): adding or editing other variants' rows leaves every
+    kernel's own code, and so its counters, unchanged; a row's name spells out its configuration
+    and is hashed separately."""
+    start = text.find(b"// ---- The variant table:")
+    if start < 0:
+        start = text.find(b"const Variant kVariants[] = {")
     if start < 0:
         return text
-    end = text.find(b"\n};", start)
+    end = text.find(b"\n};", text.find(b"const Variant kVariants[] = {", start))
     return text[:start] + text[end:] if end >= 0 else text
 
 
