@@ -706,7 +706,7 @@ sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 // before reaching that barrier (the barrier waits for outstanding LDS accesses).
 // ---------------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false,
-          bool CPRE = false>
+          bool CPRE = false, bool ACC2 = false>
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -753,14 +753,27 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) f.b[j][t] = sb[b_off + (kk * 8 + t) * BP + j * 32];
     };
+    // ACC2: odd k-steps accumulate into a second set of registers, so that consecutive MFMAs of a
+    // wave that owns a single block do not depend on each other; the two sums are added at the end
+    f32x16 acc2[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.f;
     auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
+                for (int j = 0; j < FN; ++j) {
+                    if (ACC2 && (t & 1))
+                        acc2[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc2[i][j]);
+                    else
+                        acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
+                }
     };
 
     const int nslab = (K + BK - 1) / BK;
@@ -841,6 +854,12 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         ++s;
     }
 
+    if (ACC2) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] += acc2[i][j];
+    }
     mfma_epilogue<FM, FN, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
 }
 

@@ -85,10 +85,10 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false,
-          bool CPRE = false>
+          bool CPRE = false, bool ACC2 = false>
 hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR, NTA, CPRE>;
+    auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR, NTA, CPRE, ACC2>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -320,6 +320,11 @@ const Variant kVariants[] = {
      &launch_mfma_direct<false, 6, false, false, true>, 0},
     {"mfma32r_32x32x96_w32x32_g6_cp_vec", kMfma, 32, 32, 96, 32, 32, 64, 1, 0,
      &launch_mfma_direct<true, 6, false, false, true>, 0},
+    // two accumulator sets per block ("_a2"): independent consecutive MFMAs at one wave per SIMD
+    {DEEP_NAME(64, 64, 32, 32, 32) "_cp_a2_vec", kMfma, 64, 64, 32, 32, 32, MfmaCfg<64, 64, 32, 32, 32, true>::NT, 1,
+     MfmaCfg<64, 64, 32, 32, 32, true>::LDS_BYTES, &launch_mfma_deep<64, 64, 32, 32, 32, true, 0, 0, false, true, true>, 0},
+    {DEEP_NAME(64, 64, 32, 32, 32) "_d3_a2_scalar", kMfma, 64, 64, 32, 32, 32, MfmaCfg<64, 64, 32, 32, 32, false>::NT, 0,
+     MfmaCfg<64, 64, 32, 32, 32, false>::LDS_BYTES, &launch_mfma_deep<64, 64, 32, 32, 32, false, 0, 3, false, false, true>, 0},
     NT_STREAM_VARIANT(128, 64, 32, 64, 32, true, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_nt_vec"),
     NT_STREAM_VARIANT(128, 64, 32, 64, 32, false, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_nt_scalar"),
     NT_STREAM_VARIANT(128, 32, 32, 32, 32, true, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_nt_vec"),
