@@ -214,12 +214,30 @@ def _check_matrix(t, name):
     return t.stride(0) if t.shape[0] > 1 else max(1, t.shape[1])
 
 
+def _column_major(t) -> bool:
+    """A 2-D view with unit row stride (e.g. ``x.t()`` of a row-major x): its transpose is row-major."""
+    return t.dim() == 2 and t.shape[0] > 1 and t.shape[1] > 1 and t.stride(0) == 1 and t.stride(1) >= t.shape[0]
+
+
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = -1, stream=None,
          trans_a: bool = False, trans_b: bool = False):
     """Tensor form: C := alpha*op(A)@op(B) + beta*C in place for 2-D float32 device tensors; returns C.
 
     A and B are the stored row-major arrays; ``trans_a`` reads A (K x M) as A^T, ``trans_b`` reads
-    B (N x K) as B^T."""
+    B (N x K) as B^T.  Column-major views (unit row stride, such as ``x.t()``) are accepted without
+    a copy: an operand view is passed as its row-major storage with the transposition flipped, and
+    a column-major C is computed as C^T := alpha*op(B)^T@op(A)^T + beta*C^T on its storage (with
+    ``variant`` < 0 only, since the roles of A and B swap)."""
+    if _column_major(C):
+        if variant >= 0:
+            raise ValueError("a forced variant needs a row-major C")
+        # C^T = op(B)^T op(A)^T: B takes A's place with the opposite flag, and A takes B's
+        gemm(B, A, C.t(), alpha, beta, -1, stream, trans_a=not trans_b, trans_b=not trans_a)
+        return C
+    if _column_major(A):
+        A, trans_a = A.t(), not trans_a
+    if _column_major(B):
+        B, trans_b = B.t(), not trans_b
     lda = _check_matrix(A, "A")
     ldb = _check_matrix(B, "B")
     ldc = _check_matrix(C, "C")
