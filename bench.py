@@ -5,9 +5,17 @@ One step = one call of the library's ``sgemm`` on the whole workload (inputs
 resident in HBM before the timed region).  Default workload: M = N = K = 4096,
 A, B ~ U[-1, 1), alpha = 1, beta = 0.  Prints ONE JSON line on stdout.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload square4096]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--preroll 1.0] [--workload square4096]
                     [--variant ID] [--op NN|NT|TN|TT] [--no-cpu-baseline] [--cpu-full]
-                    [--cpu-threads N] [--cold | --cold-dirty] [--shard-rows G] [--no-sclk]
+                    [--cpu-threads N] [--cold | --cold-dirty] [--shard-rows G] [--smi]
+
+Order of the GPU work: one call whose output is checked against the oracle; the pre-roll
+(``--preroll`` seconds of back-to-back steps, reported in the line as ``preroll``: the engine
+clock ramps up over the first tens of milliseconds of sustained load, and a run measured from a
+cold start times that ramp rather than the kernel); the warmup steps; an engine-clock probe; the
+timed region; a second probe (``sclk_mhz``: the clock right before and right after the timed
+region, read on the GPU on the same stream); single launches for the spread; and the launch
+floor (``launch_floor``: an empty kernel with the dispatched variant's grid, timed the same way).
 
 ``--op`` other than NN stores A as K x M and/or B as N x K and times
 ``sgemm_op`` (op(A) * op(B)) on the same logical product.
@@ -72,21 +80,19 @@ def host_cpu_model() -> str | None:
     return None
 
 
-def sample_sclk(step, record_event, step_ms: float, n_samples: int = 3, settle_s: float = 1.5,
-                spacing_s: float = 1.0, cap_s: float = 15.0):
-    """The engine clock under this workload's sustained load: amd-smi's per-XCD gfx clocks, read
-    n_samples times, spacing_s apart, after settle_s of back-to-back launches (the reading is a
-    snapshot the driver refreshes about once a second, so it needs seconds of steady load).  The
-    launch loop keeps about two 20 ms batches queued.  Returns (median over samples of the mean
-    over XCDs in MHz, samples), or None when amd-smi is missing or reports no gfx clocks."""
+def preroll(step, record_event, step_ms: float, seconds: float, smi: bool = False, settle_s: float = 1.5,
+            n_samples: int = 3, spacing_s: float = 1.0):
+    """Back-to-back steps for at least `seconds` (about two 20 ms batches kept queued), so that the
+    timed region starts at the engine clock this workload sustains.  With smi, amd-smi's per-XCD
+    gfx clocks are also read n_samples times, spacing_s apart, after settle_s of load (the reading
+    is a snapshot the driver refreshes about once a second), and the pre-roll lasts as long as that
+    takes.  Returns (steps launched, seconds, median over samples of the XCD mean in MHz or None)."""
     import shutil
     import subprocess
     import threading
 
-    exe = shutil.which("amd-smi")
-    if exe is None:
-        return None
     vals, done = [], threading.Event()
+    exe = shutil.which("amd-smi") if smi else None
 
     def poll():
         try:
@@ -108,25 +114,34 @@ def sample_sclk(step, record_event, step_ms: float, n_samples: int = 3, settle_s
         finally:
             done.set()
 
+    if seconds <= 0 and exe is None:
+        return 0, 0.0, None
     batch = max(1, int(20.0 / max(step_ms, 1e-3)))
-    th = threading.Thread(target=poll, daemon=True)
-    th.start()
+    th = None
+    if exe is not None:
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
     prev = None
+    n = 0
     t0 = time.perf_counter()
-    while not done.is_set() and time.perf_counter() - t0 < cap_s:
+    cap = max(seconds, 15.0 if exe is not None else 0.0)
+    while time.perf_counter() - t0 < cap:
+        if time.perf_counter() - t0 >= seconds and (th is None or done.is_set()):
+            break
         for _ in range(batch):
             step()
+        n += batch
         ev = record_event()
         if prev is not None:
             prev.synchronize()
         prev = ev
     if prev is not None:
         prev.synchronize()
-    th.join(timeout=1.0)
-    if not vals:
-        return None
+    dt = time.perf_counter() - t0
+    if th is not None:
+        th.join(timeout=1.0)
     vals.sort()
-    return vals[len(vals) // 2], len(vals)
+    return n, dt, (vals[len(vals) // 2] if vals else None)
 
 
 def cpu_baseline(A, B, C0, w, out_gpu, target_s: float = 15.0, full: bool = False, threads: int = 0):
@@ -210,11 +225,14 @@ def cpu_blocked_baseline(A, B, C0, w, reps: int = 3):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--no-sclk", action="store_true",
-                    help="skip reading the engine clock with amd-smi under about 4 s of sustained load")
+    ap.add_argument("--smi", action="store_true",
+                    help="also read amd-smi's gfx clocks during the pre-roll (which then lasts about 4 s)")
+    ap.add_argument("--no-sclk", action="store_true", help="no amd-smi reading (the default; kept for old commands)")
     ap.add_argument("--steps", type=int, default=200)
-    # the engine clock ramps up over the first tens of milliseconds of sustained MFMA work
     ap.add_argument("--warmup", type=int, default=100)
+    # the engine clock ramps up over the first tens of milliseconds of sustained MFMA work
+    ap.add_argument("--preroll", type=float, default=1.0, metavar="SECONDS",
+                    help="seconds of back-to-back steps before the warmup (reported in the line; 0: none)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant id (default: dispatch)")
     ap.add_argument("--op", default="NN", choices=["NN", "NT", "TN", "TT"],
@@ -286,13 +304,37 @@ def main() -> int:
             sg.sgemm_op_ex(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, w.beta,
                            dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
 
+    from fp32_gemm_05_amd.profiling import SclkProbe, launch_floor_ms
+
+    def record_event():
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        return ev
+
+    # everything the measurement needs is set up before the pre-roll: a pause of tens of
+    # milliseconds between the pre-roll and the timed region (loading a library, allocating) lets
+    # the engine clock drop again, and the timed region would then re-time its ramp
+    probe_before, probe_after = SclkProbe(), SclkProbe()
+    floor_grid = -(-w.M // info["BM"]) * -(-w.N // info["BN"])
+    launch_floor_ms(floor_grid, info["threads"], info["lds_bytes"], 1, stream, warmup=1)
+
     # first call: its output is the one checked against the oracle
     step()
     torch.cuda.synchronize()
     out_first = dC.cpu().numpy()
 
+    # a rough step time for the pre-roll's batching
+    t0 = time.perf_counter()
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    rough_ms = (time.perf_counter() - t0) * 1e3 / 3
+    pre_steps, pre_s, smi_mhz = preroll(step, record_event, rough_ms, args.preroll, smi=args.smi and not args.no_sclk)
+    # straight on into the warmup (the pre-roll returns as soon as its queue has drained)
     for _ in range(args.warmup):
         step()
+    log(f"pre-roll: {pre_steps} steps in {pre_s:.2f} s")
+    n_spread = 0
     cold = args.cold or args.cold_dirty
     if cold:
         # 512 MiB > the 256 MB Infinity Cache and every L2: the flush before each launch evicts the
@@ -303,6 +345,7 @@ def main() -> int:
         ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
+        probe_before.launch(stream)
         for i in range(args.steps):
             if args.cold_dirty:
                 flush.fill_(float(i))
@@ -311,6 +354,7 @@ def main() -> int:
             ev_s[i].record(stream)
             step()
             ev_e[i].record(stream)
+        probe_after.launch(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
@@ -323,10 +367,12 @@ def main() -> int:
         ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
+        probe_before.launch(stream)
         ev0.record(stream)
         for i in range(args.steps):
             step()
         ev1.record(stream)
+        probe_after.launch(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         total_ms = ev0.elapsed_time(ev1)
@@ -341,12 +387,14 @@ def main() -> int:
         torch.cuda.synchronize()
         per_launch = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
     ms_per_step = total_ms / args.steps
-    def record_event():
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        return ev
-
-    sclk = None if args.no_sclk else sample_sclk(step, record_event, ms_per_step)
+    sclk_before, sclk_after = probe_before.mhz(), probe_after.mhz()
+    log(f"engine clock (on-GPU probe): {sclk_before} MHz right before the timed region, {sclk_after} MHz right after")
+    # the launch floor: an empty kernel with this variant's grid, workgroup size and LDS
+    floor_ms = launch_floor_ms(floor_grid, info["threads"], info["lds_bytes"], args.steps, stream)
+    log(f"dispatch plan: first=1 rough=3 preroll={pre_steps} warmup={args.warmup} timed={args.steps} "
+        f"single={n_spread} floor={args.steps + 20}")
+    log(f"launch floor: empty kernel, {floor_grid} workgroups of {info['threads']} threads, "
+        f"{info['lds_bytes']} B LDS: {floor_ms * 1e3:.2f} us per launch")
     flops = gemm_flops(w.M, w.N, w.K)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     # cold: the mean of the individually timed launches (the flushes between them are excluded);
@@ -403,13 +451,20 @@ def main() -> int:
         "alg_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pct_hbm_peak_alg": round(100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,
-        # amd-smi's gfx clock (mean over XCDs) while this step ran back to back, and the share of
-        # the FP32 MFMA peak at that clock (the 157.3 figure assumes 2.4 GHz)
-        "sclk_mhz": round(sclk[0], 1) if sclk else None,
-        "pct_fp32_peak_at_sclk": round(100.0 * achieved / (FP32_PEAK_TFLOPS * sclk[0] / 2400.0), 2)
-        if sclk else None,
+        "preroll": {"seconds": round(pre_s, 3), "steps": pre_steps},
+        # the engine clock right before and right after the timed region, read on the GPU on the
+        # kernels' stream (shader cycles over real-time ticks of a probe kernel), and the share of
+        # the FP32 peak at their mean (the 157.3 figure assumes 2.4 GHz)
+        "sclk_mhz": {"before": round(sclk_before, 1) if sclk_before else None,
+                     "after": round(sclk_after, 1) if sclk_after else None},
+        "pct_fp32_peak_at_sclk": round(100.0 * achieved / (FP32_PEAK_TFLOPS * (sclk_before + sclk_after) / 2
+                                                           / 2400.0), 2) if sclk_before and sclk_after else None,
+        "launch_floor": {"us": round(floor_ms * 1e3, 3), "workgroups": floor_grid, "threads": info["threads"],
+                         "lds_bytes": info["lds_bytes"], "floor_over_launch": round(floor_ms / avg_launch_ms, 4)},
         "host_cpu": host_cpu_model(),
     }
+    if smi_mhz is not None:
+        line["sclk_mhz_smi_preroll"] = round(smi_mhz, 1)
     if roofline is not compute_roof:
         line["roofline_compute"] = compute_roof
     if not args.no_cpu_baseline:

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     load_library,
     sgemm,
     sgemm_ex,
+    sgemm_last_variant,
     sgemm_num_variants,
     sgemm_op,
     sgemm_op_ex,

@@ -87,6 +87,8 @@ def load_library(path: str | None = None):
         lib.sgemm_select_variant.restype = i
         lib.sgemm_tile_order.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sgemm_tile_order.restype = i
+        lib.sgemm_last_variant.argtypes = []
+        lib.sgemm_last_variant.restype = i
         lib.sgemm_version.argtypes = []
         lib.sgemm_version.restype = cp
         if path is None:
@@ -187,6 +189,11 @@ def sgemm_op_select_variant(transa, transb, M, N, K, A, lda, B, ldb, C, ldc) -> 
                                                       _ptr(A), int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc)))
 
 
+def sgemm_last_variant() -> int:
+    """Variant id of this thread's most recent computing call, or -1 (see include/sgemm.h)."""
+    return int(load_library().sgemm_last_variant())
+
+
 def sgemm_version() -> str:
     return load_library().sgemm_version().decode()
 
@@ -201,17 +208,29 @@ def tile_order(tiles_m: int, tiles_n: int, group_m: int):
     return list(tm), list(tn)
 
 
+def _require_device(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
 def _check_matrix(t, name):
+    """Validate a 2-D float32 device tensor with unit column stride; returns its leading dimension."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != torch.float32 or t.dim() != 2:
         raise TypeError(f"{name} must be a 2-D float32 tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    _require_device(t, name)
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must be row-major with unit column stride")
-    return t.stride(0) if t.shape[0] > 1 else max(1, t.shape[1])
+    if t.shape[0] <= 1 or t.shape[1] == 0:
+        return max(1, t.shape[1])  # one row, or no element: no stride is addressed
+    if t.stride(0) < t.shape[1]:
+        # a broadcast (stride 0) or overlapping view: its rows share storage, so no leading
+        # dimension describes it, and the library would address past its storage
+        raise ValueError(f"{name} has row stride {t.stride(0)} below its row length {t.shape[1]} "
+                         f"(a broadcast or overlapping view); pass a contiguous copy")
+    return t.stride(0)
 
 
 def _column_major(t) -> bool:
@@ -245,9 +264,6 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = -1, stre
     K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
-    lda = max(lda, A.shape[1], 1)
-    ldb = max(ldb, B.shape[1], 1)
-    ldc = max(ldc, N, 1)
     if trans_a or trans_b:
         sgemm_op_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
     else:

@@ -28,6 +28,11 @@ HBM_READ_LIB = os.path.join(HERE, "libhbm_read.so")
 HBM_READ_SOURCES = [os.path.join(CSRC, "hbm_read.hip")]
 
 
+# The launch-floor and engine-clock reference kernels of the bench (not part of libsgemm).
+LAUNCH_REFS_LIB = os.path.join(HERE, "liblaunch_refs.so")
+LAUNCH_REFS_SOURCES = [os.path.join(CSRC, "launch_refs.hip")]
+
+
 def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> str:
     """Compile libsgemm's HIP sources into one shared library; returns its path."""
     return _compile(SOURCES, out or LIB, verbose, extra_flags)
@@ -36,6 +41,11 @@ def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> st
 def build_hbm_read(verbose: bool = False) -> str:
     """Compile the streaming-read reference kernel (libhbm_read.so); returns its path."""
     return _compile(HBM_READ_SOURCES, HBM_READ_LIB, verbose, None)
+
+
+def build_launch_refs(verbose: bool = False) -> str:
+    """Compile the launch-floor and clock-probe reference kernels (liblaunch_refs.so)."""
+    return _compile(LAUNCH_REFS_SOURCES, LAUNCH_REFS_LIB, verbose, None)
 
 
 def _compile(sources, out: str, verbose: bool, extra_flags) -> str:

@@ -23,7 +23,8 @@ struct Variant {
     int tb;    // op(B) = B^T: B stored N x K
 };
 
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// 64-bit sum: a + b - 1 would overflow int for a near INT_MAX.
+inline int ceil_div(int a, int b) { return (int)(((long)a + b - 1) / b); }
 
 // Tile-rows per group of the workgroup -> tile map.  Measured on 4096^3 and 8192^3 with the
 // 128x128 tile over groups of 4, 8, 16 and 32 rows, with and without the XCD renumbering:

@@ -13,6 +13,8 @@
         HBM bytes per launch of one kernel from two --pmc runs, each scaled by the copy calibration.
     python -m fp32_gemm_05_amd.profiling counters <counter_collection.csv> --kernel SUBSTR --out X.md
         per-dispatch means of any collected counters for one kernel.
+    python -m fp32_gemm_05_amd.profiling series <kernel_trace.csv> --log BENCH_STDERR --command "..." --out X.md
+        per-phase durations of a traced bench run (first call, pre-roll, warmup, timed region, ...).
     python -m fp32_gemm_05_amd.profiling collect --dir D --workload W [--warmup N] [--out-dir profiles]
         runs every rocprofv3 pass below (each as a child process with its own time limit) and then
         `report`: the one command behind each committed summary.
@@ -101,6 +103,72 @@ def _hbm_read_lib():
     lib.hbm_read.restype = ctypes.c_int
     lib.hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return lib
+
+
+def launch_refs_lib():
+    """liblaunch_refs.so: the empty kernel of the launch floor and the engine-clock probe."""
+    import ctypes
+    from .build import LAUNCH_REFS_LIB, build_launch_refs
+    if not os.path.exists(LAUNCH_REFS_LIB):
+        build_launch_refs()
+    lib = ctypes.CDLL(LAUNCH_REFS_LIB)
+    lib.launch_floor.restype = ctypes.c_int
+    lib.launch_floor.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sclk_probe.restype = ctypes.c_int
+    lib.sclk_probe.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
+    lib.wall_clock_khz.restype = ctypes.c_int
+    lib.wall_clock_khz.argtypes = []
+    return lib
+
+
+class SclkProbe:
+    """The engine clock at one point of a stream: a probe kernel of one workgroup per XCD spins for
+    `ticks` ticks of the constant-rate real-time counter and counts shader cycles meanwhile.
+    launch() enqueues it (no host synchronisation); mhz() reads the result afterwards: the mean
+    over the workgroups of cycles / ticks x the real-time counter's rate."""
+
+    def __init__(self, nblocks: int = 8, ticks: int = 2000):
+        import torch
+        self.lib = launch_refs_lib()
+        self.nblocks, self.ticks = nblocks, ticks
+        self.buf = torch.zeros(2 * nblocks, dtype=torch.int64, device="cuda")
+        self.khz = self.lib.wall_clock_khz()
+
+    def launch(self, stream) -> None:
+        rc = self.lib.sclk_probe(self.nblocks, self.ticks, self.buf.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"sclk_probe returned {rc}")
+
+    def mhz(self):
+        v = self.buf.cpu().tolist()
+        ratios = [c / t for c, t in zip(v[0::2], v[1::2]) if t > 0]
+        if not ratios or self.khz <= 0:
+            return None
+        return sum(ratios) / len(ratios) * self.khz / 1000.0
+
+
+def launch_floor_ms(nwg: int, threads: int, lds_bytes: int, steps: int, stream, warmup: int = 20) -> float:
+    """Mean time per launch of an empty kernel with the given grid, workgroup size and LDS, timed
+    as the bench times a GEMM: `steps` back-to-back launches between two events on `stream`."""
+    import torch
+    lib = launch_refs_lib()
+
+    def go():
+        rc = lib.launch_floor(nwg, threads, lds_bytes, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"launch_floor returned {rc}")
+
+    for _ in range(warmup):
+        go()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        go()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def run_read(mib: int, reps: int, mode: str, chunk_kib: int = 1024) -> None:
@@ -221,6 +289,46 @@ def cmd_counters(args) -> None:
              "| Counter | Mean per dispatch |", "|---|---|"]
     for k in sorted(c):
         lines.append(f"| {k} | {_mean(c[k]):.6g} |")
+    if args.note:
+        lines += ["", args.note]
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def cmd_series(args) -> None:
+    """Per-phase durations of a traced bench run: the GEMM kernel's dispatches in order, split by
+    the bench's "dispatch plan" line (first call, step-time probe, pre-roll, warmup, timed region,
+    single launches), with the duration of every dispatch of the first and last phases shown."""
+    import re
+    with open(args.log) as f:
+        plan = next((l for l in f if l.startswith("dispatch plan:")), None)
+    if plan is None:
+        raise SystemExit(f"no 'dispatch plan' line in {args.log}")
+    phases = [(k, int(v)) for k, v in re.findall(r"(\w+)=(\d+)", plan) if k != "floor"]
+    with open(args.csv) as f:
+        rows = [r for r in csv.DictReader(f) if args.kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    starts = [int(r["Start_Timestamp"]) for r in rows]
+    expect = sum(n for _, n in phases)
+    lines = [f"# Dispatch series: {args.title}", "", "Command:", "", "```", args.command, "```", "",
+             f"Kernel match: `{args.kernel}`; {len(dur)} dispatches traced, {expect} in the bench's plan "
+             f"({plan.strip()[len('dispatch plan: '):]}).", "",
+             "| Phase | Dispatches | Mean (us) | Min (us) | Max (us) | First (us) | Last (us) | Span incl. gaps (ms) |",
+             "|---|---|---|---|---|---|---|---|"]
+    i = 0
+    for name, n in phases:
+        seg = dur[i:i + n]
+        if seg:
+            span = (starts[i + n - 1] - starts[i]) / 1e6 + seg[-1] / 1e3
+            lines.append(f"| {name} | {n} | {_mean(seg):.1f} | {min(seg):.1f} | {max(seg):.1f} | {seg[0]:.1f} | "
+                         f"{seg[-1]:.1f} | {span:.3f} |")
+        i += n
+    if args.show:
+        lines += ["", f"Durations (us) of the first {args.show} dispatches, in order:", "",
+                  ", ".join(f"{x:.0f}" for x in dur[:args.show])]
     if args.note:
         lines += ["", args.note]
     text = "\n".join(lines) + "\n"
@@ -472,6 +580,15 @@ def main(argv=None) -> int:
     p.add_argument("--command", required=True)
     p.add_argument("--note", default="")
     p.add_argument("--out", required=True)
+    p = sub.add_parser("series", help="per-phase dispatch durations of a traced bench run")
+    p.add_argument("csv", help="run_kernel_trace.csv of `rocprofv3 --kernel-trace` over bench.py")
+    p.add_argument("--log", required=True, help="the bench's stderr (holds its dispatch plan)")
+    p.add_argument("--kernel", default="sgemm")
+    p.add_argument("--title", default="")
+    p.add_argument("--command", required=True)
+    p.add_argument("--show", type=int, default=40)
+    p.add_argument("--note", default="")
+    p.add_argument("--out", required=True)
     p = sub.add_parser("collect", help="run every profiler pass of one workload and write its summary")
     p.add_argument("--dir", required=True, help="where the raw rocprofv3 output goes")
     p.add_argument("--workload", required=True)
@@ -502,6 +619,8 @@ def main(argv=None) -> int:
         cmd_traffic(args)
     elif args.cmd == "counters":
         cmd_counters(args)
+    elif args.cmd == "series":
+        cmd_series(args)
     return 0
 
 

@@ -17,18 +17,23 @@
  * = row * ncols + col addressing ("SGEMM CUDA kernel (First Half)", "Part 1:
  * CPU version") with the row stride made explicit:
  *     A(i, k) = A[i * lda + k],  B(k, j) = B[k * ldb + j],  C(i, j) = C[i * ldc + j].
- * Requirements: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).
+ * Requirements: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N), and
+ * M, N, K <= 2^31 - 1025 (tile and slab coordinates then stay inside int).
  *
  * Memory and ownership: A, B and C are DEVICE pointers (e.g. from hipMalloc or
  * a torch CUDA tensor) owned by the caller.  The library allocates no device
  * memory and keeps no pointer after it returns.  C must not overlap A or B
- * (checked, error -10); A and B may overlap each other.
+ * (checked, error -10); A and B may overlap each other.  The check compares
+ * address spans, from an operand's first addressed element to its last, so
+ * sub-matrices of one allocation whose rows interleave (e.g. disjoint column
+ * ranges of the same rows, sharing no element) are refused as well.
  *
  * Streams: work is enqueued on `stream` (0 = the null stream) and the call
  * returns without waiting for it; the usual stream ordering applies.  There is
  * no implicit synchronisation.  Calls are thread-safe: the only global state is
  * read-only after its first use (the dispatch table, each kernel's occupancy and
- * the device's compute-unit count, computed once).  The library records no
+ * the device's compute-unit count, computed once), and the one piece of mutable
+ * state, the variant of sgemm_last_variant, is per calling thread.  The library records no
  * memset and allocates nothing, so calls may be captured into a HIP graph.
  *
  * Semantics of the special cases:
@@ -163,6 +168,14 @@ SGEMM_API int sgemm_op_select_variant(char transa, char transb, int M, int N, in
                                       const float *A, int lda,
                                       const float *B, int ldb,
                                       const float *C, int ldc);
+
+/* The variant id of the calling thread's most recent computing call (sgemm,
+ * sgemm_ex, sgemm_op, sgemm_op_ex) when that call enqueued a GEMM kernel; -1 when
+ * it enqueued none (an invalid argument, M == 0 or N == 0, the alpha == 0 / K == 0
+ * scale path, a failed launch) or when this thread has made no such call.  The
+ * value is kept per host thread, so concurrent callers on other threads do not
+ * change it.  Pure host function. */
+SGEMM_API int sgemm_last_variant(void);
 
 /* Host-side copy of the workgroup -> output-tile map every kernel uses (for tests):
  * fills tile_m[w], tile_n[w] for w in [0, tiles_m * tiles_n).  Returns 0, or -1

@@ -61,3 +61,18 @@ def check_exact(got: np.ndarray, ref: np.ndarray, what: str = ""):
         idx = tuple(np.argwhere(neq)[0])
         raise AssertionError(f"{what}: {np.count_nonzero(neq)} elements differ; first at {idx}: "
                              f"got {got[idx]!r}, want {ref[idx]!r}")
+
+
+def assert_border_untouched(buf_host: np.ndarray, rows: int, cols: int, ld: int, offset: int = 0,
+                            sentinel: float = SENTINEL, what: str = ""):
+    """Every element of a 1-D host copy of C's buffer outside the rows x cols window (row stride
+    ld, starting `offset` floats in) still holds the sentinel.  Vectorised: full-size C has up to
+    hundreds of thousands of rows."""
+    inside = np.zeros(buf_host.shape[0], dtype=bool)
+    if rows and cols:
+        starts = offset + np.arange(rows, dtype=np.int64) * ld
+        idx = (starts[:, None] + np.arange(cols, dtype=np.int64)[None, :]).ravel()
+        inside[idx] = True
+    outside = buf_host[~inside]
+    bad = np.count_nonzero(outside != sentinel)
+    assert bad == 0, f"{what}: {bad} writes outside C's {rows} x {cols} window"

@@ -25,7 +25,7 @@ def declared_symbols():
 def test_header_declares_the_abi():
     names = declared_symbols()
     for n in ["sgemm", "sgemm_ex", "sgemm_num_variants", "sgemm_variant_name", "sgemm_variant_info",
-              "sgemm_select_variant", "sgemm_tile_order", "sgemm_version"]:
+              "sgemm_select_variant", "sgemm_tile_order", "sgemm_last_variant", "sgemm_version"]:
         assert n in names, n
 
 
@@ -89,6 +89,42 @@ def test_overlapping_c_rejected():
     assert _call(4, 4, 4, 4, 4, 4, A=FAKE_C + 16) == -10
     # C overlaps B's addressed range
     assert _call(4, 4, 4, 4, 4, 4, B=FAKE_C - 16) == -10
+
+
+def test_overlap_check_compares_address_spans():
+    """Disjoint column ranges of the same rows (A = X[:, :4], C = X[:, 4:8] with ld 8) share no
+    element, but their address spans interleave: the span check refuses them (-10), as
+    include/sgemm.h states.  Disjoint row ranges of one allocation pass."""
+    X = FAKE_A
+    assert _call(4, 4, 4, 8, 4, 8, A=X, C=X + 16) == -10
+    assert _call(4, 4, 4, 8, 4, 8, B=X, C=X + 16, A=FAKE_B) == -10
+    # rows 0..3 for A (K = 8, ld 8), rows 4..7 for C: spans [X, X + 128) and [X + 128, X + 256);
+    # validation passes and the out-of-range variant id is reported instead (nothing launches)
+    assert _call(4, 8, 8, 8, 8, 8, A=X, C=X + 4 * 8 * 4, variant=sg.sgemm_num_variants()) == -13
+
+
+def test_extents_beyond_the_limit_are_refused():
+    """M, N or K above 2^31 - 1025 are refused before any launch (tile and slab coordinates would
+    leave int), and the dispatcher reports no variant for them instead of a wrapped tile count."""
+    big = 2 ** 31 - 1
+    assert _call(big, 1, 1, 1, 1, 1) == -1
+    assert _call(1, big, 1, 1, big, big) == -2
+    assert _call(1, 1, big, big, 1, 1) == -3
+    assert sg.sgemm_select_variant(big, 1, 1, FAKE_A, 1, FAKE_B, 1, FAKE_C, 1) == -1
+    assert sg.sgemm_op_select_variant("N", "N", 1, big, 1, FAKE_A, 1, FAKE_B, big, FAKE_C, big) == -1
+    lim = 2 ** 31 - 1025
+    # at the limit the dispatcher still answers (a tall single column: the narrow class)
+    v = sg.sgemm_select_variant(lim, 1, 1, FAKE_A, 1, FAKE_B, 1, FAKE_C, 1)
+    assert v >= 0 and sg.sgemm_variant_info(v)["BN"] == 32
+
+
+def test_last_variant_without_launches():
+    """sgemm_last_variant is -1 after calls that enqueue no GEMM kernel (invalid arguments and
+    quick returns); only a successful GEMM launch sets it (checked on the GPU)."""
+    assert _call(-1, 4, 4, 4, 4, 4) == -1
+    assert sg.sgemm_last_variant() == -1
+    assert _call(0, 4, 4, 4, 4, 4, A=None, B=None, C=None) == 0
+    assert sg.sgemm_last_variant() == -1
 
 
 def test_quick_returns_need_no_gpu():

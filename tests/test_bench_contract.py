@@ -52,8 +52,14 @@ def test_bench_line_headline_fields():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["unit"] == "TFLOP/s"
     assert d["parity"]["pass"] is True
-    # the engine clock read with amd-smi under sustained load (None where amd-smi is missing)
-    assert "sclk_mhz" in d and (d["sclk_mhz"] is None or 100.0 <= d["sclk_mhz"] <= 2500.0)
+    # the engine clock right before and right after the timed region, read on the GPU
+    for when in ("before", "after"):
+        assert 100.0 <= d["sclk_mhz"][when] <= 2600.0, d["sclk_mhz"]
+    # the reported pre-roll, and the launch floor of the dispatched grid
+    assert d["preroll"]["seconds"] >= 0 and d["preroll"]["steps"] >= 0
+    lf = d["launch_floor"]
+    assert lf["us"] > 0 and lf["workgroups"] == 16 and lf["threads"] % 64 == 0  # 64x64 tiles of 256^2
+    assert abs(lf["floor_over_launch"] - lf["us"] * 1e-3 / d["ms_per_step"]) <= 0.01 * lf["floor_over_launch"] + 1e-3
 
 
 @pytest.mark.gpu

@@ -4,7 +4,7 @@ The header promises thread safety: the library's only global state (the dispatch
 kernel's occupancy, the device's compute-unit count) is computed once on first use and read-only
 afterwards.  Each thread runs a mix of plain and transposed calls from several shape classes on its
 own stream; every result must equal, bit for bit, the same call run alone beforehand (the kernels
-are deterministic).  The first-use case runs in a fresh process, so that the threads race to
+are deterministic), and after each call sgemm_last_variant must name that thread's own variant.  The first-use case runs in a fresh process, so that the threads race to
 initialise that state.
 """
 from __future__ import annotations
@@ -56,6 +56,13 @@ def run_threads(n_threads: int = 6, reps: int = 3) -> int:
                         j = (i + t) % len(cases)
                         C = C0.clone()
                         sg.gemm(A, B, C, alpha=alpha, beta=beta, trans_a=ta, trans_b=tb, stream=stream)
+                        # sgemm_last_variant is per thread: it names this thread's call, whatever
+                        # the other threads launched meanwhile
+                        M, N = C.shape
+                        K = A.shape[0] if ta else A.shape[1]
+                        want = sg.sgemm_op_select_variant(ta, tb, M, N, K, A, A.shape[1], B, B.shape[1], C, N)
+                        if sg.sgemm_last_variant() != want:
+                            errors.append(f"thread {t}: last variant {sg.sgemm_last_variant()} != {want}")
                         if r == reps - 1:
                             outs[t][j] = C
                 stream.synchronize()

@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from fp32_gemm_05_amd.workloads import WORKLOADS, make_inputs, sample_points
-from tests.gemm_cases import SENTINEL, check_exact, check_within_bound, device_matrix
+from fp32_gemm_05_amd.workloads import WORKLOADS, make_inputs
+from tests.gemm_cases import SENTINEL, assert_border_untouched, check_exact, check_within_bound, device_matrix
 
 pytestmark = pytest.mark.gpu
 
@@ -265,28 +265,29 @@ FULL_TRANS = [("square4096", "N", "T"), ("square4096", "T", "N"), ("square4096",
 
 @pytest.mark.parametrize("wname,ta,tb", FULL_TRANS, ids=[f"{w}_{a}{b}" for w, a, b in FULL_TRANS])
 @pytest.mark.parametrize("kind", ["float", "int"])
-def test_trans_full_size_sampled(wname, ta, tb, kind):
+def test_trans_full_size_elementwise(wname, ta, tb, kind):
     """4096^3 in each transposition and the skinny and narrow streams with B transposed, default
-    dispatch, sampled outputs (random points plus tile boundary rows/columns) computed one by one
-    by the oracle."""
+    dispatch, every element of C against the oracle's full-matrix form (integer data exactly),
+    with sentinel rows and columns around C."""
     w = WORKLOADS[wname] if kind == "float" else WORKLOADS[wname].as_int()
     _say(f"[trans-full] {ta}{tb} {w.describe()}")
     A, B, C = make_inputs(w)
     As, Bs = stored(A, B, ta, tb)
     dA = torch.from_numpy(As).cuda()
     dB = torch.from_numpy(Bs).cuda()
-    dC = torch.from_numpy(C).cuda()
-    vid = sg.sgemm_op_select_variant(ta, tb, w.M, w.N, w.K, dA, As.shape[1], dB, Bs.shape[1], dC, w.N)
+    bufC, vC, ldc = device_matrix(C, pad_cols=4, pad_rows=2, fill=SENTINEL)
+    vid = sg.sgemm_op_select_variant(ta, tb, w.M, w.N, w.K, dA, As.shape[1], dB, Bs.shape[1], vC, ldc)
     _say(f"[trans-full] variant={sg.sgemm_variant_name(vid)}")
-    sg.gemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, trans_a=(ta == "T"), trans_b=(tb == "T"))
+    sg.sgemm_op(ta, tb, w.M, w.N, w.K, w.alpha, dA, As.shape[1], dB, Bs.shape[1], w.beta, vC, ldc)
+    assert sg.sgemm_last_variant() == vid
     torch.cuda.synchronize()
-    out = dC.cpu().numpy()
-    del dA, dB, dC
-    I, J = sample_points(w.M, w.N, n_random=2048, seed=w.seed, tile=128)
-    ref, bound = oracle.ref_points(A, B, C, I, J, w.alpha, w.beta)
-    got = out[I, J]
+    host = bufC.cpu().numpy()
+    del dA, dB, bufC, vC
+    torch.cuda.empty_cache()
+    assert_border_untouched(host, w.M, w.N, ldc, what=f"full {ta}{tb}")
+    got = host[: w.M * ldc].reshape(w.M, ldc)[:, : w.N]
+    ref, bound = oracle.ref_matmul(A, B, C, w.alpha, w.beta)
     if kind == "int":
         check_exact(got, ref, f"full {ta}{tb}")
     else:
         check_within_bound(got, ref, bound, f"full {ta}{tb}")
-    assert np.all(np.isfinite(out))

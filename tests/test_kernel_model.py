@@ -93,7 +93,8 @@ def stored_elements(v, M, N):
     In split-K variants only k-group 0 (the first threads / ksplit threads) stores."""
     BM, BN, NT = v["BM"], v["BN"], v["threads"] // v["ksplit"]
     tiles_m, tiles_n = -(-M // BM), -(-N // BN)
-    tm_of, tn_of = _binding.tile_order(tiles_m, tiles_n, 8)
+    # the launches group min(tiles_m, 4) tile-rows (group_rows in csrc/sgemm_launch.hpp)
+    tm_of, tn_of = _binding.tile_order(tiles_m, tiles_n, min(tiles_m, 4))
     tid = np.arange(NT)
     rows_all, cols_all = [], []
     if v["kind"] == "mfma":
