@@ -199,6 +199,78 @@ struct PanelLoader {
     }
 };
 
+// Loader of a B slab (BK rows along K x BN columns of a row-major B) for the 32-bit-load
+// variants that stage B n-major in LDS, [BN][BK + 4]: each thread loads four consecutive k of one
+// column -- four 32-bit loads, each coalesced along N across the wave, since the lane-fastest
+// index is the column -- and writes them with ONE 128-bit LDS store, so that a lane's MFMA
+// fragment, four consecutive k of one column, is one 128-bit LDS read (the staging transpose of
+// "SGEMM CUDA kernel (First Half)", "Part 5: Reduced bank conflict (v3)", applied to B).  Against
+// PanelLoader's one LDS store per element and four 32-bit fragment reads, a quarter of the LDS
+// instructions for B.  Columns past N are clamped (they feed only C elements that are never
+// stored); k past K is zero (checked in the last slab only).  The four rows of a quad are
+// addressed from workgroup-uniform bases (scalar registers) plus one 32-bit per-lane byte offset
+// per quad (64-bit when WIDE).  Same interface as PanelLoader.
+template <int BK, int BN, int NT, bool WIDE, int NBUF = 1>
+struct KQuadLoader {
+    using OffT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
+    static constexpr int QROWS = BK / 4;          // k-quads per column per slab
+    static constexpr int QPP = NT / BN;           // k-quads of one column per pass of the workgroup
+    static constexpr int L = QROWS * BN / NT;     // quads per thread
+    static_assert(BK % 4 == 0 && NT % BN == 0 && QROWS % QPP == 0, "k-quads must split evenly");
+
+    f32x4 v[NBUF][L];
+    const float* base;  // workgroup-uniform address of the current slab's first row, first column
+    long ld_bytes;      // bytes from one row of B to the next
+    OffT off[L];        // byte offset of quad l's first element from base
+    int q0, col;        // this thread's first quad row and its column (panel coordinates)
+    long step;
+
+    __device__ inline void init(int tid, const float* __restrict__ op, long ld, int r0, int c0, int nrows,
+                                int ncols, int bk) {
+        (void)nrows;
+        col = tid % BN;
+        q0 = tid / BN;
+        step = (long)bk * ld;
+        ld_bytes = ld * 4;
+        base = op + (long)r0 * ld + c0;
+        const int c = imin(c0 + col, ncols - 1) - c0;  // clamp columns past N
+#pragma unroll
+        for (int l = 0; l < L; ++l) off[l] = (OffT)(((long)(q0 + l * QPP) * 4 * ld + c) * 4);
+    }
+
+    __device__ inline void advance() { base += step; }
+
+    template <bool TAIL, int BUF = 0>
+    __device__ inline void fetch(int kbase, int K) {
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            if (!WIDE) asm volatile("" : "+v"(off[l]));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool ok = !TAIL || kbase + (q0 + l * QPP) * 4 + t < K;
+                const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) +
+                                                                t * ld_bytes + off[l]);
+                v[BUF][l][t] = ok ? *p : 0.f;
+            }
+        }
+    }
+
+    template <int BUF = 0>
+    __device__ inline void fetch_slab(int kbase, int bk, int K) {
+        if (kbase + bk <= K)
+            fetch<false, BUF>(kbase, K);
+        else
+            fetch<true, BUF>(kbase, K);
+    }
+
+    // Store into an LDS panel [BN][PITCH] (column-major slab: element (k, n) at lds[n][k]).
+    template <int PITCH, int BUF = 0>
+    __device__ inline void store(float* __restrict__ lds) const {
+#pragma unroll
+        for (int l = 0; l < L; ++l) *reinterpret_cast<f32x4*>(lds + col * PITCH + (q0 + l * QPP) * 4) = v[BUF][l];
+    }
+};
+
 // ---------------------------------------------------------------------------------
 // MFMA kernel: v_mfma_f32_32x32x2_f32, wave tile WM x WN of 32x32 blocks.
 //
@@ -216,20 +288,23 @@ struct PanelLoader {
 // TA / TB: op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K).  The LDS slab of an
 // operand keeps the layout of its global rows: k-contiguous [rows][BK + 4] when K runs along
 // the stored rows (A, or B^T), and [BK][cols + 8] when it runs down the stored columns (B, or A^T).
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool TA = false, bool TB = false>
+// BQ: B (not transposed) is loaded in k-quads by KQuadLoader and staged n-major like B^T.
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool TA = false, bool TB = false, bool BQ = false>
 struct MfmaCfg {
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr bool B_NMAJOR = TB || BQ;  // B slab stored [BN][BK + 4], k contiguous
     // k-contiguous slabs: pitch BK+4, so the 128-bit reads of 16 consecutive rows hit distinct
     // banks; k-strided slabs: pitch (width)+8, so the two half-waves (k and k+4) land on
     // opposite bank halves.
-    static constexpr int A_PITCH = TA ? BM + 8 : BK + 4, B_PITCH = TB ? BK + 4 : BN + 8;
-    static constexpr int A_STAGE = (TA ? BK : BM) * A_PITCH, B_STAGE = (TB ? BN : BK) * B_PITCH;
+    static constexpr int A_PITCH = TA ? BM + 8 : BK + 4, B_PITCH = B_NMAJOR ? BK + 4 : BN + 8;
+    static constexpr int A_STAGE = (TA ? BK : BM) * A_PITCH, B_STAGE = (B_NMAJOR ? BN : BK) * B_PITCH;
     static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 4;
     static_assert(BM % WM == 0 && BN % WN == 0, "wave tiling");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(!(BQ && (TB || VEC)), "k-quad staging serves the 32-bit loads of an untransposed B");
 };
 
 // OCC > 0 asks the compiler for at least OCC waves per SIMD (registers capped at 512 / OCC),
@@ -421,11 +496,11 @@ struct DrainPhases {
 };
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
-          int FAIR = 0, bool NTA = false>
-__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>::NT))
+          int FAIR = 0, bool NTA = false, bool BQ = false>
+__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>;
     constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
     constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
     __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
@@ -445,8 +520,9 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     // B slab: BK rows x BN columns of B, or (TB) BN rows x BK columns of the stored B^T.
     using LoaderA = typename std::conditional<TA, PanelLoader<BK, BM, NT, VEC, true, WIDE, 1, NTA>,
                                               PanelLoader<BM, BK, NT, VEC, false, WIDE, 1, NTA>>::type;
-    using LoaderB = typename std::conditional<TB, PanelLoader<BN, BK, NT, VEC, false, WIDE>,
-                                              PanelLoader<BK, BN, NT, VEC, true, WIDE>>::type;
+    using LoaderB = typename std::conditional<
+        TB, PanelLoader<BN, BK, NT, VEC, false, WIDE>,
+        typename std::conditional<BQ, KQuadLoader<BK, BN, NT, WIDE>, PanelLoader<BK, BN, NT, VEC, true, WIDE>>::type>::type;
     LoaderA la;
     LoaderB lb;
     if (TA)
@@ -507,7 +583,7 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                if (TB) {
+                if (TB || BQ) {
                     const f32x4 v = *reinterpret_cast<const f32x4*>(sb + (wn0 + j * 32 + li) * BP + kk * 8 + lh * 4);
                     b[j][0] = v.x;
                     b[j][1] = v.y;
@@ -1163,6 +1239,301 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
     for (int d = 0; d < D; ++d) mfma(d);
 
     mfma_epilogue<1, 1, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0, n0, li, lh, cv);
+}
+
+// ---------------------------------------------------------------------------------
+// Direct-to-LDS MFMA kernel: the operand slabs go from global memory straight into LDS with
+// gfx950's global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base + 16 x lane),
+// so no register holds a prefetched slab and no LDS store instruction runs in the K loop -- the
+// stores that, at one wave per SIMD, take issue cycles and VGPR read bandwidth from the matrix
+// pipe.  STAGES LDS buffers form a ring: slab s + STAGES - 1 is requested right after the barrier
+// that opens slab s, into the buffer every wave finished reading before that barrier, so a slab
+// has STAGES - 1 slabs of MFMAs to arrive.  One barrier per slab; before it, each wave waits
+// (s_waitcnt vmcnt) only for its own loads of the next slab, leaving later slabs in flight.
+//
+// Layout: a wave's load fills 1 KiB of LDS contiguously, so the slabs are unpadded -- A as
+// [BM][BK] (k contiguous), B as [BK][BN] (n contiguous) -- and bank conflicts of the fragment
+// reads are avoided by choosing WHICH 16-byte quad of its row each lane fetches: the quad at LDS
+// position u of row r holds global quad u ^ swz(r) (an XOR swizzle, a permutation within the
+// row, so the loads of a row still cover the same cache lines).  The swizzles make the 128-bit A
+// reads (16 consecutive rows at one quad) and the 32-bit B reads (rows k and k + 4 at 32
+// consecutive columns) free of conflicts both with 64 banks and 16 lanes per pass and with 32 banks
+// and 8 lanes per pass.
+//
+// Edges: rows of A past M and columns of B past N are clamped (they feed C elements that are never
+// stored).  The slab that crosses K (K % BK != 0) is loaded with k clamped to K - 4 (A) or K - 1
+// (B), so every address lies inside the operand, and each wave then overwrites the quads it loaded
+// past K with zeros, after its loads have landed and before the barrier.  Needs 16-byte aligned
+// rows (the 128-bit variants' precondition: K and N multiples of 4).
+// ---------------------------------------------------------------------------------
+template <int QPR>
+__device__ __host__ inline int dl_swz_a(int r) {  // swizzle of A row r (QPR quads per row)
+    static_assert(QPR == 4 || QPR == 8, "A rows of 16 or 32 floats");
+    return QPR == 8 ? ((r & 15) + ((r >> 3) & 1)) & 7 : (((r >> 1) & 7) + ((r >> 3) & 1)) & 3;
+}
+__device__ __host__ inline int dl_swz_b(int k) { return ((k >> 2) & 1) * 8; }  // swizzle of B row k, in quads
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+struct DlCfg {
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int QPR_A = BK / 4, QPR_B = BN / 4;           // 16-byte quads per row
+    static constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;     // floats
+    static constexpr int LA = A_STAGE / 256 / NW, LB = B_STAGE / 256 / NW;  // 1 KiB loads per wave
+    static constexpr int LPW = LA + LB;                            // loads per wave per slab
+    static constexpr int D = STAGES - 1;                           // slabs in flight ahead
+    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 4;
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+    static_assert(A_STAGE % (256 * NW) == 0 && B_STAGE % (256 * NW) == 0, "whole 1 KiB loads per wave");
+    static_assert(BN % 64 == 0, "the B swizzle needs rows of 16 quads or more");
+    static_assert(BK % 8 == 0 && BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiling");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+// The direct loads, their waits and the barrier are inline asm.  Issued through the compiler
+// builtin, a load into LDS makes the compiler wait for it (s_waitcnt vmcnt(0)) before every later
+// LDS read it cannot tell apart from the loaded stage -- here every fragment read -- which would
+// expose the full load latency in every slab.  As asm with a memory clobber, the compiler neither
+// waits for these loads nor moves LDS accesses across them, the barrier or the waits; the kernel
+// waits for them itself.  Its own waits for other loads stay correct: counting fewer loads in
+// flight than there are only makes a vmcnt wait stricter.  M0 holds the LDS address (M0 is
+// reserved to the compiler, so the asm restores it); the s_nop covers the wait state between an
+// SALU write of M0 and the load that reads it.
+__device__ __attribute__((always_inline)) inline void dl_load(const void* base, uint32_t off, uint32_t lds) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(lds), "v"(off), "s"(base)
+        : "memory");
+}
+__device__ __attribute__((always_inline)) inline void dl_load_at(const void* p, uint32_t lds) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(lds), "v"(p)
+        : "memory");
+}
+// Wait until at most N of this wave's vector-memory loads are in flight and all its LDS accesses
+// are done.
+template <int N>
+__device__ __attribute__((always_inline)) inline void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"i"(N) : "memory");
+}
+__device__ __attribute__((always_inline)) inline void dl_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The LDS address of a pointer into a __shared__ array.
+__device__ __attribute__((always_inline)) inline uint32_t lds_addr(const float* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)(p);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int FAIR = 0, bool CPRE = false>
+__global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES>::NT))
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
+sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES>;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / 8, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
+    constexpr int QA = Cfg::QPR_A, QB = Cfg::QPR_B;
+    static_assert(KK % 2 == 0 || KK == 1, "fragment buffers alternate per 8-deep group");
+    __shared__ __attribute__((aligned(1024))) float lds_a[STAGES * Cfg::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) float lds_b[STAGES * Cfg::B_STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / Cfg::WAVES_N) * WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+    const int M = g.M, N = g.N, K = g.K;
+    const long lda = g.lda, ldb = g.ldb;
+
+    // This lane's loads: A chunk j of the wave is chunk c = wave * LA + j of the slab, rows
+    // c * 64 / QA + lane / QA, LDS quad lane % QA holding global quad (lane % QA) ^ swz(row).
+    uint32_t a_off[LA], b_off[LB];  // byte offsets from the slab's first element (full slabs)
+    int a_row[LA], a_q[LA], b_k[LB], b_n[LB];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int c = wave * LA + j;
+        const int r = (c * 64 + lane) / QA, u = lane % QA;
+        a_row[j] = imin(m0 + r, M - 1) - m0;
+        a_q[j] = u ^ dl_swz_a<QA>(r);
+        a_off[j] = (uint32_t)(((long)a_row[j] * lda + 4 * a_q[j]) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int c = wave * LB + j;
+        const int k = (c * 64 + lane) / QB, u = lane % QB;
+        b_k[j] = k;
+        b_n[j] = imin(n0 + 4 * (u ^ dl_swz_b(k)), N - 4) - n0;
+        b_off[j] = (uint32_t)(((long)k * ldb + b_n[j]) * 4);
+    }
+    const float* a_tile = g.A + (long)m0 * lda;  // A(m0, 0)
+    const float* b_tile = g.B + n0;              // B(0, n0)
+
+    // Request slab s into its stage.  TAIL: the slab crosses K; k is clamped into range here and
+    // the quads past K are zeroed by fix_tail once the loads have landed.
+    auto issue = [&](int s, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        const int st = s % STAGES, k0 = s * BK;
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * 256;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * 256;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            if (!TAIL)
+                dl_load(a_tile + k0, a_off[j], lds_addr(sa + j * 256));
+            else
+                dl_load_at(a_tile + (long)a_row[j] * lda + imin(k0 + 4 * a_q[j], K - 4), lds_addr(sa + j * 256));
+        }
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+            if (!TAIL)
+                dl_load(b_tile + (long)k0 * ldb, b_off[j], lds_addr(sb + j * 256));
+            else
+                dl_load_at(b_tile + (long)imin(k0 + b_k[j], K - 1) * ldb + b_n[j], lds_addr(sb + j * 256));
+        }
+    };
+    // After the loads of the slab that crosses K have landed: zero what lies past K (each wave
+    // its own quads, the ones its loads wrote).
+    auto fix_tail = [&](int s) {
+        const int st = s % STAGES, k0 = s * BK;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * 256;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * 256;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            if (k0 + 4 * a_q[j] >= K) *reinterpret_cast<f32x4*>(sa + j * 256 + lane * 4) = z;
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            if (k0 + b_k[j] >= K) *reinterpret_cast<f32x4*>(sb + j * 256 + lane * 4) = z;
+    };
+
+    // Fragment reads: A's quad 2 kk + h of row wm0 + 32 fi + li sits at quad ((2 kk + h) ^ swz) of
+    // that row (the swizzle depends on the row's low four bits only, so not on fi); B's element
+    // (k, n) with k = 8 kk + 4 h + t sits at column n ^ 32 h of row k (the B swizzle flips quad bit
+    // 3, i.e. column bit 5, on rows with bit 2 set).
+    int a_frag[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        a_frag[kk] = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
+    int b_frag[FN];
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh));
+    auto read_frag = [&](MfmaFrag<FM, FN>& f, int st, int kk) {
+        const float* sa = lds_a + st * Cfg::A_STAGE;
+        const float* sb = lds_b + st * Cfg::B_STAGE;
+#pragma unroll
+        for (int fi = 0; fi < FM; ++fi)
+            f.a[fi] = *reinterpret_cast<const f32x4*>(sa + a_frag[kk] + fi * 32 * BK);
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (8 * kk + t) * BN];
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<true>(f.a[i][t], f.b[j][t], acc[i][j]);
+    };
+
+    const int nslab = (K + BK - 1) / BK;
+    const int nfull = K / BK;
+    using Tail = std::integral_constant<bool, true>;
+    using Whole = std::integral_constant<bool, false>;
+    // the C values of the beta term first: the oldest loads, consumed only by the epilogue
+    f32x16 cv[FM][FN];
+    if (CPRE && g.beta != 0.f) mfma_load_c<FM, FN, true>(M, N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
+    // prologue: slabs 0 .. D-1 requested; wait for slab 0 (its later slabs may stay in flight)
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        if (s < nfull)
+            issue(s, Whole{});
+        else if (s < nslab)
+            issue(s, Tail{});
+    }
+    if (D == 2 && nslab > 1)
+        wait_vm_lgkm0<Cfg::LPW * (D - 1)>();
+    else
+        wait_vm_lgkm0<0>();
+    if (nfull == 0) {
+        fix_tail(0);
+        wait_vm_lgkm0<0>();
+    }
+    dl_barrier();
+    MfmaFrag<FM, FN> F[2];
+    read_frag(F[0], 0, 0);
+
+    // Slab s (stage ST = s % STAGES when known at compile time, else -1).  FULL: slab s + D exists
+    // and is whole, so the wait before the next barrier leaves exactly D - 1 slabs in flight.
+    auto slab = [&](int s, auto stage, auto full) {
+        constexpr int STC = decltype(stage)::value;
+        constexpr bool FULL = decltype(full)::value;
+        const int st = STC >= 0 ? STC : s % STAGES;
+        if (FULL)
+            issue(s + D, Whole{});
+        else if (s + D < nfull)
+            issue(s + D, Whole{});
+        else if (s + D < nslab)
+            issue(s + D, Tail{});
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            read_frag(F[(kk + 1) & 1], st, kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frag(F[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (FULL || s + 1 < nslab) {
+            // slabs requested after slab s + 1: s + 2 .. min(s + D, nslab - 1)
+            if (FULL) {
+                wait_vm_lgkm0<Cfg::LPW * (D - 1)>();
+            } else {
+                if (D == 2 && s + 2 < nslab)
+                    wait_vm_lgkm0<Cfg::LPW * (D - 1)>();
+                else
+                    wait_vm_lgkm0<0>();
+                if (s + 1 >= nfull) {
+                    fix_tail(s + 1);
+                    wait_vm_lgkm0<0>();
+                }
+            }
+            dl_barrier();
+            read_frag(F[0], STC >= 0 ? (STC + 1) % STAGES : (s + 1) % STAGES, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_frag(F[(KK - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Checked = std::integral_constant<bool, false>;
+    DrainPhases drain;
+    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
+    int s = 0;
+    // STAGES slabs per trip, so that every stage offset is a constant
+    for (; s + STAGES - 1 + D < nfull; s += STAGES) {
+        if (FAIR > 0) drain.step(s);
+        slab(s, std::integral_constant<int, 0>{}, Full{});
+        slab(s + 1, std::integral_constant<int, 1>{}, Full{});
+        if (STAGES == 3) slab(s + 2, std::integral_constant<int, 2 % STAGES>{}, Full{});
+    }
+    for (; s < nslab; ++s) slab(s, std::integral_constant<int, -1>{}, Checked{});
+
+    mfma_epilogue<FM, FN, true, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
 }
 
 // ---------------------------------------------------------------------------------

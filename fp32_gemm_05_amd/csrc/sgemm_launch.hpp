@@ -21,6 +21,8 @@ struct Variant {
     int ks;    // k-groups sharing one tile inside a workgroup (split-K); 0 means 1
     int ta;    // op(A) = A^T: A stored K x M
     int tb;    // op(B) = B^T: B stored N x K
+    int bq;    // B loaded in k-quads and staged n-major in LDS (KQuadLoader; 32-bit loads only)
+    int dl;    // operands loaded straight into LDS (global_load_lds), a ring of `dl` LDS stages
 };
 
 // 64-bit sum: a + b - 1 would overflow int for a near INT_MAX.
@@ -69,10 +71,10 @@ int occupancy(Kernel kernel, int threads) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
-          int FAIR = 0, bool NTA = false>
+          int FAIR = 0, bool NTA = false, bool BQ = false>
 hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB>;
-    auto kernel = &sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB, FAIR, NTA>;
+    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>;
+    auto kernel = &sgemm_mfma_kernel<BM, BN, BK, WM, WN, VEC, OCC, WIDE, TA, TB, FAIR, NTA, BQ>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -90,6 +92,22 @@ template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 
 hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
     auto kernel = &sgemm_mfma_deep_kernel<BM, BN, BK, WM, WN, VEC, OCC, FAIR, NTA, CPRE, ACC2>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    GemmArgs a = g;
+    if (FAIR > 0) {
+        static const int per_cu = occupancy(kernel, Cfg::NT);
+        a.drain_from = drain_from(tiles_m * tiles_n, per_cu);
+    }
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0,
+                           stream);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int FAIR = 0, bool CPRE = false>
+hipError_t launch_mfma_dl(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES>;
+    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -230,7 +248,17 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define CP_DEEP_VARIANT(BM, BN, BK, WM, WN, VEC, P, NAME)                                       \
     {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT, VEC,                  \
      MfmaCfg<BM, BN, BK, WM, WN, VEC>::LDS_BYTES, &launch_mfma_deep<BM, BN, BK, WM, WN, VEC, 0, P, false, true>, 0}
+// B in k-quads, staged n-major ("_bq"; 32-bit loads only)
+#define BQ_VARIANT(BM, BN, BK, WM, WN, OCC, FAIR, NTA, NAME)                                       \
+    {NAME, kMfma, BM, BN, BK, WM, WN, MfmaCfg<BM, BN, BK, WM, WN, false>::NT, 0,                    \
+     MfmaCfg<BM, BN, BK, WM, WN, false, false, false, true>::LDS_BYTES,                            \
+     &launch_mfma<BM, BN, BK, WM, WN, false, OCC, false, false, false, FAIR, NTA, true>, 0, 0, 0, 0, 1}
 #define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
+// operands loaded straight into a ring of STAGES LDS buffers ("mfma32l_", 128-bit loads only)
+#define DL_VARIANT(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX)                                  \
+    {"mfma32l_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #STAGES SUFFIX "_vec", kMfma, BM, BN, BK, WM, WN, \
+     DlCfg<BM, BN, BK, WM, WN, STAGES>::NT, 1, DlCfg<BM, BN, BK, WM, WN, STAGES>::LDS_BYTES,              \
+     &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE>, 0, 0, 0, 0, 0, STAGES}
 #define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
     DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
         DEEP_VARIANT(BM, BN, BK, WM, WN, false, DEEP_NAME(BM, BN, BK, WM, WN) "_scalar")
@@ -330,5 +358,19 @@ const Variant kVariants[] = {
     NT_STREAM_VARIANT(128, 64, 32, 64, 32, false, 3, MFMA_NAME(128, 64, 32, 64, 32) "_d3_nta_nt_scalar"),
     NT_STREAM_VARIANT(128, 32, 32, 32, 32, true, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_nt_vec"),
     NT_STREAM_VARIANT(128, 32, 32, 32, 32, false, 3, MFMA_NAME(128, 32, 32, 32, 32) "_d3_nta_nt_scalar"),
+    // unaligned operands with B in k-quads (one 128-bit LDS store and one 128-bit fragment read per
+    // four k of a column, instead of four 32-bit ones each)
+    BQ_VARIANT(64, 64, 16, 32, 32, 0, 0, false, MFMA_NAME(64, 64, 16, 32, 32) "_bq_scalar"),
+    BQ_VARIANT(64, 64, 32, 32, 32, 0, 3, false, MFMA_NAME(64, 64, 32, 32, 32) "_d3_bq_scalar"),
+    BQ_VARIANT(128, 128, 16, 64, 64, 4, 4, false, MFMA_NAME(128, 128, 16, 64, 64) "_o4_d4_bq_scalar"),
+    // direct global -> LDS loads into a ring of two or three LDS stages
+    DL_VARIANT(64, 64, 32, 32, 32, 3, 0, 0, true, "_cp"),
+    DL_VARIANT(64, 64, 32, 32, 32, 3, 0, 0, false, ""),
+    DL_VARIANT(64, 64, 32, 32, 32, 2, 0, 0, true, "_cp"),
+    DL_VARIANT(64, 64, 32, 32, 32, 3, 0, 3, false, "_d3"),
+    DL_VARIANT(128, 128, 16, 64, 64, 3, 0, 4, false, "_d4"),
+    DL_VARIANT(128, 128, 16, 64, 64, 3, 0, 3, false, "_d3"),
+    DL_VARIANT(128, 128, 16, 64, 64, 2, 4, 4, false, "_o4_d4"),
+    DL_VARIANT(128, 64, 32, 64, 32, 3, 0, 3, false, "_d3"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

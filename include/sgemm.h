@@ -150,7 +150,11 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   info[8] LDS bytes per workgroup (0 for the LDS-free variants "mfma32r_", whose BK
  *   is the K span of the loads they keep in flight); when n >= 10, info[9] 64-bit offsets (0/1); when
  *   n >= 11, info[10] the number of k-groups splitting K inside one workgroup (1 = none);
- *   when n >= 13, info[11] and info[12]: the variant reads A, resp. B, transposed (0/1).
+ *   when n >= 13, info[11] and info[12]: the variant reads A, resp. B, transposed (0/1);
+ *   when n >= 14, info[13]: B is loaded four consecutive k at a time and staged with k
+ *   contiguous in LDS (0/1; "_bq" variants, 32-bit loads only); when n >= 15, info[14]:
+ *   the number of LDS stages of a variant that loads its operands straight from global memory
+ *   into LDS (0: loads go through registers; "mfma32l_" variants, 128-bit loads only).
  *   Variants with info[11] or info[12] set serve only sgemm_op / sgemm_op_ex.
  * Returns 0, or -1 for a bad id or n < 9. */
 SGEMM_API int sgemm_variant_info(int variant, int *info, int n);

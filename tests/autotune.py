@@ -240,6 +240,11 @@ def main() -> int:
                     help="instead of tuning: time every variant on this many random shapes and report how far "
                          "the dispatched variant is from the fastest")
     ap.add_argument("--regret-seed", type=int, default=2024)
+    ap.add_argument("--only", default=None,
+                    help="comma-separated name substrings: sweep only the variants whose name contains one "
+                         "(the table's current entries are always swept, so the winner is compared with them)")
+    ap.add_argument("--vec-class", type=int, default=None, choices=[0, 1],
+                    help="run only the cases of this vector-load class (0: unaligned, 1: aligned)")
     args = ap.parse_args()
     if args.table_from:
         with open(args.table_from) as f:
@@ -256,6 +261,12 @@ def main() -> int:
 
     nvar = sg.sgemm_num_variants()
     infos = [sg.sgemm_variant_info(v) for v in range(nvar)]
+    if args.only:
+        keep = set(name for name, _ in read_table().values())
+        subs = [x for x in args.only.split(",") if x]
+        wanted = [info for info in infos if info["name"] in keep or any(x in info["name"] for x in subs)]
+    else:
+        wanted = infos
     stream = torch.cuda.current_stream()
 
     flush = {}
@@ -279,6 +290,8 @@ def main() -> int:
         flops = 2.0 * M * N * K
         log(f"== {label} ({cls}, vec={vec_ok}): M={M} N={N} K={K} alpha={alpha} beta={beta}")
         for v, info in enumerate(infos):
+            if info not in wanted:
+                continue
             if info["vec"] and not vec_ok:
                 continue
             if info["trans_a"] or info["trans_b"]:
@@ -339,6 +352,8 @@ def main() -> int:
     results = []
     for (label, cls, wname, M, N, K, dist, alpha, beta, vec_ok) in CASES:
         if cls not in classes:
+            continue
+        if args.vec_class is not None and int(vec_ok) != args.vec_class:
             continue
         w = WORKLOADS[wname]
         M = M or w.M

@@ -56,6 +56,32 @@ def panel_loads(ROWS, COLS, NT, vec, r0, c0, nrows, ncols, clamp_rows, clamp_col
     return np.concatenate(rows), np.concatenate(cols), W, np.concatenate(ok)
 
 
+def kquad_loads(BK, BN, NT, k0, c0, K, N):
+    """(rows, cols, width, loaded) of every load of one B slab, mirroring KQuadLoader.fetch: thread
+    tid takes column tid % BN (clamped to N - 1) and the k-quads tid // BN + l * NT / BN, four 32-bit
+    loads each; k past K is not loaded.  Also checks that the slab's (k, column) positions are each
+    written to LDS exactly once, inside the [BN][BK + 4] panel."""
+    QPP = NT // BN
+    assert BK % 4 == 0 and NT % BN == 0 and (BK // 4) % QPP == 0
+    L = (BK // 4) * BN // NT
+    tid = np.arange(NT)
+    col, q0 = tid % BN, tid // BN
+    c = np.minimum(c0 + col, N - 1)
+    rows, cols, ok, seen = [], [], [], []
+    for l in range(L):
+        q = q0 + l * QPP
+        assert (q * 4 + 4).max() <= BK and (col * (BK + 4) + q * 4 + 4).max() <= BN * (BK + 4)
+        for t in range(4):
+            k = k0 + 4 * q + t
+            rows.append(k)
+            cols.append(c)
+            ok.append(k < K)
+            seen.append((4 * q + t) * BN + col)
+    seen = np.concatenate(seen)
+    assert np.array_equal(np.sort(seen), np.arange(BK * BN))
+    return np.concatenate(rows), np.concatenate(cols), 1, np.concatenate(ok)
+
+
 def check_loads_in_bounds(v, M, N, K):
     """Loads of every A and B panel stay inside the STORED operand: A is M x K, or K x M when the
     variant reads it transposed (a BK x BM panel whose columns past M are clamped); B is K x N, or
@@ -80,6 +106,9 @@ def check_loads_in_bounds(v, M, N, K):
             if tb:
                 r, c, W, ok = panel_loads(BN, BK, NT, vec, tn * BN, s * BK, N, K, True, False)
                 rows, cols = N, K
+            elif v.get("b_kquad"):
+                r, c, W, ok = kquad_loads(BK, BN, NT, s * BK, tn * BN, K, N)
+                rows, cols = K, N
             else:
                 r, c, W, ok = panel_loads(BK, BN, NT, vec, s * BK, tn * BN, K, N, False, True)
                 rows, cols = K, N
@@ -145,6 +174,8 @@ def is_direct(v):
 def test_loads_in_bounds(v):
     if is_direct(v):
         pytest.skip("covered by test_direct_kernel_loads_in_bounds")
+    if v.get("dl_stages"):
+        pytest.skip("covered by test_dl_kernel_loads_and_fragments")
     for (M, N, K) in SHAPES:
         a_len = M if v["trans_a"] else K   # stored row lengths
         b_len = K if v["trans_b"] else N
@@ -228,3 +259,117 @@ def test_direct_kernel_loads_in_bounds(v):
         rows = np.minimum(np.arange(-(-M // 32) * 32), M - 1)
         cols = np.minimum(np.arange(-(-N // 32) * 32), N - 1)
         assert rows.max() < M and cols.max() < N
+
+
+# ------------------------------------------------------------------------------------------
+# the direct-to-LDS kernel (sgemm_mfma_dl_kernel): swizzled 16-byte loads straight into LDS
+# ------------------------------------------------------------------------------------------
+
+def dl_swz_a(r, qpr):
+    r = np.asarray(r)
+    return ((r & 15) + ((r >> 3) & 1)) & 7 if qpr == 8 else (((r >> 1) & 7) + ((r >> 3) & 1)) & 3
+
+
+def dl_swz_b(k):
+    return ((np.asarray(k) >> 2) & 1) * 8
+
+
+DL = [v for v in VARIANTS if v.get("dl_stages")]
+
+
+def dl_slab_model(v, M, N, K, tm, tn, s):
+    """One slab of one workgroup of sgemm_mfma_dl_kernel, restated: returns the LDS contents of
+    the A and B stages as the global (row, col) each element holds (-1 for a zeroed element past
+    K), after every wave's loads and the tail fix-up.  Asserts every load address is inside the
+    operand."""
+    BM, BN, BK, NT = v["BM"], v["BN"], v["BK"], v["threads"]
+    NW = NT // 64
+    QA, QB = BK // 4, BN // 4
+    LA, LB = BM * BK // 256 // NW, BK * BN // 256 // NW
+    m0, n0, k0 = tm * BM, tn * BN, s * BK
+    tail = k0 + BK > K
+    lane = np.arange(64)
+    a_lds = np.full((BM * BK, 2), -2, dtype=np.int64)
+    b_lds = np.full((BK * BN, 2), -2, dtype=np.int64)
+    for wave in range(NW):
+        for j in range(LA):
+            c = wave * LA + j
+            r = (c * 64 + lane) // QA
+            q = (lane % QA) ^ dl_swz_a(r, QA)
+            row = np.minimum(m0 + r, M - 1)
+            k = k0 + 4 * q
+            kl = np.minimum(k, K - 4) if tail else k
+            assert (row >= 0).all() and (row < M).all() and (kl >= 0).all() and (kl + 4 <= K).all()
+            for e in range(4):
+                pos = (c * 64 + lane) * 4 + e
+                a_lds[pos, 0] = np.where(k < K, row, -1)
+                a_lds[pos, 1] = np.where(k < K, kl + e, -1)
+        for j in range(LB):
+            c = wave * LB + j
+            kr = (c * 64 + lane) // QB
+            nq = (lane % QB) ^ dl_swz_b(kr)
+            n = np.minimum(n0 + 4 * nq, N - 4)
+            k = k0 + kr
+            kl = np.minimum(k, K - 1) if tail else k
+            assert (kl >= 0).all() and (kl < K).all() and (n >= 0).all() and (n + 4 <= N).all()
+            for e in range(4):
+                pos = (c * 64 + lane) * 4 + e
+                b_lds[pos, 0] = np.where(k < K, kl, -1)
+                b_lds[pos, 1] = np.where(k < K, n + e, -1)
+    assert (a_lds >= -1).all() and (b_lds >= -1).all()  # every LDS element written
+    return a_lds, b_lds
+
+
+@pytest.mark.parametrize("v", DL, ids=[v["name"] for v in DL])
+def test_dl_kernel_loads_and_fragments(v):
+    """sgemm_mfma_dl_kernel's loads stay inside A and B (rows past M and columns past N clamped, k
+    of the slab that crosses K clamped), every LDS element of a stage is written, and the fragment
+    read of lane (i, h), block (fi, fj), 8-deep group kk and step t -- at the kernel's swizzled
+    offsets -- returns A(m0 + wm0 + 32 fi + i, k) and B(k, n0 + wn0 + 32 fj + i) with
+    k = k0 + 8 kk + 4 h + t (rows/columns clamped at the edges), or a zero past K."""
+    BM, BN, BK, NT = v["BM"], v["BN"], v["BK"], v["threads"]
+    WM, WN = v["WM_or_TM"], v["WN_or_TN"]
+    waves_n = BN // WN
+    QA = BK // 4
+    lane = np.arange(64)
+    li, lh = lane % 32, lane // 32
+    for (M, N, K) in [(64, 64, 32), (200, 136, 100), (131, 68, 36), (257, 260, 8), (1, 4, 4)]:
+        if N % 4 or K % 4:
+            continue
+        tiles_m, tiles_n = -(-M // BM), -(-N // BN)
+        for tm in {0, tiles_m - 1}:
+            for tn in {0, tiles_n - 1}:
+                for s in range(-(-K // BK)):
+                    a_lds, b_lds = dl_slab_model(v, M, N, K, tm, tn, s)
+                    k0 = s * BK
+                    for wave in range(NT // 64):
+                        wm0, wn0 = (wave // waves_n) * WM, (wave % waves_n) * WN
+                        for kk in range(BK // 8):
+                            a_frag = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a(wm0 + li, QA))
+                            for fi in range(WM // 32):
+                                for t in range(4):
+                                    got = a_lds[a_frag + fi * 32 * BK + t]
+                                    k = k0 + 8 * kk + 4 * lh + t
+                                    row = np.minimum(tm * BM + wm0 + 32 * fi + li, M - 1)
+                                    want_r = np.where(k < K, row, -1)
+                                    want_k = np.where(k < K, k, -1)
+                                    assert (got[:, 0] == want_r).all() and (got[:, 1] == want_k).all()
+                            for fj in range(WN // 32):
+                                b_frag = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh))
+                                for t in range(4):
+                                    got = b_lds[b_frag + (8 * kk + t) * BN]
+                                    k = k0 + 8 * kk + 4 * lh + t
+                                    col = np.minimum(tn * BN + wn0 + 32 * fj + li, N - 1)
+                                    # B columns are clamped by 4-column groups: the last group of N
+                                    ok = (got[:, 1] == col) | ((col == N - 1) & (got[:, 1] >= N - 4)) | \
+                                         ((tn * BN + wn0 + 32 * fj + li >= N) & (got[:, 1] >= N - 4))
+                                    assert (np.where(k < K, ok, got[:, 1] == -1)).all()
+                                    assert (got[:, 0] == np.where(k < K, k, -1)).all()
+
+
+def test_dl_swizzles_are_row_permutations():
+    for qpr in (4, 8):
+        for r in range(64):
+            assert sorted((np.arange(qpr) ^ dl_swz_a(r, qpr)).tolist()) == list(range(qpr))
+    for k in range(64):
+        assert sorted((np.arange(16) ^ dl_swz_b(k)).tolist()) == list(range(16))
