@@ -267,6 +267,8 @@ def test_direct_kernel_loads_in_bounds(v):
 
 def dl_swz_a(r, qpr):
     r = np.asarray(r)
+    if qpr == 16:
+        return r & 15
     return ((r & 15) + ((r >> 3) & 1)) & 7 if qpr == 8 else (((r >> 1) & 7) + ((r >> 3) & 1)) & 3
 
 
@@ -281,11 +283,13 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
     """One slab of one workgroup of sgemm_mfma_dl_kernel, restated: returns the LDS contents of
     the A and B stages as the global (row, col) each element holds (-1 for a zeroed element past
     K), after every wave's loads and the tail fix-up.  Asserts every load address is inside the
-    operand."""
+    operand.  128-bit variants load W = 16 bytes per lane (a quad), 32-bit ones W = 4."""
     BM, BN, BK, NT = v["BM"], v["BN"], v["BK"], v["threads"]
     NW = NT // 64
-    QA, QB = BK // 4, BN // 4
-    LA, LB = BM * BK // 256 // NW, BK * BN // 256 // NW
+    E = 4 if v["vec"] else 1          # floats per lane load
+    CH = 64 * E                       # floats one wave's load fills
+    QA = BK // 4
+    LA, LB = BM * BK // CH // NW, BK * BN // CH // NW
     m0, n0, k0 = tm * BM, tn * BN, s * BK
     tail = k0 + BK > K
     lane = np.arange(64)
@@ -293,29 +297,28 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
     b_lds = np.full((BK * BN, 2), -2, dtype=np.int64)
     for wave in range(NW):
         for j in range(LA):
-            c = wave * LA + j
-            r = (c * 64 + lane) // QA
-            q = (lane % QA) ^ dl_swz_a(r, QA)
+            f = (wave * LA + j) * CH + E * lane
+            r = f // BK
+            u = (f % BK) // 4
+            kin = 4 * (u ^ dl_swz_a(r, QA)) + f % 4
             row = np.minimum(m0 + r, M - 1)
-            k = k0 + 4 * q
-            kl = np.minimum(k, K - 4) if tail else k
-            assert (row >= 0).all() and (row < M).all() and (kl >= 0).all() and (kl + 4 <= K).all()
-            for e in range(4):
-                pos = (c * 64 + lane) * 4 + e
-                a_lds[pos, 0] = np.where(k < K, row, -1)
-                a_lds[pos, 1] = np.where(k < K, kl + e, -1)
+            k = k0 + kin
+            kl = np.minimum(k, K - E) if tail else k
+            assert (row >= 0).all() and (row < M).all() and (kl >= 0).all() and (kl + E <= K).all()
+            for e in range(E):
+                a_lds[f + e, 0] = np.where(k < K, row, -1)
+                a_lds[f + e, 1] = np.where(k < K, kl + e, -1)
         for j in range(LB):
-            c = wave * LB + j
-            kr = (c * 64 + lane) // QB
-            nq = (lane % QB) ^ dl_swz_b(kr)
-            n = np.minimum(n0 + 4 * nq, N - 4)
+            f = (wave * LB + j) * CH + E * lane
+            kr = f // BN
+            u = (f % BN) // 4
+            n = np.minimum(n0 + 4 * (u ^ dl_swz_b(kr)) + f % 4, N - E)
             k = k0 + kr
             kl = np.minimum(k, K - 1) if tail else k
-            assert (kl >= 0).all() and (kl < K).all() and (n >= 0).all() and (n + 4 <= N).all()
-            for e in range(4):
-                pos = (c * 64 + lane) * 4 + e
-                b_lds[pos, 0] = np.where(k < K, kl, -1)
-                b_lds[pos, 1] = np.where(k < K, n + e, -1)
+            assert (kl >= 0).all() and (kl < K).all() and (n >= 0).all() and (n + E <= N).all()
+            for e in range(E):
+                b_lds[f + e, 0] = np.where(k < K, kl, -1)
+                b_lds[f + e, 1] = np.where(k < K, n + e, -1)
     assert (a_lds >= -1).all() and (b_lds >= -1).all()  # every LDS element written
     return a_lds, b_lds
 
@@ -333,8 +336,9 @@ def test_dl_kernel_loads_and_fragments(v):
     QA = BK // 4
     lane = np.arange(64)
     li, lh = lane % 32, lane // 32
-    for (M, N, K) in [(64, 64, 32), (200, 136, 100), (131, 68, 36), (257, 260, 8), (1, 4, 4)]:
-        if N % 4 or K % 4:
+    for (M, N, K) in [(64, 64, 32), (200, 136, 100), (131, 68, 36), (257, 260, 8), (1, 4, 4), (70, 67, 37),
+                      (3, 130, 1), (129, 65, 130)]:
+        if v["vec"] and (N % 4 or K % 4):
             continue
         tiles_m, tiles_n = -(-M // BM), -(-N // BN)
         for tm in {0, tiles_m - 1}:
@@ -360,15 +364,16 @@ def test_dl_kernel_loads_and_fragments(v):
                                     got = b_lds[b_frag + (8 * kk + t) * BN]
                                     k = k0 + 8 * kk + 4 * lh + t
                                     col = np.minimum(tn * BN + wn0 + 32 * fj + li, N - 1)
-                                    # B columns are clamped by 4-column groups: the last group of N
-                                    ok = (got[:, 1] == col) | ((col == N - 1) & (got[:, 1] >= N - 4)) | \
+                                    # columns past N read a clamped column of the last 4-column
+                                    # group (128-bit loads) or column N - 1 (32-bit loads)
+                                    ok = (got[:, 1] == col) | \
                                          ((tn * BN + wn0 + 32 * fj + li >= N) & (got[:, 1] >= N - 4))
                                     assert (np.where(k < K, ok, got[:, 1] == -1)).all()
                                     assert (got[:, 0] == np.where(k < K, k, -1)).all()
 
 
 def test_dl_swizzles_are_row_permutations():
-    for qpr in (4, 8):
+    for qpr in (4, 8, 16):
         for r in range(64):
             assert sorted((np.arange(qpr) ^ dl_swz_a(r, qpr)).tolist()) == list(range(qpr))
     for k in range(64):
