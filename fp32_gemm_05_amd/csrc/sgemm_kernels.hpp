@@ -1444,6 +1444,15 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             }
         }
     };
+    // Load q (0 .. LPW - 1) of whole slab s: the A loads, then the B loads.
+    auto issue_one = [&](int s, int q) {
+        const int st = s % STAGES, k0 = s * BK;
+        if (q < LA)
+            dl_load<W>(a_tile + k0, a_off[q], lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH));
+        else
+            dl_load<W>(b_tile + (long)k0 * ldb, b_off[q - LA],
+                       lds_addr(lds_b + st * Cfg::B_STAGE + (wave * LB + q - LA) * CH));
+    };
     // After the loads of the slab that crosses K have landed: zero what lies past K (each wave
     // the elements its own loads wrote; with W = 16, K % 4 == 0 makes a quad wholly in or out).
     auto fix_tail = [&](int s) {
@@ -1533,20 +1542,39 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 
     // Slab s (stage ST = s % STAGES when known at compile time, else -1).  FULL: slab s + D exists
     // and is whole, so the wait before the next barrier leaves exactly D - 1 slabs in flight.
+    // SPREAD (whole slabs, rings of three or more stages): the requests for slab s + D are issued
+    // LPG at a time after each 8-deep group's MFMAs instead of all at the top of the slab, so that
+    // they issue in the matrix pipe's shadow (per-wave timestamps at 1024^3, one wave per SIMD:
+    // 1103 against 1169 cycles per 16-MFMA slab).  With two stages a slab's requests must land
+    // within the slab itself, and issuing them later costs more than it saves.
+    constexpr bool SPREAD = D >= 2 && KK > 1;
+    constexpr int LPG = (Cfg::LPW + KK - 1) / KK;
     auto slab = [&](int s, auto stage, auto full) {
         constexpr int STC = decltype(stage)::value;
         constexpr bool FULL = decltype(full)::value;
+        constexpr bool SP = SPREAD && FULL;
         const int st = STC >= 0 ? STC : s % STAGES;
-        if (FULL || s + D < nfull)
-            issue(s + D, Whole{});
-        else if (s + D < nslab)
-            issue(s + D, Tail{});
+        if (!SP) {
+            if (FULL || s + D < nfull)
+                issue(s + D, Whole{});
+            else if (s + D < nslab)
+                issue(s + D, Tail{});
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
             read_frag(F[(kk + 1) & 1], st, kk + 1);
             __builtin_amdgcn_sched_barrier(0);
             mfma_frag(F[kk & 1]);
+            if (SP) {
+#pragma unroll
+                for (int q = kk * LPG; q < (kk + 1) * LPG && q < Cfg::LPW; ++q) issue_one(s + D, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (SP) {
+#pragma unroll
+            for (int q = (KK - 1) * LPG; q < Cfg::LPW; ++q) issue_one(s + D, q);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (FULL || s + 1 < nslab) {
