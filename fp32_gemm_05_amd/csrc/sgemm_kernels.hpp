@@ -1363,7 +1363,8 @@ __device__ __attribute__((always_inline)) inline uint32_t lds_addr(const float* 
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)(p);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
+          bool SPREAD = false>
 __global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -1544,15 +1545,16 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     // and is whole, so the wait before the next barrier leaves exactly D - 1 slabs in flight.
     // SPREAD (whole slabs, rings of three or more stages): the requests for slab s + D are issued
     // LPG at a time after each 8-deep group's MFMAs instead of all at the top of the slab, so that
-    // they issue in the matrix pipe's shadow (per-wave timestamps at 1024^3, one wave per SIMD:
-    // 1103 against 1169 cycles per 16-MFMA slab).  With two stages a slab's requests must land
-    // within the slab itself, and issuing them later costs more than it saves.
-    constexpr bool SPREAD = D >= 2 && KK > 1;
+    // they issue in the matrix pipe's shadow.  It pays at one wave per SIMD on L2-resident operands
+    // (per-wave timestamps at 1024^3: 1103 against 1169 cycles per 16-MFMA slab), and costs where
+    // the last requests, issued at the end of the slab, then have one slab instead of two to land
+    // (three-stage 128x128 tiles at 4096^3: 1120 against 922 us), so it is a variant of its own.
+    constexpr bool SP_ON = SPREAD && D >= 2 && KK > 1;
     constexpr int LPG = (Cfg::LPW + KK - 1) / KK;
     auto slab = [&](int s, auto stage, auto full) {
         constexpr int STC = decltype(stage)::value;
         constexpr bool FULL = decltype(full)::value;
-        constexpr bool SP = SPREAD && FULL;
+        constexpr bool SP = SP_ON && FULL;
         const int st = STC >= 0 ? STC : s % STAGES;
         if (!SP) {
             if (FULL || s + D < nfull)

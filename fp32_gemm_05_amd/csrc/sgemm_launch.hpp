@@ -104,10 +104,11 @@ hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
                            stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
+          bool SPREAD = false>
 hipError_t launch_mfma_dl(const GemmArgs& g, hipStream_t stream) {
     using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
-    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE>;
+    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SPREAD>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -256,15 +257,20 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 #define DEEP_NAME(BM, BN, BK, WM, WN) "mfma32d_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN
 // operands loaded straight into a ring of STAGES LDS buffers ("mfma32l_"): 128-bit loads ("_vec")
 // or 32-bit loads ("_scalar")
-#define DL_ROW(BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, NAME)                                     \
+#define DL_ROW(BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SP, NAME)                                 \
     {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT, W == 16,                  \
-     DlCfg<BM, BN, BK, WM, WN, STAGES, W>::LDS_BYTES, &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE>, \
-     0, 0, 0, 0, 0, STAGES}
+     DlCfg<BM, BN, BK, WM, WN, STAGES, W>::LDS_BYTES,                                                     \
+     &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SP>, 0, 0, 0, 0, 0, STAGES}
 #define DL_NAME(BM, BN, BK, WM, WN, STAGES) "mfma32l_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #STAGES
 #define DL_VARIANT(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
-    DL_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, FAIR, CPRE, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_vec")
+    DL_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, FAIR, CPRE, false, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_vec")
 #define DL_SCALAR(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
-    DL_ROW(BM, BN, BK, WM, WN, STAGES, 4, OCC, FAIR, CPRE, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_scalar")
+    DL_ROW(BM, BN, BK, WM, WN, STAGES, 4, OCC, FAIR, CPRE, false, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_scalar")
+// the same with the next slab's requests spread over the slab's 8-deep groups ("_sp")
+#define DL_SP_VARIANT(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
+    DL_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, FAIR, CPRE, true, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_sp_vec")
+#define DL_SP_SCALAR(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
+    DL_ROW(BM, BN, BK, WM, WN, STAGES, 4, OCC, FAIR, CPRE, true, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_sp_scalar")
 #define BOTH_DEEP(BM, BN, BK, WM, WN)                                                        \
     DEEP_VARIANT(BM, BN, BK, WM, WN, true, DEEP_NAME(BM, BN, BK, WM, WN) "_vec"),            \
         DEEP_VARIANT(BM, BN, BK, WM, WN, false, DEEP_NAME(BM, BN, BK, WM, WN) "_scalar")
@@ -388,5 +394,13 @@ const Variant kVariants[] = {
     DL_SCALAR(64, 64, 32, 32, 32, 3, 0, 3, false, "_d3"),
     DL_SCALAR(64, 64, 16, 32, 32, 2, 0, 0, false, ""),
     DL_SCALAR(128, 128, 16, 64, 64, 3, 0, 4, false, "_d4"),
+    DL_SP_VARIANT(64, 64, 32, 32, 32, 3, 0, 0, true, "_cp"),
+    DL_SP_VARIANT(64, 64, 32, 32, 32, 3, 0, 0, false, ""),
+    DL_SP_VARIANT(64, 64, 32, 32, 32, 4, 0, 0, true, "_cp"),
+    DL_SP_VARIANT(64, 64, 32, 32, 32, 3, 0, 3, false, "_d3"),
+    DL_SP_VARIANT(128, 128, 16, 64, 64, 4, 0, 3, false, "_d3"),
+    DL_SP_VARIANT(128, 64, 32, 64, 32, 3, 0, 3, false, "_d3"),
+    DL_SP_SCALAR(64, 64, 16, 32, 32, 3, 0, 0, false, ""),
+    DL_SP_SCALAR(64, 64, 32, 32, 32, 3, 0, 3, false, "_d3"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
