@@ -9,7 +9,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsgemm.so")
 SOURCES = [os.path.join(CSRC, "sgemm.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("sgemm_kernels.hpp", "sgemm_launch.hpp", "tuned_table.inc")] + [
+KERNEL_HEADERS = ("kernel_common.hpp", "kernel_mfma.hpp", "kernel_pipe.hpp", "kernel_deep.hpp", "kernel_splitk.hpp",
+                  "kernel_direct.hpp", "kernel_dl.hpp", "kernel_valu.hpp")
+DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("sgemm_kernels.hpp", "sgemm_launch.hpp", "tuned_table.inc")
+                     + KERNEL_HEADERS] + [
     os.path.join(os.path.dirname(HERE), "include", "sgemm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,382 @@
+// kernel_dl.hpp -- the direct-to-LDS MFMA kernel (global_load_lds into a ring of LDS stages).
+#pragma once
+
+#include "kernel_common.hpp"
+
+namespace libsgemm {
+
+// ---------------------------------------------------------------------------------
+// Direct-to-LDS MFMA kernel: the operand slabs go from global memory straight into LDS with
+// gfx950's global_load_lds (each lane's W bytes land at the wave's LDS base + W x lane; W = 16
+// with global_load_lds_dwordx4 for 16-byte aligned rows, W = 4 with global_load_lds_dword
+// otherwise), so no register holds a prefetched slab and no LDS store instruction runs in the K
+// loop -- the stores that, at one wave per SIMD, take issue cycles and VGPR read bandwidth from
+// the matrix pipe.  STAGES LDS buffers form a ring: slab s + STAGES - 1 is requested right after
+// the barrier that opens slab s, into the buffer every wave finished reading before that
+// barrier, so a slab has STAGES - 1 slabs of MFMAs to arrive.  One barrier per slab; before it,
+// each wave waits (s_waitcnt vmcnt) only for its own loads of the next slab, leaving later slabs
+// in flight.
+//
+// Layout: a wave's load fills 64 W bytes of LDS contiguously, so the slabs are unpadded -- A as
+// [BM][BK] (k contiguous), B as [BK][BN] (n contiguous) -- and bank conflicts of the fragment
+// reads are avoided by choosing WHICH 16-byte quad of its row a lane (W = 16) or a group of four
+// lanes (W = 4) fetches: the quad at LDS position u of row r holds global quad u ^ swz(r) (an XOR
+// swizzle, a permutation within the row, so the loads of a row still cover the same cache lines).
+// The swizzles make the 128-bit A reads (16 consecutive rows at one quad) and the 32-bit B reads
+// (rows k and k + 4 at 32 consecutive columns) free of conflicts both with 64 banks and 16 lanes
+// per pass and with 32 banks and 8 lanes per pass.
+//
+// Edges: rows of A past M and columns of B past N are clamped (they feed C elements that are never
+// stored).  The slab that crosses K is loaded with k clamped into range, so every address lies
+// inside the operand, and each wave then overwrites what it loaded past K with zeros, after its
+// loads have landed and before the barrier.  W = 16 needs the 128-bit variants' precondition
+// (16-byte aligned rows; K and N multiples of 4).
+// ---------------------------------------------------------------------------------
+template <int QPR>
+__device__ __host__ inline int dl_swz_a(int r) {  // swizzle of A row r (QPR quads per row)
+    static_assert(QPR == 4 || QPR == 8 || QPR == 16, "A rows of 16, 32 or 64 floats");
+    return QPR == 16 ? r & 15
+                     : QPR == 8 ? ((r & 15) + ((r >> 3) & 1)) & 7 : (((r >> 1) & 7) + ((r >> 3) & 1)) & 3;
+}
+__device__ __host__ inline int dl_swz_b(int k) { return ((k >> 2) & 1) * 8; }  // swizzle of B row k, in quads
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W = 16>
+struct DlCfg {
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int QPR_A = BK / 4, QPR_B = BN / 4;           // 16-byte quads per row
+    static constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;     // floats
+    static constexpr int CH = 16 * W;                              // floats one wave's load fills
+    static constexpr int LA = A_STAGE / CH / NW, LB = B_STAGE / CH / NW;  // loads per wave and slab
+    static constexpr int LPW = LA + LB;
+    static constexpr int D = STAGES - 1;                           // slabs in flight ahead
+    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 4;
+    static_assert(W == 4 || W == 16, "32-bit or 128-bit loads");
+    static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+    static_assert(A_STAGE % (CH * NW) == 0 && B_STAGE % (CH * NW) == 0, "whole loads per wave");
+    static_assert(BN % 64 == 0, "the B swizzle needs rows of 16 quads or more");
+    static_assert(BK % 8 == 0 && BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiling");
+    static_assert(LPW * D < 64, "vmcnt counts at most 63 loads in flight");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+// The direct loads, their waits and the barrier are inline asm.  Issued through the compiler
+// builtin, a load into LDS makes the compiler wait for it (s_waitcnt vmcnt(0)) before every later
+// LDS read it cannot tell apart from the loaded stage -- here every fragment read -- which would
+// expose the full load latency in every slab.  As asm with a memory clobber, the compiler neither
+// waits for these loads nor moves LDS accesses across them, the barrier or the waits; the kernel
+// waits for them itself.  Its own waits for other loads stay correct: counting fewer loads in
+// flight than there are only makes a vmcnt wait stricter.  The loads have no register results.
+// M0 holds the LDS address (M0 is reserved to the compiler, so the asm restores it); the s_nop
+// covers the wait state between an SALU write of M0 and the load that reads it.
+template <int W>
+__device__ __attribute__((always_inline)) inline void dl_load(const void* base, uint32_t off, uint32_t lds) {
+    uint32_t keep;
+    if (W == 16)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(off), "s"(base)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(off), "s"(base)
+            : "memory");
+}
+template <int W>
+__device__ __attribute__((always_inline)) inline void dl_load_at(const void* p, uint32_t lds) {
+    uint32_t keep;
+    if (W == 16)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(p)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(p)
+            : "memory");
+}
+// Wait until at most N of this wave's vector-memory loads are in flight and all its LDS accesses
+// are done.
+template <int N>
+__device__ __attribute__((always_inline)) inline void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"i"(N) : "memory");
+}
+// The same with N = n * PER chosen at run time (n = 0 .. 3 slabs of PER loads each).
+template <int PER>
+__device__ __attribute__((always_inline)) inline void wait_slabs(int n) {
+    if (n <= 0)
+        wait_vm_lgkm0<0>();
+    else if (n == 1)
+        wait_vm_lgkm0<PER>();
+    else if (n == 2)
+        wait_vm_lgkm0<(2 * PER < 64 ? 2 * PER : 63)>();
+    else
+        wait_vm_lgkm0<(3 * PER < 64 ? 3 * PER : 63)>();
+}
+__device__ __attribute__((always_inline)) inline void dl_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The LDS address of a pointer into a __shared__ array.
+__device__ __attribute__((always_inline)) inline uint32_t lds_addr(const float* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)(p);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
+          bool SPREAD = false>
+__global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT))
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
+sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / 8, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
+    constexpr int QA = Cfg::QPR_A, QB = Cfg::QPR_B, CH = Cfg::CH, E = W / 4;  // E: floats per lane load
+    constexpr bool VEC = W == 16;
+    static_assert(KK % 2 == 0 || KK == 1, "fragment buffers alternate per 8-deep group");
+    __shared__ __attribute__((aligned(1024))) float lds_a[STAGES * Cfg::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) float lds_b[STAGES * Cfg::B_STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / Cfg::WAVES_N) * WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+    const int M = g.M, N = g.N, K = g.K;
+    const long lda = g.lda, ldb = g.ldb;
+
+    // This lane's loads: load j of the wave fills floats [c CH, (c + 1) CH) of the slab,
+    // c = wave * L + j; the lane's E floats start at float f = c CH + E lane, i.e. row f / (row
+    // length), LDS quad u = (f % row length) / 4, element f % 4 of it, which holds global quad
+    // u ^ swz(row).
+    // The k of a lane's load j inside the slab (recomputed where needed: only the slab that
+    // crosses K uses it, and keeping it live would cost registers throughout the loop).
+    auto a_kin = [&](int j) {
+        const int f = (wave * LA + j) * CH + E * lane;
+        return 4 * (((f % BK) / 4) ^ dl_swz_a<QA>(f / BK)) + f % 4;
+    };
+    auto b_kin = [&](int j) { return ((wave * LB + j) * CH + E * lane) / BN; };
+    uint32_t a_off[LA], b_off[LB];  // byte offsets from the slab's first element
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int f = (wave * LA + j) * CH + E * lane;
+        const int row = imin(m0 + f / BK, M - 1) - m0;
+        a_off[j] = (uint32_t)(((long)row * lda + a_kin(j)) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int f = (wave * LB + j) * CH + E * lane;
+        const int k = f / BN, u = (f % BN) / 4;
+        const int n = imin(n0 + 4 * (u ^ dl_swz_b(k)) + f % 4, N - E) - n0;
+        b_off[j] = (uint32_t)(((long)k * ldb + n) * 4);
+    }
+    const float* a_tile = g.A + (long)m0 * lda;  // A(m0, 0)
+    const float* b_tile = g.B + n0;              // B(0, n0)
+
+    // Request slab s into its stage.  TAIL: the slab crosses K; k is clamped into range here (the
+    // address moves from k0 + k to min(k0 + k, K - E) for A, to row min(k0 + k, K - 1) for B) and
+    // what lies past K is zeroed by fix_tail once the loads have landed.
+    auto issue = [&](int s, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        const int st = s % STAGES, k0 = s * BK;
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            if (!TAIL) {
+                dl_load<W>(a_tile + k0, a_off[j], lds_addr(sa + j * CH));
+            } else {
+                const int k = a_kin(j);
+                dl_load_at<W>(reinterpret_cast<const char*>(a_tile) + a_off[j] + 4L * (imin(k0 + k, K - E) - k),
+                              lds_addr(sa + j * CH));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+            if (!TAIL) {
+                dl_load<W>(b_tile + (long)k0 * ldb, b_off[j], lds_addr(sb + j * CH));
+            } else {
+                const int k = b_kin(j);
+                dl_load_at<W>(reinterpret_cast<const char*>(b_tile) + b_off[j] + 4L * (imin(k0 + k, K - 1) - k) * ldb,
+                              lds_addr(sb + j * CH));
+            }
+        }
+    };
+    // Load q (0 .. LPW - 1) of whole slab s: the A loads, then the B loads.
+    auto issue_one = [&](int s, int q) {
+        const int st = s % STAGES, k0 = s * BK;
+        if (q < LA)
+            dl_load<W>(a_tile + k0, a_off[q], lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH));
+        else
+            dl_load<W>(b_tile + (long)k0 * ldb, b_off[q - LA],
+                       lds_addr(lds_b + st * Cfg::B_STAGE + (wave * LB + q - LA) * CH));
+    };
+    // After the loads of the slab that crosses K have landed: zero what lies past K (each wave
+    // the elements its own loads wrote; with W = 16, K % 4 == 0 makes a quad wholly in or out).
+    auto fix_tail = [&](int s) {
+        const int st = s % STAGES, k0 = s * BK;
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            if (k0 + a_kin(j) >= K) {
+                if (VEC)
+                    *reinterpret_cast<f32x4*>(sa + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+                else
+                    sa[j * CH + lane] = 0.f;
+            }
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            if (k0 + b_kin(j) >= K) {
+                if (VEC)
+                    *reinterpret_cast<f32x4*>(sb + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+                else
+                    sb[j * CH + lane] = 0.f;
+            }
+    };
+
+    // Fragment reads: A's quad 2 kk + h of row wm0 + 32 fi + li sits at quad ((2 kk + h) ^ swz) of
+    // that row (the swizzle depends on the row's low four bits only, so not on fi); B's element
+    // (k, n) with k = 8 kk + 4 h + t sits at column n ^ 32 h of row k (the B swizzle flips quad bit
+    // 3, i.e. column bit 5, on rows with bit 2 set).
+    int a_frag[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        a_frag[kk] = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
+    int b_frag[FN];
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh));
+    auto read_frag = [&](MfmaFrag<FM, FN>& f, int st, int kk) {
+        const float* sa = lds_a + st * Cfg::A_STAGE;
+        const float* sb = lds_b + st * Cfg::B_STAGE;
+#pragma unroll
+        for (int fi = 0; fi < FM; ++fi)
+            f.a[fi] = *reinterpret_cast<const f32x4*>(sa + a_frag[kk] + fi * 32 * BK);
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (8 * kk + t) * BN];
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
+    };
+
+    const int nslab = (K + BK - 1) / BK;
+    const int nfull = K / BK;
+    using Tail = std::integral_constant<bool, true>;
+    using Whole = std::integral_constant<bool, false>;
+    // the C values of the beta term first: the oldest loads, consumed only by the epilogue
+    f32x16 cv[FM][FN];
+    if (CPRE && g.beta != 0.f) mfma_load_c<FM, FN, VEC>(M, N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
+    // prologue: slabs 0 .. D-1 requested; wait for slab 0 (the later ones may stay in flight)
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        if (s < nfull)
+            issue(s, Whole{});
+        else if (s < nslab)
+            issue(s, Tail{});
+    }
+    wait_slabs<Cfg::LPW>(imin(D, nslab) - 1);
+    if (nfull == 0) {
+        fix_tail(0);
+        wait_vm_lgkm0<0>();
+    }
+    dl_barrier();
+    MfmaFrag<FM, FN> F[2];
+    read_frag(F[0], 0, 0);
+
+    // Slab s (stage ST = s % STAGES when known at compile time, else -1).  FULL: slab s + D exists
+    // and is whole, so the wait before the next barrier leaves exactly D - 1 slabs in flight.
+    // SPREAD (whole slabs, rings of three or more stages): the requests for slab s + D are issued
+    // LPG at a time after each 8-deep group's MFMAs instead of all at the top of the slab, so that
+    // they issue in the matrix pipe's shadow.  It pays at one wave per SIMD on L2-resident operands
+    // (per-wave timestamps at 1024^3: 1103 against 1169 cycles per 16-MFMA slab), and costs where
+    // the last requests, issued at the end of the slab, then have one slab instead of two to land
+    // (three-stage 128x128 tiles at 4096^3: 1120 against 922 us), so it is a variant of its own.
+    constexpr bool SP_ON = SPREAD && D >= 2 && KK > 1;
+    constexpr int LPG = (Cfg::LPW + KK - 1) / KK;
+    auto slab = [&](int s, auto stage, auto full) {
+        constexpr int STC = decltype(stage)::value;
+        constexpr bool FULL = decltype(full)::value;
+        constexpr bool SP = SP_ON && FULL;
+        const int st = STC >= 0 ? STC : s % STAGES;
+        if (!SP) {
+            if (FULL || s + D < nfull)
+                issue(s + D, Whole{});
+            else if (s + D < nslab)
+                issue(s + D, Tail{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            read_frag(F[(kk + 1) & 1], st, kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frag(F[kk & 1]);
+            if (SP) {
+#pragma unroll
+                for (int q = kk * LPG; q < (kk + 1) * LPG && q < Cfg::LPW; ++q) issue_one(s + D, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (SP) {
+#pragma unroll
+            for (int q = (KK - 1) * LPG; q < Cfg::LPW; ++q) issue_one(s + D, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (FULL || s + 1 < nslab) {
+            // slabs requested after slab s + 1: s + 2 .. min(s + D, nslab - 1)
+            if (FULL) {
+                wait_vm_lgkm0<Cfg::LPW * (D - 1)>();
+            } else {
+                wait_slabs<Cfg::LPW>(imin(s + D, nslab - 1) - (s + 1));
+                if (s + 1 >= nfull) {
+                    fix_tail(s + 1);
+                    wait_vm_lgkm0<0>();
+                }
+            }
+            dl_barrier();
+            read_frag(F[0], STC >= 0 ? (STC + 1) % STAGES : (s + 1) % STAGES, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_frag(F[(KK - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Checked = std::integral_constant<bool, false>;
+    DrainPhases drain;
+    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
+    int s = 0;
+    // STAGES slabs per trip, so that every stage offset is a constant
+    for (; s + STAGES - 1 + D < nfull; s += STAGES) {
+        if (FAIR > 0) drain.step(s);
+        slab(s, std::integral_constant<int, 0>{}, Full{});
+        slab(s + 1, std::integral_constant<int, 1>{}, Full{});
+        if (STAGES > 2) slab(s + 2, std::integral_constant<int, 2 % STAGES>{}, Full{});
+        if (STAGES > 3) slab(s + 3, std::integral_constant<int, 3 % STAGES>{}, Full{});
+    }
+    for (; s < nslab; ++s) slab(s, std::integral_constant<int, -1>{}, Checked{});
+
+    mfma_epilogue<FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
+}
+
+}  // namespace libsgemm

@@ -1,1758 +1,21 @@
-// sgemm_kernels.hpp -- HIP kernels of libsgemm for gfx950 (CDNA4, wave64).
+// sgemm_kernels.hpp -- the HIP kernels of libsgemm for gfx950, one header per kernel family.
 //
-// Every kernel computes C := alpha*A*B + beta*C on row-major fp32 matrices with
-// leading dimensions (the operation of "SGEMM CUDA kernel (First Half)",
-// introduction).  One workgroup owns one BM x BN tile of C and walks K in
-// BK-deep slabs, staging a BM x BK slab of A and a BK x BN slab of B in LDS
-// (the shared-memory tiling of "Shared Memory and Register Blocking", CUDA
-// Handbook ch. 17).  What is MI355X-specific:
-//
-//   * two LDS stages: slab s+1 is fetched from global memory into registers
-//     while slab s is multiplied out of LDS, then written to the other stage,
-//     so each slab costs one workgroup barrier instead of two;
-//   * the MFMA family multiplies with v_mfma_f32_32x32x2_f32: a wave owns a
-//     WM x WN sub-tile made of 32x32 blocks (the warp tiling of "Optimizing
-//     Matrix Multiplication in CUDA", section "Warp Tiling", re-cut for 64-lane
-//     waves and matrix cores);
-//   * the VALU family keeps a TM x TN register microtile per lane (the outer
-//     product of "SGEMM CUDA kernel (First Half)", "Part 4", and Figure 17-3 of
-//     the handbook) with A stored k-major in LDS (the transposed slab of "Part
-//     5: Reduced bank conflict (v3)");
-//   * global loads are 128-bit (the float4 loads of "Part 6: Vectorized load
-//     (v4)") when every row is 16-byte aligned, otherwise 32-bit; in both the
-//     lane-fastest index walks contiguous memory (the coalescing of "Global
-//     Memory Coalescing");
-//   * the workgroup -> tile map is XCD-aware: consecutive workgroup ids are
-//     spread round-robin over the 8 XCDs, so each XCD is handed a contiguous
-//     range of tiles, ordered in groups of rows so that tiles running at the
-//     same time share A rows and B columns in that XCD's L2.
-//
-// Edge handling (out-of-range slab elements are zero, stores are guarded, as
-// in the pages' bounds-checked kernels): A rows past M and B columns past N
-// are clamped to the last valid row/column -- they only feed accumulators of C
-// elements that are never stored -- while slab elements past K are zero, so
-// that they add nothing (and no NaN) to valid outputs.
+// kernel_common.hpp  shared pieces: argument block, workgroup -> tile map, slab loaders, MFMA step,
+//                    epilogue, drain ordering, and the beta * C scale kernel;
+// kernel_mfma.hpp    plain MFMA kernel (two LDS stages, register prefetch);
+// kernel_pipe.hpp    the same with double-buffered LDS -> register fragments;
+// kernel_deep.hpp    deep prefetch for about one workgroup per CU;
+// kernel_splitk.hpp  in-workgroup split-K;
+// kernel_direct.hpp  LDS-free kernel of small grids;
+// kernel_dl.hpp      direct global -> LDS loads into a ring of LDS stages;
+// kernel_valu.hpp    vector-FMA register microtile.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
-
-namespace libsgemm {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-struct GemmArgs {
-    int M, N, K;
-    float alpha, beta;
-    const float* A;
-    long lda;
-    const float* B;
-    long ldb;
-    float* C;
-    long ldc;
-    int drain_from;  // first workgroup of the grid's last round (no workgroup starts after it)
-};
-
-constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
-
-// Workgroup id -> (tile_m, tile_n).  A bijection of [0, tiles_m*tiles_n).
-__host__ __device__ inline void tile_of(int wg, int nwg, int tiles_m, int tiles_n, int group_m,
-                                        int& tm, int& tn) {
-    // (1) the hardware hands workgroup w to XCD w % 8; renumber so that XCD x
-    //     gets the contiguous range [start_x, start_x + count_x).
-    const int q = nwg / kNumXcd, r = nwg % kNumXcd;
-    const int x = wg % kNumXcd, p = wg / kNumXcd;
-    const int t = x * q + (x < r ? x : r) + p;
-    // (2) grouped order: blocks of group_m tile-rows, swept column by column.
-    const int per_group = group_m * tiles_n;
-    const int g = t / per_group;
-    const int first_m = g * group_m;
-    const int rows_left = tiles_m - first_m;
-    const int gsz = rows_left < group_m ? rows_left : group_m;
-    const int local = t - g * per_group;
-    tm = first_m + local % gsz;
-    tn = local / gsz;
-}
-
-__device__ inline int imin(int a, int b) { return a < b ? a : b; }
-
-// ---------------------------------------------------------------------------------
-// Slab loaders (global -> registers -> LDS).  LDS slabs are row-major with a
-// padded pitch: A as [BM][BK + PA] (k contiguous) for the MFMA kernel.
-// ---------------------------------------------------------------------------------
-
-// Loader of one operand's slab: a ROWS x COLS row-major panel, moved one slab
-// along K per call of advance().  KROWS selects which panel dimension runs
-// along K: false for A (the slab is BM rows x BK columns, K along columns),
-// true for B (BK rows x BN columns, K along rows).  The other dimension is
-// clamped once, at init, to the operand's last valid row/column (those lanes
-// feed only C elements that are never stored); elements past K are zero and
-// are checked only in the last, partial slab.  Vector form: one 16-byte load
-// covers 4 consecutive columns (needs ld % 4 == 0, ncols % 4 == 0 and a
-// 16-byte aligned base, which also make every 4-column group wholly inside or
-// outside K).  Per-lane offsets are 32-bit unless WIDE (64-bit, for leading
-// dimensions so large that one workgroup's panel spans 4 GiB or more).  NTL marks
-// the loads nontemporal (streamed: no other workgroup reads this operand's panel).
-template <int ROWS, int COLS, int NT, bool VEC, bool KROWS, bool WIDE, int NBUF = 1, bool NTL = false>
-struct PanelLoader {
-    using OffT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
-    static constexpr int W = VEC ? 4 : 1;             // floats per load
-    static constexpr int CPR = COLS / W;              // loads per panel row
-    static constexpr int L = ROWS * CPR / NT;         // loads per thread
-    static_assert(COLS % W == 0, "panel width");
-    static_assert((ROWS * CPR) % NT == 0, "panel must split evenly over the workgroup");
-    static_assert(NT % CPR == 0, "a load pass must cover whole panel rows");
-    static constexpr int ROWS_PER_PASS = NT / CPR;
-
-    f32x4 v[NBUF][L];      // NBUF register buffers of one slab each; only .x used when !VEC
-    const float* base;     // workgroup-uniform address of the current slab's first row/column
-    OffT off[L];           // this thread's BYTE offsets from base (same for every slab)
-    int row0, col;         // this thread's first panel row and its column (panel coordinates)
-    long step;             // address step from one slab to the next
-
-    // The panel's top-left element is (r0, c0) of an nrows x ncols operand with leading
-    // dimension ld.  Unless WIDE, byte offsets are 32-bit (the load then takes the uniform
-    // base from scalar registers and only the offset from a vector register): the caller
-    // guarantees ((ROWS - 1) * ld + COLS) * 4 < 2^32.
-    __device__ inline void init(int tid, const float* __restrict__ op, long ld, int r0, int c0, int nrows,
-                                int ncols, int bk) {
-        row0 = tid / CPR;
-        col = (tid % CPR) * W;
-        step = KROWS ? (long)bk * ld : (long)bk;
-        base = op + (long)r0 * ld + c0;
-        int c = col;
-        if (KROWS) c = imin(c0 + col, ncols - W) - c0;  // B: clamp columns past N
-#pragma unroll
-        for (int l = 0; l < L; ++l) {
-            int r = row0 + l * ROWS_PER_PASS;
-            if (!KROWS) r = imin(r0 + r, nrows - 1) - r0;  // A: clamp rows past M
-            off[l] = (OffT)(((long)r * ld + c) * 4);
-        }
-    }
-
-    __device__ inline void advance() { base += step; }
-
-    // Position along K of the l-th element, relative to the slab start.
-    __device__ inline int kpos(int l) const { return KROWS ? row0 + l * ROWS_PER_PASS : col; }
-
-    // Fetch the current slab; with TAIL, elements whose K index (kbase + kpos) is >= K become zero.
-    template <bool TAIL, int BUF = 0>
-    __device__ inline void fetch(int kbase, int K) {
-#pragma unroll
-        for (int l = 0; l < L; ++l) {
-            const bool ok = !TAIL || kbase + kpos(l) < K;
-            // An empty asm statement that "redefines" the 32-bit offset keeps its zero extension
-            // inside the loop, where it folds into the load's scalar-base + 32-bit-offset form
-            // instead of becoming a 64-bit vector add per load and slab.
-            if (!WIDE) asm volatile("" : "+v"(off[l]));
-            const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + off[l]);
-            if (VEC) {
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
-                v[BUF][l] = ok ? (NTL ? __builtin_nontemporal_load(p4) : *p4) : z;
-            } else {
-                v[BUF][l].x = ok ? (NTL ? __builtin_nontemporal_load(p) : *p) : 0.f;
-            }
-        }
-    }
-
-    // Fetch the slab starting at K index kbase (the pointers must already point at it).
-    template <int BUF = 0>
-    __device__ inline void fetch_slab(int kbase, int bk, int K) {
-        if (kbase + bk <= K)
-            fetch<false, BUF>(kbase, K);
-        else
-            fetch<true, BUF>(kbase, K);
-    }
-
-    // Store into an LDS panel [ROWS][PITCH].
-    template <int PITCH, int BUF = 0>
-    __device__ inline void store(float* __restrict__ lds) const {
-#pragma unroll
-        for (int l = 0; l < L; ++l) {
-            float* q = lds + (row0 + l * ROWS_PER_PASS) * PITCH + col;
-            if (VEC)
-                *reinterpret_cast<f32x4*>(q) = v[BUF][l];
-            else
-                *q = v[BUF][l].x;
-        }
-    }
-
-    // Store transposed into an LDS panel [COLS][PITCH] (element (r, c) -> lds[c][r]).
-    template <int PITCH>
-    __device__ inline void store_transposed(float* __restrict__ lds) const {
-#pragma unroll
-        for (int l = 0; l < L; ++l) {
-            const int r = row0 + l * ROWS_PER_PASS;
-            if (VEC) {
-                lds[(col + 0) * PITCH + r] = v[0][l].x;
-                lds[(col + 1) * PITCH + r] = v[0][l].y;
-                lds[(col + 2) * PITCH + r] = v[0][l].z;
-                lds[(col + 3) * PITCH + r] = v[0][l].w;
-            } else {
-                lds[col * PITCH + r] = v[0][l].x;
-            }
-        }
-    }
-};
-
-// Loader of a B slab (BK rows along K x BN columns of a row-major B) for the 32-bit-load
-// variants that stage B n-major in LDS, [BN][BK + 4]: each thread loads four consecutive k of one
-// column -- four 32-bit loads, each coalesced along N across the wave, since the lane-fastest
-// index is the column -- and writes them with ONE 128-bit LDS store, so that a lane's MFMA
-// fragment, four consecutive k of one column, is one 128-bit LDS read (the staging transpose of
-// "SGEMM CUDA kernel (First Half)", "Part 5: Reduced bank conflict (v3)", applied to B).  Against
-// PanelLoader's one LDS store per element and four 32-bit fragment reads, a quarter of the LDS
-// instructions for B.  Columns past N are clamped (they feed only C elements that are never
-// stored); k past K is zero (checked in the last slab only).  The four rows of a quad are
-// addressed from workgroup-uniform bases (scalar registers) plus one 32-bit per-lane byte offset
-// per quad (64-bit when WIDE).  Same interface as PanelLoader.
-template <int BK, int BN, int NT, bool WIDE, int NBUF = 1>
-struct KQuadLoader {
-    using OffT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
-    static constexpr int QROWS = BK / 4;          // k-quads per column per slab
-    static constexpr int QPP = NT / BN;           // k-quads of one column per pass of the workgroup
-    static constexpr int L = QROWS * BN / NT;     // quads per thread
-    static_assert(BK % 4 == 0 && NT % BN == 0 && QROWS % QPP == 0, "k-quads must split evenly");
-
-    f32x4 v[NBUF][L];
-    const float* base;  // workgroup-uniform address of the current slab's first row, first column
-    long ld_bytes;      // bytes from one row of B to the next
-    OffT off[L];        // byte offset of quad l's first element from base
-    int q0, col;        // this thread's first quad row and its column (panel coordinates)
-    long step;
-
-    __device__ inline void init(int tid, const float* __restrict__ op, long ld, int r0, int c0, int nrows,
-                                int ncols, int bk) {
-        (void)nrows;
-        col = tid % BN;
-        q0 = tid / BN;
-        step = (long)bk * ld;
-        ld_bytes = ld * 4;
-        base = op + (long)r0 * ld + c0;
-        const int c = imin(c0 + col, ncols - 1) - c0;  // clamp columns past N
-#pragma unroll
-        for (int l = 0; l < L; ++l) off[l] = (OffT)(((long)(q0 + l * QPP) * 4 * ld + c) * 4);
-    }
-
-    __device__ inline void advance() { base += step; }
-
-    template <bool TAIL, int BUF = 0>
-    __device__ inline void fetch(int kbase, int K) {
-#pragma unroll
-        for (int l = 0; l < L; ++l) {
-            if (!WIDE) asm volatile("" : "+v"(off[l]));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bool ok = !TAIL || kbase + (q0 + l * QPP) * 4 + t < K;
-                const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) +
-                                                                t * ld_bytes + off[l]);
-                v[BUF][l][t] = ok ? *p : 0.f;
-            }
-        }
-    }
-
-    template <int BUF = 0>
-    __device__ inline void fetch_slab(int kbase, int bk, int K) {
-        if (kbase + bk <= K)
-            fetch<false, BUF>(kbase, K);
-        else
-            fetch<true, BUF>(kbase, K);
-    }
-
-    // Store into an LDS panel [BN][PITCH] (column-major slab: element (k, n) at lds[n][k]).
-    template <int PITCH, int BUF = 0>
-    __device__ inline void store(float* __restrict__ lds) const {
-#pragma unroll
-        for (int l = 0; l < L; ++l) *reinterpret_cast<f32x4*>(lds + col * PITCH + (q0 + l * QPP) * 4) = v[BUF][l];
-    }
-};
-
-// ---------------------------------------------------------------------------------
-// MFMA kernel: v_mfma_f32_32x32x2_f32, wave tile WM x WN of 32x32 blocks.
-//
-// One 32x32x2 step computes D += X * Y where lane l (h = l / 32, i = l % 32)
-// supplies X(i, h) and Y(h, i), and accumulator register r of lane l holds
-// D(8*(r/4) + 4*h + r%4, i).  In the 128-bit variants each 32x32 block of C is
-// accumulated transposed: X is fed from B (X(i, h) = B(k(h), n0 + i)) and Y from A
-// (Y(h, i) = A(m0 + i, k(h))), so D = (A B)^T and register r of lane l holds
-// C(m0 + i, n0 + 8*(r/4) + 4*h + r%4): every group of four registers is four
-// consecutive columns of one row of C, written back with a single 128-bit store.
-// Within one 8-deep group of a slab, step s in 0..3 takes k = 4*h + s for half h,
-// so a lane's four A values are contiguous in the k-major LDS slab (one 128-bit
-// LDS read) and the 8 k's of the group are each used exactly once.
-// ---------------------------------------------------------------------------------
-// TA / TB: op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K).  The LDS slab of an
-// operand keeps the layout of its global rows: k-contiguous [rows][BK + 4] when K runs along
-// the stored rows (A, or B^T), and [BK][cols + 8] when it runs down the stored columns (B, or A^T).
-// BQ: B (not transposed) is loaded in k-quads by KQuadLoader and staged n-major like B^T.
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool TA = false, bool TB = false, bool BQ = false>
-struct MfmaCfg {
-    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
-    static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr bool B_NMAJOR = TB || BQ;  // B slab stored [BN][BK + 4], k contiguous
-    // k-contiguous slabs: pitch BK+4, so the 128-bit reads of 16 consecutive rows hit distinct
-    // banks; k-strided slabs: pitch (width)+8, so the two half-waves (k and k+4) land on
-    // opposite bank halves.
-    static constexpr int A_PITCH = TA ? BM + 8 : BK + 4, B_PITCH = B_NMAJOR ? BK + 4 : BN + 8;
-    static constexpr int A_STAGE = (TA ? BK : BM) * A_PITCH, B_STAGE = (B_NMAJOR ? BN : BK) * B_PITCH;
-    static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 4;
-    static_assert(BM % WM == 0 && BN % WN == 0, "wave tiling");
-    static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    static_assert(!(BQ && (TB || VEC)), "k-quad staging serves the 32-bit loads of an untransposed B");
-};
-
-// OCC > 0 asks the compiler for at least OCC waves per SIMD (registers capped at 512 / OCC),
-// so that OCC workgroups of 4 waves fit on one CU.
-// One 32x32x2 step on a block.  TRANS (used by the 128-bit variants) accumulates the block
-// transposed, as described above; otherwise X comes from A and Y from B, D = A B, and register
-// r of lane l holds C(m0 + 8*(r/4) + 4*h + r%4, n0 + i): lanes run along a row of C, which
-// keeps the 32-bit stores of the unaligned variants coalesced.
-template <bool TRANS>
-__device__ __attribute__((always_inline)) inline f32x16 mfma_step(float a, float b, const f32x16& c) {
-    return TRANS ? __builtin_amdgcn_mfma_f32_32x32x2f32(b, a, c, 0, 0, 0)
-                 : __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-// Epilogue of the MFMA kernels: C = alpha*acc + beta*C (C not read when beta == 0) for a
-// wave whose tile starts at (m_base, n_base).  The 128-bit variants hold blocks transposed
-// (four consecutive columns per four registers: one 128-bit store); the others hold them
-// upright (32 lanes along a row: coalesced 32-bit stores).
-// (Scalars are passed by value: taking the argument struct by reference makes the compiler
-// keep an addressable copy of it, which it may place in LDS.)
-// The C values a wave's output blocks need for the beta term, in the accumulators' layout
-// (entries outside the matrix are left unset; the epilogue skips them).  Kernels of one-round
-// grids read them at the start of the tile, after their first operand loads, so that the
-// read's latency hides under the K loop instead of stalling the epilogue.
-template <int FM, int FN, bool VEC>
-__device__ __attribute__((always_inline)) inline void mfma_load_c(int M, int N, const float* __restrict__ C,
-                                                                  long ldc, f32x16 (&cv)[FM][FN], int m_base,
-                                                                  int n_base, int li, int lh) {
-    if (VEC) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m_base + i * 32 + li;
-            if (row >= M) continue;
-            const float* prow = C + (long)row * ldc;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = n_base + j * 32 + q * 8 + lh * 4;
-                    if (col >= N) continue;
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(prow + col);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cv[i][j][4 * q + e] = v[e];
-                }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int lrow = m_base + i * 32 + lh * 4;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n_base + j * 32 + li;
-                if (col >= N) continue;
-                const float* pl = C + (long)lrow * ldc + col;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dr = (r >> 2) * 8 + (r & 3);
-                    if (lrow + dr < M) cv[i][j][r] = pl[dr * ldc];
-                }
-            }
-        }
-    }
-}
-
-// C := alpha * acc + beta * C over a wave's output blocks.  With beta != 0 the C values of a
-// block are loaded before its first store: the row stride is a run-time value, so the compiler
-// cannot tell a later load from an earlier store's address and would otherwise wait out one
-// memory round trip per loaded value.  (The 128-bit path's loads of one row differ by constant
-// offsets and already issue together; with several blocks per wave it keeps them that way,
-// which needs no extra registers.)  With PRE the C values come from cv instead, filled by
-// mfma_load_c at the start of the tile.
-template <int FM, int FN, bool VEC, bool PRE = false>
-__device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N, float alpha, float beta,
-                                                                    float* __restrict__ C, long ldc,
-                                                                    const f32x16 (&acc)[FM][FN], int m_base,
-                                                                    int n_base, int li, int lh,
-                                                                    const f32x16 (*cv)[FN] = nullptr) {
-    if (VEC) {
-        constexpr bool BATCH = PRE || FM * FN == 1;  // C values taken from registers
-        f32x16 cl[FM][FN];
-        if (BATCH && !PRE && beta != 0.f) mfma_load_c<FM, FN, VEC>(M, N, C, ldc, cl, m_base, n_base, li, lh);
-        const f32x16 (*cs)[FN] = PRE ? cv : cl;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m_base + i * 32 + li;
-            if (row >= M) continue;
-            float* prow = C + (long)row * ldc;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // N % 4 == 0 and col % 4 == 0: the 4 columns are all inside or all outside
-                    const int col = n_base + j * 32 + q * 8 + lh * 4;
-                    if (col >= N) continue;
-                    f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                               acc[i][j][4 * q + 3]};
-                    v *= alpha;
-                    f32x4* pc = reinterpret_cast<f32x4*>(prow + col);
-                    if (beta != 0.f) {
-                        if (BATCH) {
-                            const f32x4 c = {cs[i][j][4 * q + 0], cs[i][j][4 * q + 1], cs[i][j][4 * q + 2],
-                                             cs[i][j][4 * q + 3]};
-                            v += beta * c;
-                        } else {
-                            v += beta * *pc;
-                        }
-                    }
-                    *pc = v;
-                }
-            }
-        }
-    } else {
-        // register r holds row 8*(r/4) + 4*lh + r%4 of the block: one per-lane pointer per block,
-        // and a wave-uniform row step (8*(r/4) + r%4) * ldc per register
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int lrow = m_base + i * 32 + lh * 4;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n_base + j * 32 + li;
-                if (col >= N) continue;
-                float* pl = C + (long)lrow * ldc + col;
-                f32x16 c;
-                if (beta != 0.f) {
-                    if (PRE) {
-                        c = cv[i][j];
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int dr = (r >> 2) * 8 + (r & 3);
-                            if (lrow + dr < M) c[r] = pl[dr * ldc];
-                        }
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dr = (r >> 2) * 8 + (r & 3);
-                    if (lrow + dr < M) {
-                        float x = alpha * acc[i][j][r];
-                        if (beta != 0.f) x += beta * c[r];
-                        pl[dr * ldc] = x;
-                    }
-                }
-            }
-        }
-    }
-}
-
-// Drain ordering.  A SIMD issues from its highest-priority ready wave, oldest first among equals,
-// so of the workgroups sharing a CU the oldest runs nearly alone and finishes first; in a grid's
-// last round nothing refills the freed slots, and the last workgroup ends up alone on its CU, where
-// one wave per SIMD keeps the matrix pipe about two-thirds busy.  With FAIR, every wave starts at
-// priority 3 and, in the last round only, steps down at three points of its K loop (schedule
-// FAIR picks them): a wave ahead of the others on its SIMD drops below them until they catch up,
-// so the last round's workgroups end together.
-struct DrainPhases {
-    int next, after, last;  // slabs of the remaining steps down (even; INT_MAX: none)
-    int phase;              // 0..3
-    // drain_from: first workgroup of the last round; INT_MAX turns the ordering off (a grid with no
-    // more workgroups than CUs, where no two share a SIMD and priority changes only cost).
-    __device__ inline void init(int fair, int nslab, int drain_from) {
-        next = after = last = 0x7fffffff;
-        phase = 0;
-        if (drain_from == 0x7fffffff) return;
-        const bool last_round = (int)blockIdx.x >= drain_from;
-        // schedule 2: 1/2, 3/4, 7/8 of the K loop; 3: 3/4, 7/8, 15/16; 4: 7/8, 15/16, 31/32
-        const int n1 = fair == 4 ? 28 : (fair == 3 ? 24 : 16);
-        const int n2 = fair == 4 ? 30 : (fair == 3 ? 28 : 24);
-        const int n3 = fair == 4 ? 31 : (fair == 3 ? 30 : 28);
-        next = last_round ? (int)(((long)nslab * n1 / 32) & ~1L) : 0x7fffffff;
-        after = (int)(((long)nslab * n2 / 32) & ~1L);
-        last = (int)(((long)nslab * n3 / 32) & ~1L);
-        __builtin_amdgcn_s_setprio(3);
-    }
-    __device__ inline void step(int s) {
-        if (s >= next) {
-            ++phase;
-            if (phase == 1)
-                __builtin_amdgcn_s_setprio(2);
-            else if (phase == 2)
-                __builtin_amdgcn_s_setprio(1);
-            else
-                __builtin_amdgcn_s_setprio(0);
-            next = after;
-            after = last;
-            last = 0x7fffffff;
-        }
-    }
-};
-
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, bool TA = false, bool TB = false,
-          int FAIR = 0, bool NTA = false, bool BQ = false>
-__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>::NT))
-__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
-sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>;
-    constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
-    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
-    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
-    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
-
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / Cfg::WAVES_N) * WM;
-    const int wn0 = (wave % Cfg::WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
-
-    const int K = g.K;
-    // A slab: BM rows x BK columns of A, or (TA) BK rows x BM columns of the stored A^T.
-    // B slab: BK rows x BN columns of B, or (TB) BN rows x BK columns of the stored B^T.
-    using LoaderA = typename std::conditional<TA, PanelLoader<BK, BM, NT, VEC, true, WIDE, 1, NTA>,
-                                              PanelLoader<BM, BK, NT, VEC, false, WIDE, 1, NTA>>::type;
-    using LoaderB = typename std::conditional<
-        TB, PanelLoader<BN, BK, NT, VEC, false, WIDE>,
-        typename std::conditional<BQ, KQuadLoader<BK, BN, NT, WIDE>, PanelLoader<BK, BN, NT, VEC, true, WIDE>>::type>::type;
-    LoaderA la;
-    LoaderB lb;
-    if (TA)
-        la.init(tid, g.A, g.lda, 0, m0, K, g.M, BK);
-    else
-        la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
-    if (TB)
-        lb.init(tid, g.B, g.ldb, n0, 0, g.N, K, BK);
-    else
-        lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int nslab = (K + BK - 1) / BK;
-    const int nfull = K / BK;  // slabs with no element past K
-
-    la.fetch_slab(0, BK, K);
-    lb.fetch_slab(0, BK, K);
-    la.template store<AP>(lds_a);
-    lb.template store<BP>(lds_b);
-    __syncthreads();
-
-    // One slab: prefetch slab s+1 (PREFETCH 1: a full slab, 2: the partial last slab,
-    // 0: none), multiply slab s out of LDS, store the prefetched slab to the other stage.
-    // STAGE is s & 1 when known at compile time (the unrolled main loop), -1 otherwise.
-    auto slab = [&](int s, auto prefetch, auto stage) {
-        constexpr int PREFETCH = decltype(prefetch)::value;
-        constexpr int STAGE = decltype(stage)::value;
-        const int cur = STAGE >= 0 ? STAGE : (s & 1);
-        if (PREFETCH != 0) {
-            la.advance();
-            lb.advance();
-            la.template fetch<PREFETCH == 2>((s + 1) * BK, K);
-            lb.template fetch<PREFETCH == 2>((s + 1) * BK, K);
-            // keep the prefetch at the top of the slab: its latency hides under the MFMAs below
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const float* sa = lds_a + cur * Cfg::A_STAGE;
-        const float* sb = lds_b + cur * Cfg::B_STAGE;
-#pragma unroll
-        for (int kk = 0; kk < BK / 8; ++kk) {
-            f32x4 a[FM];
-            float b[FN][4];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                if (TA) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) a[i][t] = sa[(kk * 8 + lh * 4 + t) * AP + wm0 + i * 32 + li];
-                } else {
-                    a[i] = *reinterpret_cast<const f32x4*>(sa + (wm0 + i * 32 + li) * AP + kk * 8 + lh * 4);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                if (TB || BQ) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(sb + (wn0 + j * 32 + li) * BP + kk * 8 + lh * 4);
-                    b[j][0] = v.x;
-                    b[j][1] = v.y;
-                    b[j][2] = v.z;
-                    b[j][3] = v.w;
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) b[j][t] = sb[(kk * 8 + lh * 4 + t) * BP + wn0 + j * 32 + li];
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = mfma_step<VEC>(a[i][t], b[j][t], acc[i][j]);
-        }
-        if (PREFETCH != 0) {
-            la.template store<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
-            lb.template store<BP>(lds_b + (cur ^ 1) * Cfg::B_STAGE);
-        }
-        __syncthreads();
-    };
-    using Full = std::integral_constant<int, 1>;
-    using Dyn = std::integral_constant<int, -1>;
-    DrainPhases drain;
-    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
-    int s = 0;
-    // main loop, two slabs per trip so that both LDS stage offsets are constants
-    for (; s + 2 < nfull; s += 2) {
-        if (FAIR > 0) drain.step(s);
-        slab(s, Full{}, std::integral_constant<int, 0>{});
-        slab(s + 1, Full{}, std::integral_constant<int, 1>{});
-    }
-    for (; s + 1 < nfull; ++s) slab(s, Full{}, Dyn{});
-    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{}, Dyn{});
-    slab(s, std::integral_constant<int, 0>{}, Dyn{});
-
-    mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
-}
-
-// ---------------------------------------------------------------------------------
-// Pipelined MFMA kernel: same tiling, operand mapping and LDS layout as
-// sgemm_mfma_kernel, with the LDS -> register fragments double-buffered:
-// while the MFMAs of one 8-deep group run, the fragments of the next group are
-// read; the next slab's first fragments are read right after the slab's barrier,
-// under the MFMAs of the current slab's last group.  One barrier per slab:
-//   store slab s+1 (registers -> LDS stage (s+1)&1); barrier; fetch slab s+2
-//   (global -> registers); read group 0 of slab s+1; MFMAs of slab s's last group.
-// Stage (s+1)&1 was last read during slab s-1, whose reads all completed before
-// the barrier of iteration s-1 (the barrier waits for outstanding LDS accesses).
-// ---------------------------------------------------------------------------------
-template <int FM, int FN>
-struct MfmaFrag {
-    f32x4 a[FM];
-    float b[FN][4];
-};
-
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, int FAIR = 0>
-__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
-__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
-sgemm_mfma_pipe_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
-    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
-    constexpr int KK = BK / 8;
-    static_assert(KK % 2 == 0, "the fragment double buffer alternates per 8-deep group: BK must be 16 or 32");
-    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
-    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
-
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / Cfg::WAVES_N) * WM;
-    const int wn0 = (wave % Cfg::WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
-
-    const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false, WIDE> la;
-    PanelLoader<BK, BN, NT, VEC, true, WIDE> lb;
-    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
-    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // per-lane offsets of the fragment reads inside one LDS stage
-    const int a_off = (wm0 + li) * AP + lh * 4;
-    const int b_off = (lh * 4) * BP + wn0 + li;
-
-    auto read_frag = [&](MfmaFrag<FM, FN>& f, const float* sa, const float* sb, int kk) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            f.a[i] = *reinterpret_cast<const f32x4*>(sa + a_off + i * 32 * AP + kk * 8);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) f.b[j][t] = sb[b_off + (kk * 8 + t) * BP + j * 32];
-    };
-    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
-    };
-
-    const int nslab = (K + BK - 1) / BK;
-    const int nfull = K / BK;
-
-    la.fetch_slab(0, BK, K);
-    lb.fetch_slab(0, BK, K);
-    la.template store<AP>(lds_a);
-    lb.template store<BP>(lds_b);
-    __syncthreads();
-    if (nslab > 1) {
-        la.advance();
-        lb.advance();
-        la.fetch_slab(BK, BK, K);
-        lb.fetch_slab(BK, BK, K);
-    }
-    MfmaFrag<FM, FN> F[2];
-    read_frag(F[0], lds_a, lds_b, 0);
-
-    // One slab.  MODE 0: s is the last slab; 1: slab s+1 exists and a full slab s+2 is
-    // prefetched; 2: the partial slab s+2 is prefetched; 3: slab s+1 exists, no s+2.
-    auto slab = [&](int s, auto mode, auto stage) {
-        constexpr int MODE = decltype(mode)::value;
-        constexpr int STAGE = decltype(stage)::value;  // s & 1 when known at compile time, else -1
-        const int cur = STAGE >= 0 ? STAGE : (s & 1);
-        const float* sa = lds_a + cur * Cfg::A_STAGE;
-        const float* sb = lds_b + cur * Cfg::B_STAGE;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 1 < KK) {
-                read_frag(F[(kk + 1) & 1], sa, sb, kk + 1);
-            } else if (MODE != 0) {
-                float* na = lds_a + (cur ^ 1) * Cfg::A_STAGE;
-                float* nb = lds_b + (cur ^ 1) * Cfg::B_STAGE;
-                la.template store<AP>(na);
-                lb.template store<BP>(nb);
-                __syncthreads();
-                if (MODE == 1 || MODE == 2) {
-                    la.advance();
-                    lb.advance();
-                    la.template fetch<MODE == 2>((s + 2) * BK, K);
-                    lb.template fetch<MODE == 2>((s + 2) * BK, K);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                read_frag(F[0], na, nb, 0);
-            }
-            mfma_frag(F[kk & 1]);
-        }
-    };
-    using Dyn = std::integral_constant<int, -1>;
-    DrainPhases drain;
-    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
-    int s = 0;
-    for (; s + 3 < nfull; s += 2) {  // two slabs per trip: constant LDS stage offsets
-        if (FAIR > 0) drain.step(s);
-        slab(s, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
-        slab(s + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-    }
-    for (; s + 2 < nfull; ++s) slab(s, std::integral_constant<int, 1>{}, Dyn{});
-    for (; s + 2 < nslab; ++s) slab(s, std::integral_constant<int, 2>{}, Dyn{});
-    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 3>{}, Dyn{});
-    slab(s, std::integral_constant<int, 0>{}, Dyn{});
-
-    mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
-}
-
-// ---------------------------------------------------------------------------------
-// Deep-prefetch MFMA kernel, for grids of about one workgroup per compute unit: there a
-// SIMD runs a single wave, and no other wave covers its stalls.  Same tiling, operand
-// mapping, LDS layout (two stages) and epilogue as sgemm_mfma_kernel, with
-//   - global loads two slabs ahead, into two register buffers (slab s+2 is fetched at the
-//     top of slab s; slab s+1, fetched one slab earlier, is stored to LDS at its end), so a
-//     load has two slabs of MFMAs to arrive instead of one;
-//   - LDS -> register fragments read one 8-deep group ahead of the MFMAs that use them (the
-//     order is pinned with scheduling barriers; left alone, the compiler reads each
-//     fragment just before its use and the wave waits on every read);
-//   - the next slab's first fragments read right after the slab's barrier, under the MFMAs
-//     of the slab's last group.
-// LDS safety with two stages and one barrier per slab: stage (s+1)&1 is written in slab s
-// after the barrier of slab s-1, and every wave finished its reads of that stage (slab s-1)
-// before reaching that barrier (the barrier waits for outstanding LDS accesses).
-// ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 0, bool NTA = false,
-          bool CPRE = false, bool ACC2 = false>
-__global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
-__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
-sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
-    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
-    constexpr int KK = BK / 8;
-    static_assert(KK % 2 == 0, "fragment buffers alternate per 8-deep group: BK must be a multiple of 16");
-    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
-    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
-
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / Cfg::WAVES_N) * WM;
-    const int wn0 = (wave % Cfg::WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
-
-    const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false, false, 2, NTA> la;
-    PanelLoader<BK, BN, NT, VEC, true, false, 2> lb;
-    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
-    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // per-lane offsets of the fragment reads inside one LDS stage
-    const int a_off = (wm0 + li) * AP + lh * 4;
-    const int b_off = (lh * 4) * BP + wn0 + li;
-    auto read_frag = [&](MfmaFrag<FM, FN>& f, const float* sa, const float* sb, int kk) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            f.a[i] = *reinterpret_cast<const f32x4*>(sa + a_off + i * 32 * AP + kk * 8);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) f.b[j][t] = sb[b_off + (kk * 8 + t) * BP + j * 32];
-    };
-    // ACC2: odd k-steps accumulate into a second set of registers, so that consecutive MFMAs of a
-    // wave that owns a single block do not depend on each other; the two sums are added at the end
-    f32x16 acc2[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.f;
-    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    if (ACC2 && (t & 1))
-                        acc2[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc2[i][j]);
-                    else
-                        acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
-                }
-    };
-
-    const int nslab = (K + BK - 1) / BK;
-    const int nfull = K / BK;  // slabs with no element past K
-
-    // prologue: slab 0 to LDS stage 0, slab 1 into register buffer 1
-    la.template fetch_slab<0>(0, BK, K);
-    lb.template fetch_slab<0>(0, BK, K);
-    la.template store<AP, 0>(lds_a);
-    lb.template store<BP, 0>(lds_b);
-    if (nslab > 1) {
-        la.advance();
-        lb.advance();
-        la.template fetch_slab<1>(BK, BK, K);
-        lb.template fetch_slab<1>(BK, BK, K);
-    }
-    f32x16 cv[FM][FN];  // CPRE: C for the beta term, read after the first operand loads
-    if (CPRE && g.beta != 0.f) mfma_load_c<FM, FN, VEC>(g.M, g.N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
-    __syncthreads();
-    MfmaFrag<FM, FN> F[2];
-    read_frag(F[0], lds_a, lds_b, 0);
-
-    // Slab s, with P = s & 1: LDS stage P holds slab s, register buffer P is free (slab s went
-    // to LDS during slab s-1) and buffer P^1 holds slab s+1.  FULL: slab s+2 is a whole slab
-    // (no K checks) and slab s+1 exists; otherwise both are decided at run time.
-    auto slab = [&](int s, auto parity, auto full) {
-        constexpr int P = decltype(parity)::value;
-        constexpr bool FULL = decltype(full)::value;
-        const float* sa = lds_a + P * Cfg::A_STAGE;
-        const float* sb = lds_b + P * Cfg::B_STAGE;
-        if (FULL) {
-            la.advance();
-            lb.advance();
-            la.template fetch<false, P>((s + 2) * BK, K);
-            lb.template fetch<false, P>((s + 2) * BK, K);
-        } else if (s + 2 < nslab) {
-            la.advance();
-            lb.advance();
-            la.template fetch<true, P>((s + 2) * BK, K);
-            lb.template fetch<true, P>((s + 2) * BK, K);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) {
-            read_frag(F[(kk + 1) & 1], sa, sb, kk + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_frag(F[kk & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (FULL || s + 1 < nslab) {
-            float* na = lds_a + (P ^ 1) * Cfg::A_STAGE;
-            float* nb = lds_b + (P ^ 1) * Cfg::B_STAGE;
-            la.template store<AP, P ^ 1>(na);
-            lb.template store<BP, P ^ 1>(nb);
-            __syncthreads();
-            read_frag(F[0], na, nb, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_frag(F[(KK - 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    using Even = std::integral_constant<int, 0>;
-    using Odd = std::integral_constant<int, 1>;
-    using Full = std::integral_constant<bool, true>;
-    using Checked = std::integral_constant<bool, false>;
-    DrainPhases drain;
-    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
-    int s = 0;
-    for (; s + 3 < nfull; s += 2) {  // two slabs per trip: the buffer and stage of each are constants
-        if (FAIR > 0) drain.step(s);
-        slab(s, Even{}, Full{});
-        slab(s + 1, Odd{}, Full{});
-    }
-    while (s < nslab) {  // s is even here
-        slab(s, Even{}, Checked{});
-        if (++s >= nslab) break;
-        slab(s, Odd{}, Checked{});
-        ++s;
-    }
-
-    if (ACC2) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] += acc2[i][j];
-    }
-    mfma_epilogue<FM, FN, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
-}
-
-// ---------------------------------------------------------------------------------
-// Split-K MFMA kernel for shapes with few output tiles: KS groups of waves share one
-// workgroup and one BM x BN tile.  Group g multiplies slabs g, g + KS, g + 2 KS, ...
-// (each group with its own two LDS stages, loaders and accumulators, same K loop as
-// sgemm_mfma_kernel), so a CU gets KS times the waves and each wave a K loop KS times
-// shorter.  At the end groups 1..KS-1 leave their accumulators in LDS and group 0 adds
-// them in group order (a fixed order: results are deterministic) and writes C.
-// ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool VEC>
-struct SplitKCfg {
-    using Base = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    static constexpr int GT = Base::NT;  // threads per k-group
-    static constexpr int NT = GT * KS;
-    static constexpr int GROUP_FLOATS = 2 * (Base::A_STAGE + Base::B_STAGE);
-    static constexpr int RED_FLOATS = (KS - 1) * BM * BN;
-    static constexpr int LDS_FLOATS = KS * GROUP_FLOATS > RED_FLOATS ? KS * GROUP_FLOATS : RED_FLOATS;
-    static constexpr int LDS_BYTES = LDS_FLOATS * 4;
-    static_assert(KS >= 2 && NT <= 1024, "2..(1024 / group threads) k-groups");
-};
-
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool VEC>
-__global__ void __launch_bounds__((SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>::NT))
-sgemm_mfma_splitk_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Base = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
-    using Cfg = SplitKCfg<BM, BN, BK, WM, WN, KS, VEC>;
-    constexpr int GT = Cfg::GT, FM = Base::FM, FN = Base::FN;
-    constexpr int AP = Base::A_PITCH, BP = Base::B_PITCH;
-    __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
-
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int grp = tid / GT;           // k-group: whole waves, so wave-uniform
-    const int gtid = tid - grp * GT;    // thread index within the group
-    const int lane = gtid & 63, wave = gtid >> 6;
-    const int wm0 = (wave / Base::WAVES_N) * WM;
-    const int wn0 = (wave % Base::WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
-    float* lds_a = lds + grp * Cfg::GROUP_FLOATS;  // [2][A_STAGE] of this group
-    float* lds_b = lds_a + 2 * Base::A_STAGE;      // [2][B_STAGE] of this group
-
-    const int K = g.K;
-    PanelLoader<BM, BK, GT, VEC, false, false> la;
-    PanelLoader<BK, BN, GT, VEC, true, false> lb;
-    la.init(gtid, g.A, g.lda, m0, grp * BK, g.M, K, KS * BK);
-    lb.init(gtid, g.B, g.ldb, grp * BK, n0, K, g.N, KS * BK);
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int nslab = (K + BK - 1) / BK;
-    const int nfull = K / BK;
-    const int niter = (nslab + KS - 1) / KS;  // every group runs this many slab steps
-
-    la.fetch_slab(grp * BK, BK, K);  // a group whose first slab lies past K loads zeros
-    lb.fetch_slab(grp * BK, BK, K);
-    la.template store<AP>(lds_a);
-    lb.template store<BP>(lds_b);
-    __syncthreads();
-
-    // Step i: group grp multiplies slab i*KS + grp.  PREFETCH 1: the next step's slabs are
-    // full for every group; 2: some are partial or past K (checked loads); 0: no next step.
-    auto step = [&](int i, auto prefetch) {
-        constexpr int PREFETCH = decltype(prefetch)::value;
-        const int cur = i & 1;
-        if (PREFETCH != 0) {
-            la.advance();
-            lb.advance();
-            const int kb = ((i + 1) * KS + grp) * BK;
-            la.template fetch<PREFETCH == 2>(kb, K);
-            lb.template fetch<PREFETCH == 2>(kb, K);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const float* sa = lds_a + cur * Base::A_STAGE;
-        const float* sb = lds_b + cur * Base::B_STAGE;
-#pragma unroll
-        for (int kk = 0; kk < BK / 8; ++kk) {
-            f32x4 a[FM];
-            float b[FN][4];
-#pragma unroll
-            for (int i2 = 0; i2 < FM; ++i2)
-                a[i2] = *reinterpret_cast<const f32x4*>(sa + (wm0 + i2 * 32 + li) * AP + kk * 8 + lh * 4);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) b[j][t] = sb[(kk * 8 + lh * 4 + t) * BP + wn0 + j * 32 + li];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i2 = 0; i2 < FM; ++i2)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i2][j] = mfma_step<VEC>(a[i2][t], b[j][t], acc[i2][j]);
-        }
-        if (PREFETCH != 0) {
-            la.template store<AP>(lds_a + (cur ^ 1) * Base::A_STAGE);
-            lb.template store<BP>(lds_b + (cur ^ 1) * Base::B_STAGE);
-        }
-        __syncthreads();
-    };
-    int i = 0;
-    for (; i + 1 < niter && (i + 2) * KS <= nfull; ++i) step(i, std::integral_constant<int, 1>{});
-    for (; i + 1 < niter; ++i) step(i, std::integral_constant<int, 2>{});
-    step(i, std::integral_constant<int, 0>{});  // ends with a barrier: every LDS stage is free
-
-    // Reduction through LDS: group g >= 1 writes its partial tile, group 0 adds them in order.
-    constexpr int WAVE_FLOATS = FM * FN * 16 * 64;
-    if (grp > 0) {
-        float* red = lds + (grp - 1) * BM * BN + wave * WAVE_FLOATS;
-#pragma unroll
-        for (int i2 = 0; i2 < FM; ++i2)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f32x4 v = {acc[i2][j][4 * q + 0], acc[i2][j][4 * q + 1], acc[i2][j][4 * q + 2],
-                               acc[i2][j][4 * q + 3]};
-                    *reinterpret_cast<f32x4*>(red + (((i2 * FN + j) * 4 + q) * 64 + lane) * 4) = v;
-                }
-    }
-    __syncthreads();
-    if (grp == 0) {
-        for (int g2 = 1; g2 < KS; ++g2) {
-            const float* red = lds + (g2 - 1) * BM * BN + wave * WAVE_FLOATS;
-#pragma unroll
-            for (int i2 = 0; i2 < FM; ++i2)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = *reinterpret_cast<const f32x4*>(red + (((i2 * FN + j) * 4 + q) * 64 + lane) * 4);
-                        acc[i2][j][4 * q + 0] += v.x;
-                        acc[i2][j][4 * q + 1] += v.y;
-                        acc[i2][j][4 * q + 2] += v.z;
-                        acc[i2][j][4 * q + 3] += v.w;
-                    }
-        }
-        mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
-    }
-}
-
-// ---------------------------------------------------------------------------------
-// LDS-free MFMA kernel for small grids.  One wave per workgroup owns a 32x32 tile of C and loads
-// its MFMA operands from global memory straight into registers, in the layout the 32x32x2
-// instruction takes: for each 8-deep group of K, lane (i, h) needs A(m0+i, k) and B(k, n0+i) for
-// k = 4h + t, t = 0..3.  There is no LDS and no barrier; the loads run D groups ahead of the
-// MFMAs in a ring of registers.  Rows past M and columns past N are clamped (they feed outputs
-// that are never stored); k past K is zero.
-// ---------------------------------------------------------------------------------
-
-// One operand of the LDS-free kernel, X(r, k) with r = r0 + i along the tile (m for A, n for B).
-// KC: k runs along the stored rows (A, or B^T): a lane's four k values are contiguous, one
-// 128-bit load (VEC) or four 32-bit loads from row min(r0+i, R-1).  Otherwise (B, or A^T) each k
-// is a stored row and the lane reads column min(r0+i, R-1) of it: four 32-bit loads whose 32
-// lanes read 128 contiguous bytes.  Addressing of the full groups of the main loop: the tile's
-// origin plus a workgroup-uniform byte position that moves D groups per trip, plus
-// loop-invariant 32-bit per-lane byte offsets (KC: one, the group's step being an immediate;
-// otherwise one per (slot, t)), so each load is a scalar base plus a vector offset.  The
-// prologue's and the last trips' groups, which may reach past K, are addressed from the origin
-// with k clamped to K - 1, so no address outside the operand is ever formed.  The caller
-// guarantees the offsets fit 32 bits: KC: (31 * ld + 16 D) * 4 < 2^32, otherwise
-// ((16 D - 1) * ld + 32) * 4 < 2^32.
-template <bool KC, bool VEC, int D>
-struct DirectOperand {
-    static constexpr int NO = KC ? 1 : 4 * D;
-    const char* origin;  // X(r0, 0)
-    long pos;            // byte position of the current trip's first group from the origin
-    long step;           // bytes per trip
-    long ld;
-    int r;               // this lane's clamped row (KC) or column, relative to r0
-    uint32_t off[NO];
-
-    __device__ inline void init(const float* X, long ld_, int r0, int R, int li, int lh) {
-        ld = ld_;
-        r = imin(r0 + li, R - 1) - r0;
-        pos = 0;
-        if (KC) {
-            origin = reinterpret_cast<const char*>(X + (long)r0 * ld);
-            step = (long)D * 32;
-            off[0] = (uint32_t)(((long)r * ld + lh * 4) * 4);
-        } else {
-            origin = reinterpret_cast<const char*>(X + r0);
-            step = (long)D * 8 * ld * 4;
-            const long o = ((long)(lh * 4) * ld + r) * 4;
-#pragma unroll
-            for (int d = 0; d < D; ++d)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) off[d * 4 + t] = (uint32_t)(o + ((long)(D + d) * 8 + t) * ld * 4);
-        }
-    }
-
-    __device__ inline void advance() { pos += step; }
-
-    // Slot d's values for k = kb + t, kb = 8 g + 4h.  Without TAIL, group g is the trip's
-    // (D + d)-th group from its position and lies wholly below K.  With TAIL (any group), k >= K
-    // gives zero: such elements are read at k = K - 1 (K - 4 for the 128-bit load) and then
-    // replaced, so that no load is conditional (a branch around a load would stop the compiler
-    // from counting the loads in flight across the loop, and it would wait for all of them at
-    // the top of every trip).
-    template <bool TAIL>
-    __device__ inline void load(f32x4& v, int d, int kb, int K) {
-        if (KC) {
-            if (!TAIL) {
-                asm volatile("" : "+v"(off[0]));
-                const char* q = origin + pos + off[0] + (D + d) * 32;
-                if (VEC)
-                    v = *reinterpret_cast<const f32x4*>(q);
-                else
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = reinterpret_cast<const float*>(q)[t];
-            } else if (VEC) {  // K % 4 == 0: the four k are all below K or all at or past it
-                const f32x4 x = *reinterpret_cast<const f32x4*>(origin + ((long)r * ld + imin(kb, K - 4)) * 4);
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                v = kb < K ? x : z;
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float x = *reinterpret_cast<const float*>(origin + ((long)r * ld + imin(kb + t, K - 1)) * 4);
-                    v[t] = kb + t < K ? x : 0.f;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (!TAIL) {
-                    asm volatile("" : "+v"(off[d * 4 + t]));
-                    v[t] = *reinterpret_cast<const float*>(origin + pos + off[d * 4 + t]);
-                } else {
-                    const float x = *reinterpret_cast<const float*>(origin + ((long)imin(kb + t, K - 1) * ld + r) * 4);
-                    v[t] = kb + t < K ? x : 0.f;
-                }
-            }
-        }
-    }
-};
-
-template <bool VEC, int D, bool TA = false, bool TB = false, bool CPRE = false>
-__global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * 32, n0 = tn * 32;
-    const int lane = threadIdx.x, li = lane & 31, lh = lane >> 5;
-    const int K = g.K;
-    DirectOperand<!TA, VEC, D> oa;  // A (M x K): k along its rows; A^T (K x M): k down its rows
-    DirectOperand<TB, VEC, D> ob;   // B (K x N): k down its rows; B^T (N x K): k along its rows
-    oa.init(g.A, g.lda, m0, g.M, li, lh);
-    ob.init(g.B, g.ldb, n0, g.N, li, lh);
-
-    f32x4 ra[D], rb[D];
-    auto load = [&](int d, int grp, auto tail) {  // group grp into slot d
-        constexpr bool TAIL = decltype(tail)::value;
-        const int kb = 8 * grp + 4 * lh;
-        oa.template load<TAIL>(ra[d], d, kb, K);
-        ob.template load<TAIL>(rb[d], d, kb, K);
-    };
-    f32x16 acc[1][1];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.f;
-    auto mfma = [&](int d) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[0][0] = mfma_step<VEC>(ra[d][t], rb[d][t], acc[0][0]);
-    };
-    auto advance = [&]() {
-        oa.advance();
-        ob.advance();
-    };
-    using Tail = std::integral_constant<bool, true>;
-    using Full = std::integral_constant<bool, false>;
-
-    const int ngroups = (K + 7) / 8, nfull = K / 8;
-    // at the top of the trip at group q, slot d holds group q + d (zeros for groups past K)
-#pragma unroll
-    for (int d = 0; d < D; ++d) load(d, d, Tail{});
-    f32x16 cv[1][1];  // CPRE: C for the beta term, read after the ring's first loads
-    if (CPRE && g.beta != 0.f) mfma_load_c<1, 1, VEC>(g.M, g.N, g.C, g.ldc, cv, m0, n0, li, lh);
-    int q = 0;
-    for (; q + 2 * D <= nfull; q += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            mfma(d);
-            load(d, q + D + d, Full{});
-        }
-        advance();
-    }
-    for (; q + D < ngroups; q += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            mfma(d);
-            load(d, q + D + d, Tail{});
-        }
-    }
-#pragma unroll
-    for (int d = 0; d < D; ++d) mfma(d);
-
-    mfma_epilogue<1, 1, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0, n0, li, lh, cv);
-}
-
-// ---------------------------------------------------------------------------------
-// Direct-to-LDS MFMA kernel: the operand slabs go from global memory straight into LDS with
-// gfx950's global_load_lds (each lane's W bytes land at the wave's LDS base + W x lane; W = 16
-// with global_load_lds_dwordx4 for 16-byte aligned rows, W = 4 with global_load_lds_dword
-// otherwise), so no register holds a prefetched slab and no LDS store instruction runs in the K
-// loop -- the stores that, at one wave per SIMD, take issue cycles and VGPR read bandwidth from
-// the matrix pipe.  STAGES LDS buffers form a ring: slab s + STAGES - 1 is requested right after
-// the barrier that opens slab s, into the buffer every wave finished reading before that
-// barrier, so a slab has STAGES - 1 slabs of MFMAs to arrive.  One barrier per slab; before it,
-// each wave waits (s_waitcnt vmcnt) only for its own loads of the next slab, leaving later slabs
-// in flight.
-//
-// Layout: a wave's load fills 64 W bytes of LDS contiguously, so the slabs are unpadded -- A as
-// [BM][BK] (k contiguous), B as [BK][BN] (n contiguous) -- and bank conflicts of the fragment
-// reads are avoided by choosing WHICH 16-byte quad of its row a lane (W = 16) or a group of four
-// lanes (W = 4) fetches: the quad at LDS position u of row r holds global quad u ^ swz(r) (an XOR
-// swizzle, a permutation within the row, so the loads of a row still cover the same cache lines).
-// The swizzles make the 128-bit A reads (16 consecutive rows at one quad) and the 32-bit B reads
-// (rows k and k + 4 at 32 consecutive columns) free of conflicts both with 64 banks and 16 lanes
-// per pass and with 32 banks and 8 lanes per pass.
-//
-// Edges: rows of A past M and columns of B past N are clamped (they feed C elements that are never
-// stored).  The slab that crosses K is loaded with k clamped into range, so every address lies
-// inside the operand, and each wave then overwrites what it loaded past K with zeros, after its
-// loads have landed and before the barrier.  W = 16 needs the 128-bit variants' precondition
-// (16-byte aligned rows; K and N multiples of 4).
-// ---------------------------------------------------------------------------------
-template <int QPR>
-__device__ __host__ inline int dl_swz_a(int r) {  // swizzle of A row r (QPR quads per row)
-    static_assert(QPR == 4 || QPR == 8 || QPR == 16, "A rows of 16, 32 or 64 floats");
-    return QPR == 16 ? r & 15
-                     : QPR == 8 ? ((r & 15) + ((r >> 3) & 1)) & 7 : (((r >> 1) & 7) + ((r >> 3) & 1)) & 3;
-}
-__device__ __host__ inline int dl_swz_b(int k) { return ((k >> 2) & 1) * 8; }  // swizzle of B row k, in quads
-
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W = 16>
-struct DlCfg {
-    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-    static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
-    static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int QPR_A = BK / 4, QPR_B = BN / 4;           // 16-byte quads per row
-    static constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;     // floats
-    static constexpr int CH = 16 * W;                              // floats one wave's load fills
-    static constexpr int LA = A_STAGE / CH / NW, LB = B_STAGE / CH / NW;  // loads per wave and slab
-    static constexpr int LPW = LA + LB;
-    static constexpr int D = STAGES - 1;                           // slabs in flight ahead
-    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 4;
-    static_assert(W == 4 || W == 16, "32-bit or 128-bit loads");
-    static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
-    static_assert(A_STAGE % (CH * NW) == 0 && B_STAGE % (CH * NW) == 0, "whole loads per wave");
-    static_assert(BN % 64 == 0, "the B swizzle needs rows of 16 quads or more");
-    static_assert(BK % 8 == 0 && BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiling");
-    static_assert(LPW * D < 64, "vmcnt counts at most 63 loads in flight");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-};
-
-// The direct loads, their waits and the barrier are inline asm.  Issued through the compiler
-// builtin, a load into LDS makes the compiler wait for it (s_waitcnt vmcnt(0)) before every later
-// LDS read it cannot tell apart from the loaded stage -- here every fragment read -- which would
-// expose the full load latency in every slab.  As asm with a memory clobber, the compiler neither
-// waits for these loads nor moves LDS accesses across them, the barrier or the waits; the kernel
-// waits for them itself.  Its own waits for other loads stay correct: counting fewer loads in
-// flight than there are only makes a vmcnt wait stricter.  The loads have no register results.
-// M0 holds the LDS address (M0 is reserved to the compiler, so the asm restores it); the s_nop
-// covers the wait state between an SALU write of M0 and the load that reads it.
-template <int W>
-__device__ __attribute__((always_inline)) inline void dl_load(const void* base, uint32_t off, uint32_t lds) {
-    uint32_t keep;
-    if (W == 16)
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-            : "=&s"(keep)
-            : "s"(lds), "v"(off), "s"(base)
-            : "memory");
-    else
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-            : "=&s"(keep)
-            : "s"(lds), "v"(off), "s"(base)
-            : "memory");
-}
-template <int W>
-__device__ __attribute__((always_inline)) inline void dl_load_at(const void* p, uint32_t lds) {
-    uint32_t keep;
-    if (W == 16)
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-            : "=&s"(keep)
-            : "s"(lds), "v"(p)
-            : "memory");
-    else
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-            : "=&s"(keep)
-            : "s"(lds), "v"(p)
-            : "memory");
-}
-// Wait until at most N of this wave's vector-memory loads are in flight and all its LDS accesses
-// are done.
-template <int N>
-__device__ __attribute__((always_inline)) inline void wait_vm_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"i"(N) : "memory");
-}
-// The same with N = n * PER chosen at run time (n = 0 .. 3 slabs of PER loads each).
-template <int PER>
-__device__ __attribute__((always_inline)) inline void wait_slabs(int n) {
-    if (n <= 0)
-        wait_vm_lgkm0<0>();
-    else if (n == 1)
-        wait_vm_lgkm0<PER>();
-    else if (n == 2)
-        wait_vm_lgkm0<(2 * PER < 64 ? 2 * PER : 63)>();
-    else
-        wait_vm_lgkm0<(3 * PER < 64 ? 3 * PER : 63)>();
-}
-__device__ __attribute__((always_inline)) inline void dl_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// The LDS address of a pointer into a __shared__ array.
-__device__ __attribute__((always_inline)) inline uint32_t lds_addr(const float* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)(p);
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
-          bool SPREAD = false>
-__global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT))
-__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
-sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / 8, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
-    constexpr int QA = Cfg::QPR_A, QB = Cfg::QPR_B, CH = Cfg::CH, E = W / 4;  // E: floats per lane load
-    constexpr bool VEC = W == 16;
-    static_assert(KK % 2 == 0 || KK == 1, "fragment buffers alternate per 8-deep group");
-    __shared__ __attribute__((aligned(1024))) float lds_a[STAGES * Cfg::A_STAGE];
-    __shared__ __attribute__((aligned(1024))) float lds_b[STAGES * Cfg::B_STAGE];
-
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave / Cfg::WAVES_N) * WM;
-    const int wn0 = (wave % Cfg::WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
-    const int M = g.M, N = g.N, K = g.K;
-    const long lda = g.lda, ldb = g.ldb;
-
-    // This lane's loads: load j of the wave fills floats [c CH, (c + 1) CH) of the slab,
-    // c = wave * L + j; the lane's E floats start at float f = c CH + E lane, i.e. row f / (row
-    // length), LDS quad u = (f % row length) / 4, element f % 4 of it, which holds global quad
-    // u ^ swz(row).
-    // The k of a lane's load j inside the slab (recomputed where needed: only the slab that
-    // crosses K uses it, and keeping it live would cost registers throughout the loop).
-    auto a_kin = [&](int j) {
-        const int f = (wave * LA + j) * CH + E * lane;
-        return 4 * (((f % BK) / 4) ^ dl_swz_a<QA>(f / BK)) + f % 4;
-    };
-    auto b_kin = [&](int j) { return ((wave * LB + j) * CH + E * lane) / BN; };
-    uint32_t a_off[LA], b_off[LB];  // byte offsets from the slab's first element
-#pragma unroll
-    for (int j = 0; j < LA; ++j) {
-        const int f = (wave * LA + j) * CH + E * lane;
-        const int row = imin(m0 + f / BK, M - 1) - m0;
-        a_off[j] = (uint32_t)(((long)row * lda + a_kin(j)) * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < LB; ++j) {
-        const int f = (wave * LB + j) * CH + E * lane;
-        const int k = f / BN, u = (f % BN) / 4;
-        const int n = imin(n0 + 4 * (u ^ dl_swz_b(k)) + f % 4, N - E) - n0;
-        b_off[j] = (uint32_t)(((long)k * ldb + n) * 4);
-    }
-    const float* a_tile = g.A + (long)m0 * lda;  // A(m0, 0)
-    const float* b_tile = g.B + n0;              // B(0, n0)
-
-    // Request slab s into its stage.  TAIL: the slab crosses K; k is clamped into range here (the
-    // address moves from k0 + k to min(k0 + k, K - E) for A, to row min(k0 + k, K - 1) for B) and
-    // what lies past K is zeroed by fix_tail once the loads have landed.
-    auto issue = [&](int s, auto tail) {
-        constexpr bool TAIL = decltype(tail)::value;
-        const int st = s % STAGES, k0 = s * BK;
-        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
-        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
-#pragma unroll
-        for (int j = 0; j < LA; ++j) {
-            if (!TAIL) {
-                dl_load<W>(a_tile + k0, a_off[j], lds_addr(sa + j * CH));
-            } else {
-                const int k = a_kin(j);
-                dl_load_at<W>(reinterpret_cast<const char*>(a_tile) + a_off[j] + 4L * (imin(k0 + k, K - E) - k),
-                              lds_addr(sa + j * CH));
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < LB; ++j) {
-            if (!TAIL) {
-                dl_load<W>(b_tile + (long)k0 * ldb, b_off[j], lds_addr(sb + j * CH));
-            } else {
-                const int k = b_kin(j);
-                dl_load_at<W>(reinterpret_cast<const char*>(b_tile) + b_off[j] + 4L * (imin(k0 + k, K - 1) - k) * ldb,
-                              lds_addr(sb + j * CH));
-            }
-        }
-    };
-    // Load q (0 .. LPW - 1) of whole slab s: the A loads, then the B loads.
-    auto issue_one = [&](int s, int q) {
-        const int st = s % STAGES, k0 = s * BK;
-        if (q < LA)
-            dl_load<W>(a_tile + k0, a_off[q], lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH));
-        else
-            dl_load<W>(b_tile + (long)k0 * ldb, b_off[q - LA],
-                       lds_addr(lds_b + st * Cfg::B_STAGE + (wave * LB + q - LA) * CH));
-    };
-    // After the loads of the slab that crosses K have landed: zero what lies past K (each wave
-    // the elements its own loads wrote; with W = 16, K % 4 == 0 makes a quad wholly in or out).
-    auto fix_tail = [&](int s) {
-        const int st = s % STAGES, k0 = s * BK;
-        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
-        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
-#pragma unroll
-        for (int j = 0; j < LA; ++j)
-            if (k0 + a_kin(j) >= K) {
-                if (VEC)
-                    *reinterpret_cast<f32x4*>(sa + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
-                else
-                    sa[j * CH + lane] = 0.f;
-            }
-#pragma unroll
-        for (int j = 0; j < LB; ++j)
-            if (k0 + b_kin(j) >= K) {
-                if (VEC)
-                    *reinterpret_cast<f32x4*>(sb + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
-                else
-                    sb[j * CH + lane] = 0.f;
-            }
-    };
-
-    // Fragment reads: A's quad 2 kk + h of row wm0 + 32 fi + li sits at quad ((2 kk + h) ^ swz) of
-    // that row (the swizzle depends on the row's low four bits only, so not on fi); B's element
-    // (k, n) with k = 8 kk + 4 h + t sits at column n ^ 32 h of row k (the B swizzle flips quad bit
-    // 3, i.e. column bit 5, on rows with bit 2 set).
-    int a_frag[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        a_frag[kk] = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
-    int b_frag[FN];
-#pragma unroll
-    for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh));
-    auto read_frag = [&](MfmaFrag<FM, FN>& f, int st, int kk) {
-        const float* sa = lds_a + st * Cfg::A_STAGE;
-        const float* sb = lds_b + st * Cfg::B_STAGE;
-#pragma unroll
-        for (int fi = 0; fi < FM; ++fi)
-            f.a[fi] = *reinterpret_cast<const f32x4*>(sa + a_frag[kk] + fi * 32 * BK);
-#pragma unroll
-        for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (8 * kk + t) * BN];
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
-    };
-
-    const int nslab = (K + BK - 1) / BK;
-    const int nfull = K / BK;
-    using Tail = std::integral_constant<bool, true>;
-    using Whole = std::integral_constant<bool, false>;
-    // the C values of the beta term first: the oldest loads, consumed only by the epilogue
-    f32x16 cv[FM][FN];
-    if (CPRE && g.beta != 0.f) mfma_load_c<FM, FN, VEC>(M, N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
-    // prologue: slabs 0 .. D-1 requested; wait for slab 0 (the later ones may stay in flight)
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-        if (s < nfull)
-            issue(s, Whole{});
-        else if (s < nslab)
-            issue(s, Tail{});
-    }
-    wait_slabs<Cfg::LPW>(imin(D, nslab) - 1);
-    if (nfull == 0) {
-        fix_tail(0);
-        wait_vm_lgkm0<0>();
-    }
-    dl_barrier();
-    MfmaFrag<FM, FN> F[2];
-    read_frag(F[0], 0, 0);
-
-    // Slab s (stage ST = s % STAGES when known at compile time, else -1).  FULL: slab s + D exists
-    // and is whole, so the wait before the next barrier leaves exactly D - 1 slabs in flight.
-    // SPREAD (whole slabs, rings of three or more stages): the requests for slab s + D are issued
-    // LPG at a time after each 8-deep group's MFMAs instead of all at the top of the slab, so that
-    // they issue in the matrix pipe's shadow.  It pays at one wave per SIMD on L2-resident operands
-    // (per-wave timestamps at 1024^3: 1103 against 1169 cycles per 16-MFMA slab), and costs where
-    // the last requests, issued at the end of the slab, then have one slab instead of two to land
-    // (three-stage 128x128 tiles at 4096^3: 1120 against 922 us), so it is a variant of its own.
-    constexpr bool SP_ON = SPREAD && D >= 2 && KK > 1;
-    constexpr int LPG = (Cfg::LPW + KK - 1) / KK;
-    auto slab = [&](int s, auto stage, auto full) {
-        constexpr int STC = decltype(stage)::value;
-        constexpr bool FULL = decltype(full)::value;
-        constexpr bool SP = SP_ON && FULL;
-        const int st = STC >= 0 ? STC : s % STAGES;
-        if (!SP) {
-            if (FULL || s + D < nfull)
-                issue(s + D, Whole{});
-            else if (s + D < nslab)
-                issue(s + D, Tail{});
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) {
-            read_frag(F[(kk + 1) & 1], st, kk + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_frag(F[kk & 1]);
-            if (SP) {
-#pragma unroll
-                for (int q = kk * LPG; q < (kk + 1) * LPG && q < Cfg::LPW; ++q) issue_one(s + D, q);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (SP) {
-#pragma unroll
-            for (int q = (KK - 1) * LPG; q < Cfg::LPW; ++q) issue_one(s + D, q);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (FULL || s + 1 < nslab) {
-            // slabs requested after slab s + 1: s + 2 .. min(s + D, nslab - 1)
-            if (FULL) {
-                wait_vm_lgkm0<Cfg::LPW * (D - 1)>();
-            } else {
-                wait_slabs<Cfg::LPW>(imin(s + D, nslab - 1) - (s + 1));
-                if (s + 1 >= nfull) {
-                    fix_tail(s + 1);
-                    wait_vm_lgkm0<0>();
-                }
-            }
-            dl_barrier();
-            read_frag(F[0], STC >= 0 ? (STC + 1) % STAGES : (s + 1) % STAGES, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_frag(F[(KK - 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    using Full = std::integral_constant<bool, true>;
-    using Checked = std::integral_constant<bool, false>;
-    DrainPhases drain;
-    if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
-    int s = 0;
-    // STAGES slabs per trip, so that every stage offset is a constant
-    for (; s + STAGES - 1 + D < nfull; s += STAGES) {
-        if (FAIR > 0) drain.step(s);
-        slab(s, std::integral_constant<int, 0>{}, Full{});
-        slab(s + 1, std::integral_constant<int, 1>{}, Full{});
-        if (STAGES > 2) slab(s + 2, std::integral_constant<int, 2 % STAGES>{}, Full{});
-        if (STAGES > 3) slab(s + 3, std::integral_constant<int, 3 % STAGES>{}, Full{});
-    }
-    for (; s < nslab; ++s) slab(s, std::integral_constant<int, -1>{}, Checked{});
-
-    mfma_epilogue<FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
-}
-
-// ---------------------------------------------------------------------------------
-// VALU kernel: TM x TN register microtile per lane, A stored k-major in LDS.
-// A lane's TM rows are TM/4 groups of 4 consecutive rows spaced BM/(TM/4)
-// apart (likewise for columns), so the 128-bit LDS reads of a wave touch
-// consecutive addresses (B) or broadcast (A).
-// ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int TM, int TN, bool VEC>
-struct ValuCfg {
-    static constexpr int TX = BN / TN, TY = BM / TM, NT = TX * TY;
-    static constexpr int GM = TM / 4, GN = TN / 4;
-    static constexpr int SM = BM / GM, SN = BN / GN;
-    static constexpr int PA = 4, PB = 4;
-    static constexpr int A_PITCH = BM + PA, B_PITCH = BN + PB;
-    static constexpr int A_STAGE = BK * A_PITCH, B_STAGE = BK * B_PITCH;
-    static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * 4;
-    static_assert(TM % 4 == 0 && TN % 4 == 0, "microtile in groups of 4");
-    static_assert(BM % TM == 0 && BN % TN == 0, "tiling");
-};
-
-template <int BM, int BN, int BK, int TM, int TN, bool VEC, bool WIDE>
-__global__ void __launch_bounds__((ValuCfg<BM, BN, BK, TM, TN, VEC>::NT))
-sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = ValuCfg<BM, BN, BK, TM, TN, VEC>;
-    constexpr int NT = Cfg::NT, GM = Cfg::GM, GN = Cfg::GN, SM = Cfg::SM, SN = Cfg::SN;
-    constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
-    __shared__ __attribute__((aligned(16))) float lds_a[2 * Cfg::A_STAGE];
-    __shared__ __attribute__((aligned(16))) float lds_b[2 * Cfg::B_STAGE];
-
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int tx = tid % Cfg::TX, ty = tid / Cfg::TX;
-
-    const int K = g.K;
-    PanelLoader<BM, BK, NT, VEC, false, WIDE> la;
-    PanelLoader<BK, BN, NT, VEC, true, WIDE> lb;
-    la.init(tid, g.A, g.lda, m0, 0, g.M, K, BK);
-    lb.init(tid, g.B, g.ldb, 0, n0, K, g.N, BK);
-
-    float acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
-
-    const int nslab = (K + BK - 1) / BK;
-    const int nfull = K / BK;
-    la.fetch_slab(0, BK, K);
-    lb.fetch_slab(0, BK, K);
-    la.template store_transposed<AP>(lds_a);
-    lb.template store<BP>(lds_b);
-    __syncthreads();
-
-    auto slab = [&](int s, auto prefetch) {
-        constexpr int PREFETCH = decltype(prefetch)::value;
-        const int cur = s & 1;
-        if (PREFETCH != 0) {
-            la.advance();
-            lb.advance();
-            la.template fetch<PREFETCH == 2>((s + 1) * BK, K);
-            lb.template fetch<PREFETCH == 2>((s + 1) * BK, K);
-            // keep the prefetch at the top of the slab: its latency hides under the MFMAs below
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const float* sa = lds_a + cur * Cfg::A_STAGE;
-        const float* sb = lds_b + cur * Cfg::B_STAGE;
-#pragma unroll
-        for (int k = 0; k < BK; ++k) {
-            float a[TM], b[TN];
-#pragma unroll
-            for (int gi = 0; gi < GM; ++gi) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(sa + k * AP + gi * SM + ty * 4);
-                a[gi * 4 + 0] = v.x; a[gi * 4 + 1] = v.y; a[gi * 4 + 2] = v.z; a[gi * 4 + 3] = v.w;
-            }
-#pragma unroll
-            for (int gj = 0; gj < GN; ++gj) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(sb + k * BP + gj * SN + tx * 4);
-                b[gj * 4 + 0] = v.x; b[gj * 4 + 1] = v.y; b[gj * 4 + 2] = v.z; b[gj * 4 + 3] = v.w;
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-        }
-        if (PREFETCH != 0) {
-            la.template store_transposed<AP>(lds_a + (cur ^ 1) * Cfg::A_STAGE);
-            lb.template store<BP>(lds_b + (cur ^ 1) * Cfg::B_STAGE);
-        }
-        __syncthreads();
-    };
-    int s = 0;
-    for (; s + 1 < nfull; ++s) slab(s, std::integral_constant<int, 1>{});
-    for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{});
-    slab(s, std::integral_constant<int, 0>{});
-
-    const float alpha = g.alpha, beta = g.beta;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = m0 + (i / 4) * SM + ty * 4 + (i % 4);
-        if (row >= g.M) continue;
-        float* prow = g.C + (long)row * g.ldc;
-#pragma unroll
-        for (int gj = 0; gj < GN; ++gj) {
-            const int col = n0 + gj * SN + tx * 4;
-            if (VEC) {
-                // N % 4 == 0: a 4-column group is entirely inside or outside.
-                if (col < g.N) {
-                    f32x4* pc = reinterpret_cast<f32x4*>(prow + col);
-                    f32x4 v = {alpha * acc[i][gj * 4 + 0], alpha * acc[i][gj * 4 + 1],
-                               alpha * acc[i][gj * 4 + 2], alpha * acc[i][gj * 4 + 3]};
-                    if (beta != 0.f) v += beta * *pc;
-                    *pc = v;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (col + e < g.N) {
-                        float v = alpha * acc[i][gj * 4 + e];
-                        if (beta != 0.f) v += beta * prow[col + e];
-                        prow[col + e] = v;
-                    }
-                }
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------
-// C := beta * C (the alpha == 0 / K == 0 case; beta == 0 writes zeros without reading C).
-// ---------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float beta, float* C, long ldc) {
-    const long total = (long)M * N;
-    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
-        const long i = e / N, j = e - i * N;
-        float* p = C + i * ldc + j;
-        *p = (beta == 0.f) ? 0.f : beta * *p;
-    }
-}
-
-}  // namespace libsgemm
+#include "kernel_common.hpp"
+#include "kernel_mfma.hpp"
+#include "kernel_pipe.hpp"
+#include "kernel_deep.hpp"
+#include "kernel_splitk.hpp"
+#include "kernel_direct.hpp"
+#include "kernel_dl.hpp"
+#include "kernel_valu.hpp"

@@ -1,7 +1,7 @@
 // sgemm_launch.hpp -- the kernel variants of libsgemm: how each is launched (grid, block,
 // workgroup-to-tile grouping) and the table of all variants with their tile parameters.
 // Included by sgemm.hip only, inside its anonymous namespace; the kernels themselves are in
-// sgemm_kernels.hpp.  Together these two files fix what runs on the GPU for a given variant;
+// sgemm_kernels.hpp (one header per kernel family).  Together they fix what runs on the GPU for a given variant;
 // which variant runs for a given call is decided in sgemm.hip and tuned_table.inc.
 #pragma once
 

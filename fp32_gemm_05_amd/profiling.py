@@ -45,10 +45,21 @@ from .roofline import FP32_PEAK_TFLOPS, algorithmic_bytes, gemm_flops, panel_rea
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-# The files that fix what runs on the GPU for a given variant: the kernels, and how each variant
-# is launched.  The dispatch (which variant a call gets) is not included: the counter summaries
-# are per variant, so a retuned table leaves them valid.
-KERNEL_SOURCES = ("sgemm_kernels.hpp", "sgemm_launch.hpp")
+# The files that fix what runs on the GPU for a given variant: the shared kernel pieces, the
+# variant's kernel family, and how each variant is launched.  The dispatch (which variant a call
+# gets) is not included: the counter summaries are per variant, so a retuned table leaves them
+# valid, and so does a change to another kernel family.
+KERNEL_COMMON = ("kernel_common.hpp", "sgemm_launch.hpp")
+# kernel family of a variant, by its name's prefix
+KERNEL_FAMILIES = (("mfma32p_", "kernel_pipe.hpp"), ("mfma32d_", "kernel_deep.hpp"), ("mfma32k", "kernel_splitk.hpp"),
+                   ("mfma32r_", "kernel_direct.hpp"), ("mfma32l_", "kernel_dl.hpp"), ("mfma32_", "kernel_mfma.hpp"),
+                   ("valu_", "kernel_valu.hpp"))
+
+
+def kernel_sources(variant: str):
+    """The source files whose text determines the code a variant runs."""
+    fam = next((f for prefix, f in KERNEL_FAMILIES if variant.startswith(prefix)), None)
+    return KERNEL_COMMON + ((fam,) if fam else ())
 
 
 def _strip_variant_table(text: bytes) -> bytes:
@@ -66,11 +77,12 @@ def _strip_variant_table(text: bytes) -> bytes:
 
 
 def kernel_source_hash(variant: str) -> str:
-    """Hash of the kernel code a variant runs: the kernel templates, the launch code (without the
-    variant table) and the variant's name, which spells out its template configuration."""
+    """Hash of the kernel code a variant runs: the shared kernel pieces and its family's kernel
+    template, the launch code (without the variant table) and the variant's name, which spells out
+    its template configuration."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp32_gemm_05_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in kernel_sources(variant):
         with open(os.path.join(csrc, name), "rb") as f:
             text = f.read()
         if name == "sgemm_launch.hpp":

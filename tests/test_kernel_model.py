@@ -2,7 +2,7 @@
 every output element of C is stored exactly once, nothing outside C's M x N window
 is stored, and each MFMA accumulator receives every k of a slab exactly once.
 
-The model restates, in numpy, the addressing of sgemm_kernels.hpp (PanelLoader,
+The model restates, in numpy, the addressing of the kernel headers (PanelLoader,
 the MFMA and VALU epilogues) for each variant the library reports, over a sweep
 of shapes with ragged edges in every dimension.  It runs on the CPU and guards
 the GPU against out-of-bounds accesses before any kernel is launched.
