@@ -126,6 +126,19 @@ __device__ __attribute__((always_inline)) inline void dl_barrier() { asm volatil
 __device__ __attribute__((always_inline)) inline uint32_t lds_addr(const float* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)(p);
 }
+// Wave-uniform values the compiler cannot prove uniform (the persistent kernel's, which change
+// from tile to tile), moved into scalar registers for the loads' M0 and scalar base operands.
+// The builtin returns a signed int: each 32-bit half goes through uint32_t before it is widened,
+// or a low word with bit 31 set would fill the high word with ones.
+__device__ __attribute__((always_inline)) inline uint32_t uniform_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __attribute__((always_inline)) inline const float* uniform_ptr(const float* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = uniform_u32((uint32_t)v);
+    const uint64_t hi = uniform_u32((uint32_t)(v >> 32));
+    return reinterpret_cast<const float*>(lo | (hi << 32));
+}
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
           bool SPREAD = false>
@@ -377,6 +390,267 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     for (; s < nslab; ++s) slab(s, std::integral_constant<int, -1>{}, Checked{});
 
     mfma_epilogue<FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
+}
+
+// ---------------------------------------------------------------------------------
+// Persistent direct-to-LDS kernel: a grid-stride tile loop (the block loops of the handbook's
+// sgemm_tiled / sgemm_regblock, "Shared Memory and Register Blocking"), one workgroup per
+// resident slot.  Workgroup w runs tiles w, w + G, w + 2 G, ... (G = grid size, tile t placed by
+// tile_of exactly where the one-tile-per-workgroup kernels place workgroup t), and its slabs form
+// ONE sequence through the LDS ring across tiles: slab gs of the workgroup is slab gs % nslab of
+// its tile gs / nslab.  So the first slabs of the next tile are requested while the current tile
+// finishes, and the next tile's prologue hides under the current tile's last slabs and epilogue
+// instead of stalling a newly started workgroup.  Same loads, layout, waits and edge handling as
+// sgemm_mfma_dl_kernel; the per-lane load offsets (which depend on the tile through the M and N
+// clamps) are recomputed when the requests move to the next tile.  Every vmcnt wait also covers
+// the epilogue's C accesses issued before it, which only makes it stricter.
+// ---------------------------------------------------------------------------------
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, bool SPREAD = false>
+__global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT))
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
+sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / 8, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
+    constexpr int QA = Cfg::QPR_A, CH = Cfg::CH, E = W / 4;
+    constexpr bool VEC = W == 16;
+    static_assert(KK % 2 == 0 || KK == 1, "fragment buffers alternate per 8-deep group");
+    __shared__ __attribute__((aligned(1024))) float lds_a[STAGES * Cfg::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) float lds_b[STAGES * Cfg::B_STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / Cfg::WAVES_N) * WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+    // the arguments as local scalars: lambdas that capture the argument block itself make the
+    // compiler keep an addressable copy of it in private memory
+    const int M = g.M, N = g.N, K = g.K;
+    const long lda = g.lda, ldb = g.ldb, ldc = g.ldc;
+    const float alpha = g.alpha, beta = g.beta;
+    const float* const Ag = g.A;
+    const float* const Bg = g.B;
+    float* const Cg = g.C;
+    const int nt = tiles_m * tiles_n;
+    const int mine = (nt - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // tiles of this workgroup
+    const int nslab = (K + BK - 1) / BK;
+    const int nfull = K / BK;
+    const int total = mine * nslab;  // slabs of this workgroup
+
+    auto origin = [&](int i, int& m0, int& n0) {
+        int tm, tn;
+        tile_of((int)blockIdx.x + i * (int)gridDim.x, nt, tiles_m, tiles_n, group_m, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    };
+    auto a_kin = [&](int j) {
+        const int f = (wave * LA + j) * CH + E * lane;
+        return 4 * (((f % BK) / 4) ^ dl_swz_a<QA>(f / BK)) + f % 4;
+    };
+    auto b_kin = [&](int j) { return ((wave * LB + j) * CH + E * lane) / BN; };
+    // Per lane and load: the in-tile row (A) or column (B) and the byte offset before the M / N
+    // clamp, fixed for the whole kernel; a request applies the clamp of its tile to them.
+    int a_row[LA], b_col[LB];
+    uint32_t a_off0[LA], b_off0[LB];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int f = (wave * LA + j) * CH + E * lane;
+        a_row[j] = f / BK;
+        a_off0[j] = (uint32_t)(((long)a_row[j] * lda + a_kin(j)) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int f = (wave * LB + j) * CH + E * lane;
+        const int k = f / BN, u = (f % BN) / 4;
+        b_col[j] = 4 * (u ^ dl_swz_b(k)) + f % 4;
+        b_off0[j] = (uint32_t)(((long)k * ldb + b_col[j]) * 4);
+    }
+    // the tile whose slabs are being requested (uniform values only)
+    int req = -1, req_m0 = 0, req_n0 = 0;
+    const float* a_tile = Ag;
+    const float* b_tile = Bg;
+    auto request_tile = [&](int i) {
+        if (i == req) return;
+        req = i;
+        origin(i, req_m0, req_n0);
+        a_tile = uniform_ptr(Ag + (long)req_m0 * lda);
+        b_tile = uniform_ptr(Bg + req_n0);
+    };
+    // clamped offsets: rows past M to M - 1, columns past N to the last E-wide group
+    auto a_off = [&](int j) {
+        const int over = req_m0 + a_row[j] - (M - 1);
+        return a_off0[j] - (over > 0 ? (uint32_t)(over * lda * 4) : 0u);
+    };
+    auto b_off = [&](int j) {
+        const int over = req_n0 + b_col[j] - (N - E);
+        return b_off0[j] - (over > 0 ? (uint32_t)(over * 4) : 0u);
+    };
+    // request slab gs of the workgroup into stage gs % STAGES
+    auto issue = [&](int gs) {
+        const int i = gs / nslab, j = gs - i * nslab;
+        request_tile(i);
+        const int st = gs % STAGES, k0 = j * BK;
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
+        if (j < nfull) {
+#pragma unroll
+            for (int q = 0; q < LA; ++q)
+                dl_load<W>(uniform_ptr(a_tile + k0), a_off(q), uniform_u32(lds_addr(sa + q * CH)));
+#pragma unroll
+            for (int q = 0; q < LB; ++q)
+                dl_load<W>(uniform_ptr(b_tile + (long)k0 * ldb), b_off(q), uniform_u32(lds_addr(sb + q * CH)));
+        } else {
+#pragma unroll
+            for (int q = 0; q < LA; ++q) {
+                const int k = a_kin(q);
+                dl_load_at<W>(reinterpret_cast<const char*>(a_tile) + a_off(q) + 4L * (imin(k0 + k, K - E) - k),
+                              uniform_u32(lds_addr(sa + q * CH)));
+            }
+#pragma unroll
+            for (int q = 0; q < LB; ++q) {
+                const int k = b_kin(q);
+                dl_load_at<W>(reinterpret_cast<const char*>(b_tile) + b_off(q) + 4L * (imin(k0 + k, K - 1) - k) * ldb,
+                              uniform_u32(lds_addr(sb + q * CH)));
+            }
+        }
+    };
+    // load q of whole slab gs (request_tile must already hold the slab's tile)
+    auto issue_one = [&](int gs, int q) {
+        const int st = gs % STAGES, k0 = (gs - (gs / nslab) * nslab) * BK;
+        if (q < LA)
+            dl_load<W>(uniform_ptr(a_tile + k0), a_off(q),
+                       uniform_u32(lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH)));
+        else
+            dl_load<W>(uniform_ptr(b_tile + (long)k0 * ldb), b_off(q - LA),
+                       uniform_u32(lds_addr(lds_b + st * Cfg::B_STAGE + (wave * LB + q - LA) * CH)));
+    };
+    auto fix_tail = [&](int gs) {
+        const int st = gs % STAGES, k0 = (gs - (gs / nslab) * nslab) * BK;
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            if (k0 + a_kin(j) >= K) {
+                if (VEC)
+                    *reinterpret_cast<f32x4*>(sa + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+                else
+                    sa[j * CH + lane] = 0.f;
+            }
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            if (k0 + b_kin(j) >= K) {
+                if (VEC)
+                    *reinterpret_cast<f32x4*>(sb + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+                else
+                    sb[j * CH + lane] = 0.f;
+            }
+    };
+
+    int a_frag[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        a_frag[kk] = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
+    int b_frag[FN];
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh));
+    auto read_frag = [&](MfmaFrag<FM, FN>& f, int st, int kk) {
+        const float* sa = lds_a + st * Cfg::A_STAGE;
+        const float* sb = lds_b + st * Cfg::B_STAGE;
+#pragma unroll
+        for (int fi = 0; fi < FM; ++fi)
+            f.a[fi] = *reinterpret_cast<const f32x4*>(sa + a_frag[kk] + fi * 32 * BK);
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (8 * kk + t) * BN];
+    };
+
+    f32x16 acc[FM][FN];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    };
+    zero_acc();
+    auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
+    };
+
+    // prologue: slabs 0 .. D-1 requested; wait for slab 0
+#pragma unroll
+    for (int gs = 0; gs < D; ++gs)
+        if (gs < total) issue(gs);
+    wait_slabs<Cfg::LPW>(imin(D, total) - 1);
+    if (nfull == 0) {
+        fix_tail(0);
+        wait_vm_lgkm0<0>();
+    }
+    dl_barrier();
+    MfmaFrag<FM, FN> F[2];
+    read_frag(F[0], 0, 0);
+
+    constexpr bool SP_ON = SPREAD && D >= 2 && KK > 1;
+    constexpr int LPG = (Cfg::LPW + KK - 1) / KK;
+    auto slab = [&](int gs, auto stage) {
+        constexpr int ST = decltype(stage)::value;  // gs % STAGES
+        const int nxt = gs + D;
+        const bool sp = SP_ON && nxt < total && (nxt - (nxt / nslab) * nslab) < nfull;
+        if (sp)
+            request_tile(nxt / nslab);
+        else if (nxt < total)
+            issue(nxt);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+            read_frag(F[(kk + 1) & 1], ST, kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frag(F[kk & 1]);
+            if (SP_ON && sp) {
+#pragma unroll
+                for (int q = kk * LPG; q < (kk + 1) * LPG && q < Cfg::LPW; ++q) issue_one(nxt, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (SP_ON && sp) {
+#pragma unroll
+            for (int q = (KK - 1) * LPG; q < Cfg::LPW; ++q) issue_one(nxt, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (gs + 1 < total) {
+            wait_slabs<Cfg::LPW>(imin(gs + D, total - 1) - (gs + 1));
+            if ((gs + 1) - ((gs + 1) / nslab) * nslab >= nfull) {
+                fix_tail(gs + 1);
+                wait_vm_lgkm0<0>();
+            }
+            dl_barrier();
+            read_frag(F[0], (ST + 1) % STAGES, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_frag(F[(KK - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (gs - (gs / nslab) * nslab == nslab - 1) {  // the tile's last slab: its epilogue
+            int m0, n0;
+            origin(gs / nslab, m0, n0);
+            mfma_epilogue<FM, FN, VEC>(M, N, alpha, beta, Cg, ldc, acc, m0 + wm0, n0 + wn0, li, lh);
+            zero_acc();
+        }
+    };
+    for (int gs = 0; gs < total; ++gs) {
+        switch (gs % STAGES) {
+            case 0: slab(gs, std::integral_constant<int, 0>{}); break;
+            case 1: slab(gs, std::integral_constant<int, 1 % STAGES>{}); break;
+            case 2: slab(gs, std::integral_constant<int, 2 % STAGES>{}); break;
+            default: slab(gs, std::integral_constant<int, 3 % STAGES>{}); break;
+        }
+    }
 }
 
 }  // namespace libsgemm

@@ -23,6 +23,7 @@ struct Variant {
     int tb;    // op(B) = B^T: B stored N x K
     int bq;    // B loaded in k-quads and staged n-major in LDS (KQuadLoader; 32-bit loads only)
     int dl;    // operands loaded straight into LDS (global_load_lds), a ring of `dl` LDS stages
+    int ps;    // persistent: one workgroup per resident slot, looping over tiles
 };
 
 // 64-bit sum: a + b - 1 would overflow int for a near INT_MAX.
@@ -119,6 +120,22 @@ hipError_t launch_mfma_dl(const GemmArgs& g, hipStream_t stream) {
     void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(tiles_m * tiles_n), dim3(Cfg::NT), args, 0,
                            stream);
+}
+
+// Persistent form: one workgroup per resident slot (occupancy x CUs, at most one per tile).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, bool SPREAD = false>
+hipError_t launch_mfma_dlp(const GemmArgs& g, hipStream_t stream) {
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
+    auto kernel = &sgemm_mfma_dlp_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, SPREAD>;
+    int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
+    int group_m = group_rows(tiles_m, tiles_n);
+    static const int per_cu = occupancy(kernel, Cfg::NT);
+    const long slots = (long)(per_cu > 0 ? per_cu : 1) * (device_cus() > 0 ? device_cus() : 1);
+    const long tiles = (long)tiles_m * tiles_n;
+    const int grid = (int)(tiles < slots ? tiles : slots);
+    GemmArgs a = g;
+    void* args[] = {&a, &tiles_m, &tiles_n, &group_m};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(Cfg::NT), args, 0, stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, int FAIR = 0>
@@ -266,6 +283,11 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     DL_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, FAIR, CPRE, false, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_vec")
 #define DL_SCALAR(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
     DL_ROW(BM, BN, BK, WM, WN, STAGES, 4, OCC, FAIR, CPRE, false, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_scalar")
+// persistent grid-stride form ("_ps"): one workgroup per resident slot, tiles in a loop
+#define DLP_ROW(BM, BN, BK, WM, WN, STAGES, W, OCC, SP, NAME)                                            \
+    {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT, W == 16,                  \
+     DlCfg<BM, BN, BK, WM, WN, STAGES, W>::LDS_BYTES, &launch_mfma_dlp<BM, BN, BK, WM, WN, STAGES, W, OCC, SP>, \
+     0, 0, 0, 0, 0, STAGES, 1}
 // the same with the next slab's requests spread over the slab's 8-deep groups ("_sp")
 #define DL_SP_VARIANT(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
     DL_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, FAIR, CPRE, true, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_sp_vec")
@@ -402,5 +424,9 @@ const Variant kVariants[] = {
     DL_SP_VARIANT(128, 64, 32, 64, 32, 3, 0, 3, false, "_d3"),
     DL_SP_SCALAR(64, 64, 16, 32, 32, 3, 0, 0, false, ""),
     DL_SP_SCALAR(64, 64, 32, 32, 32, 3, 0, 3, false, "_d3"),
+    DLP_ROW(64, 64, 32, 32, 32, 3, 16, 0, true, DL_NAME(64, 64, 32, 32, 32, 3) "_ps_sp_vec"),
+    DLP_ROW(128, 128, 16, 64, 64, 4, 16, 0, true, DL_NAME(128, 128, 16, 64, 64, 4) "_ps_sp_vec"),
+    DLP_ROW(128, 128, 16, 64, 64, 4, 16, 0, false, DL_NAME(128, 128, 16, 64, 64, 4) "_ps_vec"),
+    DLP_ROW(128, 64, 32, 64, 32, 3, 16, 0, true, DL_NAME(128, 64, 32, 64, 32, 3) "_ps_sp_vec"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

@@ -154,7 +154,9 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   when n >= 14, info[13]: B is loaded four consecutive k at a time and staged with k
  *   contiguous in LDS (0/1; "_bq" variants, 32-bit loads only); when n >= 15, info[14]:
  *   the number of LDS stages of a variant that loads its operands straight from global memory
- *   into LDS (0: loads go through registers; "mfma32l_" variants, 128-bit loads only).
+ *   into LDS (0: loads go through registers; "mfma32l_" variants); when n >= 16, info[15]:
+ *   the variant is persistent, launching one workgroup per resident slot that loops over
+ *   output tiles ("_ps"; 0/1).
  *   Variants with info[11] or info[12] set serve only sgemm_op / sgemm_op_ex.
  * Returns 0, or -1 for a bad id or n < 9. */
 SGEMM_API int sgemm_variant_info(int variant, int *info, int n);

@@ -378,3 +378,133 @@ def test_dl_swizzles_are_row_permutations():
             assert sorted((np.arange(qpr) ^ dl_swz_a(r, qpr)).tolist()) == list(range(qpr))
     for k in range(64):
         assert sorted((np.arange(16) ^ dl_swz_b(k)).tolist()) == list(range(16))
+
+
+# ------------------------------------------------------------------------------------------
+# the direct-to-LDS ring: the order of requests, waits, tail fix-ups, barriers and reads
+# ------------------------------------------------------------------------------------------
+
+def dl_ring_events(stages, nslab, nfull, mine):
+    """The sequence of ring operations one wave of sgemm_mfma_dl_kernel (mine = 1) or of the
+    persistent sgemm_mfma_dlp_kernel performs, restated: ("issue", gs), ("wait", n) -- at most n
+    slabs' loads still in flight --, ("fix", gs), ("barrier",), ("read", gs) and ("epilogue", i).
+    Slab gs is slab gs % nslab of tile gs // nslab; its loads land in stage gs % stages."""
+    D = stages - 1
+    total = mine * nslab
+    ev = []
+    for gs in range(D):
+        if gs < total:
+            ev.append(("issue", gs))
+    ev.append(("wait", min(D, total) - 1))
+    if nfull == 0:
+        ev.append(("fix", 0))
+        ev.append(("wait", 0))
+    ev.append(("barrier",))
+    ev.append(("read", 0))
+    for gs in range(total):
+        if gs + D < total:
+            ev.append(("issue", gs + D))
+        ev.append(("read", gs))           # the slab's remaining 8-deep groups
+        if gs + 1 < total:
+            ev.append(("wait", min(gs + D, total - 1) - (gs + 1)))
+            if (gs + 1) % nslab >= nfull:
+                ev.append(("fix", gs + 1))
+                ev.append(("wait", 0))
+            ev.append(("barrier",))
+            ev.append(("read", gs + 1))   # the next slab's first group
+        if gs % nslab == nslab - 1:
+            ev.append(("epilogue", gs // nslab))
+    return ev
+
+
+def check_dl_ring(stages, nslab, nfull, mine):
+    """Every wave runs the same sequence, so a barrier orders each wave's operations before it
+    against every wave's operations after it.  Checks: a slab's loads have landed (and, if it
+    crosses K, been fixed up) before the barrier that precedes its first read; a stage is requested
+    again only after a barrier that follows the last read of its previous slab; every slab is
+    requested once, and read; the epilogues come once per tile, in order."""
+    ev = dl_ring_events(stages, nslab, nfull, mine)
+    total = mine * nslab
+    inflight, landed, fixed = [], set(), set()
+    last_read = {}          # slab -> index of its last read
+    last_barrier = -1
+    stage_of_req = {}       # stage -> slab last requested into it
+    requested, epis = [], []
+    for idx, e in enumerate(ev):
+        kind = e[0]
+        if kind == "issue":
+            gs = e[1]
+            st = gs % stages
+            prev = stage_of_req.get(st)
+            if prev is not None:
+                assert prev in last_read and last_read[prev] < last_barrier, (stages, nslab, nfull, mine, gs)
+            stage_of_req[st] = gs
+            inflight.append(gs)
+            requested.append(gs)
+        elif kind == "wait":
+            n = e[1]
+            while len(inflight) > max(n, 0):
+                landed.add(inflight.pop(0))
+        elif kind == "fix":
+            assert e[1] in landed and e[1] % nslab >= nfull
+            fixed.add(e[1])
+        elif kind == "barrier":
+            last_barrier = idx
+        elif kind == "read":
+            gs = e[1]
+            assert gs in landed, (stages, nslab, nfull, mine, gs)
+            if gs % nslab >= nfull:
+                assert gs in fixed
+            # the slab's data must have landed before the last barrier (other waves' loads)
+            if gs not in last_read:
+                assert ev.index(("issue", gs)) < last_barrier
+            last_read[gs] = idx
+        elif kind == "epilogue":
+            epis.append(e[1])
+    assert requested == list(range(total)) and set(last_read) == set(range(total))
+    assert epis == list(range(mine))
+
+
+@pytest.mark.parametrize("stages", [2, 3, 4])
+def test_dl_ring_protocol(stages):
+    for nslab in (1, 2, 3, 4, 5, 7, 9):
+        for tail in (False, True):
+            nfull = nslab - 1 if tail else nslab
+            for mine in (1, 2, 3, 5):
+                check_dl_ring(stages, nslab, nfull, mine)
+
+
+def test_dl_ring_model_catches_a_short_wait():
+    """The check is not vacuous: waiting for one slab fewer than the kernel does, or requesting a
+    stage one slab too early, is caught."""
+    orig = globals()["dl_ring_events"]
+
+    def short_wait(stages, nslab, nfull, mine):
+        return [("wait", e[1] + 1) if e[0] == "wait" else e for e in orig(stages, nslab, nfull, mine)]
+
+    def early_request(stages, nslab, nfull, mine):
+        ev = orig(stages, nslab, nfull, mine)
+        # move the first request that reuses a stage to before the preceding barrier
+        i = next(k for k, e in enumerate(ev) if e[0] == "issue" and e[1] >= stages)
+        j = max(k for k in range(i) if ev[k][0] == "barrier")
+        return ev[:j] + [ev[i]] + ev[j:i] + ev[i + 1:]
+
+    try:
+        for bad in (short_wait, early_request):
+            globals()["dl_ring_events"] = bad
+            with pytest.raises(AssertionError):
+                check_dl_ring(3, 6, 6, 2)
+    finally:
+        globals()["dl_ring_events"] = orig
+
+
+@pytest.mark.parametrize("nt,grid", [(1, 1), (7, 7), (8, 3), (3713, 2048), (4096, 512), (1000, 1), (1024, 1000)])
+def test_persistent_grid_stride_covers_tiles_once(nt, grid):
+    """Workgroup w of the persistent kernel runs tiles w, w + G, ... for (nt - w + G - 1) // G
+    tiles: every tile exactly once."""
+    seen = []
+    for w in range(grid):
+        mine = (nt - w + grid - 1) // grid
+        assert mine >= 1
+        seen += [w + i * grid for i in range(mine)]
+    assert sorted(seen) == list(range(nt))
