@@ -78,6 +78,7 @@ __host__ __device__ inline void tile_of(int wg, int nwg, int tiles_m, int tiles_
 }
 
 __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+__device__ inline int imax(int a, int b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------------------------
 // Slab loaders (global -> registers -> LDS).  LDS slabs are row-major with a

@@ -485,20 +485,25 @@ sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         const int over = req_n0 + b_col[j] - (N - E);
         return b_off0[j] - (over > 0 ? (uint32_t)(over * 4) : 0u);
     };
-    // request slab gs of the workgroup into stage gs % STAGES
-    auto issue = [&](int gs) {
-        const int i = gs / nslab, j = gs - i * nslab;
+    // request the whole slab at k0 of the request tile into ring stage st
+    auto issue_full = [&](int k0, int st) {
+        float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
+        float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
+#pragma unroll
+        for (int q = 0; q < LA; ++q)
+            dl_load<W>(uniform_ptr(a_tile + k0), a_off(q), uniform_u32(lds_addr(sa + q * CH)));
+#pragma unroll
+        for (int q = 0; q < LB; ++q)
+            dl_load<W>(uniform_ptr(b_tile + (long)k0 * ldb), b_off(q), uniform_u32(lds_addr(sb + q * CH)));
+    };
+    // request slab j of tile i into ring stage st
+    auto issue = [&](int i, int j, int st) {
         request_tile(i);
-        const int st = gs % STAGES, k0 = j * BK;
+        const int k0 = j * BK;
         float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
         float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
         if (j < nfull) {
-#pragma unroll
-            for (int q = 0; q < LA; ++q)
-                dl_load<W>(uniform_ptr(a_tile + k0), a_off(q), uniform_u32(lds_addr(sa + q * CH)));
-#pragma unroll
-            for (int q = 0; q < LB; ++q)
-                dl_load<W>(uniform_ptr(b_tile + (long)k0 * ldb), b_off(q), uniform_u32(lds_addr(sb + q * CH)));
+            issue_full(k0, st);
         } else {
 #pragma unroll
             for (int q = 0; q < LA; ++q) {
@@ -514,9 +519,8 @@ sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             }
         }
     };
-    // load q of whole slab gs (request_tile must already hold the slab's tile)
-    auto issue_one = [&](int gs, int q) {
-        const int st = gs % STAGES, k0 = (gs - (gs / nslab) * nslab) * BK;
+    // load q of the whole slab at k0 into stage st (request_tile must already hold the slab's tile)
+    auto issue_one = [&](int k0, int st, int q) {
         if (q < LA)
             dl_load<W>(uniform_ptr(a_tile + k0), a_off(q),
                        uniform_u32(lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH)));
@@ -524,26 +528,38 @@ sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             dl_load<W>(uniform_ptr(b_tile + (long)k0 * ldb), b_off(q - LA),
                        uniform_u32(lds_addr(lds_b + st * Cfg::B_STAGE + (wave * LB + q - LA) * CH)));
     };
-    auto fix_tail = [&](int gs) {
-        const int st = gs % STAGES, k0 = (gs - (gs / nslab) * nslab) * BK;
+    // zero the entries of tail slab j (in stage st) whose k is past K
+    auto fix_tail = [&](int j, int st) {
+        const int k0 = j * BK;
         float* sa = lds_a + st * Cfg::A_STAGE + wave * LA * CH;
         float* sb = lds_b + st * Cfg::B_STAGE + wave * LB * CH;
 #pragma unroll
-        for (int j = 0; j < LA; ++j)
-            if (k0 + a_kin(j) >= K) {
+        for (int q = 0; q < LA; ++q)
+            if (k0 + a_kin(q) >= K) {
                 if (VEC)
-                    *reinterpret_cast<f32x4*>(sa + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    *reinterpret_cast<f32x4*>(sa + q * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
                 else
-                    sa[j * CH + lane] = 0.f;
+                    sa[q * CH + lane] = 0.f;
             }
 #pragma unroll
-        for (int j = 0; j < LB; ++j)
-            if (k0 + b_kin(j) >= K) {
+        for (int q = 0; q < LB; ++q)
+            if (k0 + b_kin(q) >= K) {
                 if (VEC)
-                    *reinterpret_cast<f32x4*>(sb + j * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    *reinterpret_cast<f32x4*>(sb + q * CH + E * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
                 else
-                    sb[j * CH + lane] = 0.f;
+                    sb[q * CH + lane] = 0.f;
             }
+    };
+    // The request cursor: the next slab to request is slab rj of tile ri, into stage rst;
+    // `requested` slabs of the workgroup have been requested so far.
+    int ri = 0, rj = 0, rst = 0, requested = 0;
+    auto advance_request = [&]() {
+        ++requested;
+        rst = rst + 1 == STAGES ? 0 : rst + 1;
+        if (++rj == nslab) {
+            rj = 0;
+            ++ri;
+        }
     };
 
     int a_frag[KK];
@@ -584,13 +600,16 @@ sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
                 for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
     };
 
-    // prologue: slabs 0 .. D-1 requested; wait for slab 0
+    // prologue: the first D slabs requested; wait for slab 0
 #pragma unroll
-    for (int gs = 0; gs < D; ++gs)
-        if (gs < total) issue(gs);
+    for (int d = 0; d < D; ++d)
+        if (requested < total) {
+            issue(ri, rj, rst);
+            advance_request();
+        }
     wait_slabs<Cfg::LPW>(imin(D, total) - 1);
     if (nfull == 0) {
-        fix_tail(0);
+        fix_tail(0, 0);
         wait_vm_lgkm0<0>();
     }
     dl_barrier();
@@ -599,57 +618,96 @@ sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 
     constexpr bool SP_ON = SPREAD && D >= 2 && KK > 1;
     constexpr int LPG = (Cfg::LPW + KK - 1) / KK;
-    auto slab = [&](int gs, auto stage) {
-        constexpr int ST = decltype(stage)::value;  // gs % STAGES
-        const int nxt = gs + D;
-        const bool sp = SP_ON && nxt < total && (nxt - (nxt / nslab) * nslab) < nfull;
-        if (sp)
-            request_tile(nxt / nslab);
-        else if (nxt < total)
-            issue(nxt);
-        __builtin_amdgcn_sched_barrier(0);
+    // Tiles outside, slabs inside: the accumulators are one loop-carried set and the epilogue
+    // has one copy.  The ring stage runs on as a counter across tiles.
+    int st = 0;  // stage of the current slab
+    // The MFMAs of the slab in stage st, with the loads of the slab at rk0 into stage rs spread
+    // over its 8-deep groups (spread = true) or issued before it.
+    auto slab_mfma = [&](bool spread, int rk0, int rs) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
-            read_frag(F[(kk + 1) & 1], ST, kk + 1);
+            read_frag(F[(kk + 1) & 1], st, kk + 1);
             __builtin_amdgcn_sched_barrier(0);
             mfma_frag(F[kk & 1]);
-            if (SP_ON && sp) {
+            if (SP_ON && spread) {
 #pragma unroll
-                for (int q = kk * LPG; q < (kk + 1) * LPG && q < Cfg::LPW; ++q) issue_one(nxt, q);
+                for (int q = kk * LPG; q < (kk + 1) * LPG && q < Cfg::LPW; ++q) issue_one(rk0, rs, q);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (SP_ON && sp) {
+        if (SP_ON && spread) {
 #pragma unroll
-            for (int q = (KK - 1) * LPG; q < Cfg::LPW; ++q) issue_one(nxt, q);
+            for (int q = (KK - 1) * LPG; q < Cfg::LPW; ++q) issue_one(rk0, rs, q);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        if (gs + 1 < total) {
-            wait_slabs<Cfg::LPW>(imin(gs + D, total - 1) - (gs + 1));
-            if ((gs + 1) - ((gs + 1) / nslab) * nslab >= nfull) {
-                fix_tail(gs + 1);
-                wait_vm_lgkm0<0>();
-            }
-            dl_barrier();
-            read_frag(F[0], (ST + 1) % STAGES, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_frag(F[(KK - 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (gs - (gs / nslab) * nslab == nslab - 1) {  // the tile's last slab: its epilogue
-            int m0, n0;
-            origin(gs / nslab, m0, n0);
-            mfma_epilogue<FM, FN, VEC>(M, N, alpha, beta, Cg, ldc, acc, m0 + wm0, n0 + wn0, li, lh);
-            zero_acc();
         }
     };
-    for (int gs = 0; gs < total; ++gs) {
-        switch (gs % STAGES) {
-            case 0: slab(gs, std::integral_constant<int, 0>{}); break;
-            case 1: slab(gs, std::integral_constant<int, 1 % STAGES>{}); break;
-            case 2: slab(gs, std::integral_constant<int, 2 % STAGES>{}); break;
-            default: slab(gs, std::integral_constant<int, 3 % STAGES>{}); break;
+    for (int i = 0; i < mine; ++i) {
+        // Steady slabs j < nfull - D: slab gs + D is a whole slab of this tile (so the request tile
+        // is this tile and the cursor needs no checks), slab gs + 1 is a whole slab, and D - 1 slabs
+        // stay in flight at the wait -- a body with no branches.  At j = 0 the cursor is at slab
+        // D of this tile; the steady slabs move it on by jfast.
+        const int jfast = imax(nfull - D, 0);
+        for (int j = 0; j < jfast; ++j) {
+            const int rs = st == 0 ? STAGES - 1 : st - 1;  // stage of slab gs + D (read by slab gs - 1)
+            const int rk0 = (j + D) * BK;
+            if (!SP_ON) issue_full(rk0, rs);
+            __builtin_amdgcn_sched_barrier(0);
+            slab_mfma(true, rk0, rs);
+            const int nst = st + 1 == STAGES ? 0 : st + 1;
+            wait_vm_lgkm0<Cfg::LPW * (D - 1)>();
+            dl_barrier();
+            read_frag(F[0], nst, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frag(F[(KK - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            st = nst;
         }
+        if (jfast > 0) {
+            requested += jfast;
+            rst = (rst + jfast) % STAGES;
+            rj += jfast;
+            if (rj == nslab) {
+                rj = 0;
+                ++ri;
+            }
+        }
+        // the last slabs of the tile: requests move on to the next tile, tails, the end of the work
+        for (int j = jfast; j < nslab; ++j) {
+            const int gs = i * nslab + j;
+            // slab gs + D, the cursor's slab, if there is one: whole slabs may be spread
+            const int sk0 = rj * BK, sst = rst;
+            const bool more = requested < total;
+            const bool sp = SP_ON && more && rj < nfull;
+            if (sp) {
+                request_tile(ri);
+                advance_request();
+            } else if (more) {
+                issue(ri, rj, rst);
+                advance_request();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            slab_mfma(sp, sk0, sst);
+            const int nst = st + 1 == STAGES ? 0 : st + 1;
+            if (gs + 1 < total) {
+                // slabs requested after slab gs + 1 may stay in flight
+                wait_slabs<Cfg::LPW>(requested - (gs + 2));
+                const int nj = j + 1 == nslab ? 0 : j + 1;
+                if (nj >= nfull) {
+                    fix_tail(nj, nst);
+                    wait_vm_lgkm0<0>();
+                }
+                dl_barrier();
+                read_frag(F[0], nst, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mfma_frag(F[(KK - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            st = nst;
+        }
+        int m0, n0;
+        origin(i, m0, n0);
+        mfma_epilogue<FM, FN, VEC>(M, N, alpha, beta, Cg, ldc, acc, m0 + wm0, n0 + wn0, li, lh);
+        zero_acc();
     }
 }
 
