@@ -168,11 +168,11 @@ def sgemm_variant_name(variant: int):
 
 
 def sgemm_variant_info(variant: int) -> dict:
-    info = (ctypes.c_int * 16)()
-    if load_library().sgemm_variant_info(int(variant), info, 16) != 0:
+    info = (ctypes.c_int * 17)()
+    if load_library().sgemm_variant_info(int(variant), info, 17) != 0:
         raise ValueError(f"no variant {variant}")
     keys = ["kind", "BM", "BN", "BK", "WM_or_TM", "WN_or_TN", "threads", "vec", "lds_bytes", "wide", "ksplit",
-            "trans_a", "trans_b", "b_kquad", "dl_stages", "persistent"]
+            "trans_a", "trans_b", "b_kquad", "dl_stages", "persistent", "mfma_block"]
     d = dict(zip(keys, list(info)))
     d["kind"] = "mfma" if d["kind"] == 0 else "valu"
     d["name"] = sgemm_variant_name(variant)

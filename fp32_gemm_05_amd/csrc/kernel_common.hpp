@@ -454,6 +454,118 @@ __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N
     }
 }
 
+// 16x16x4 blocks (v_mfma_f32_16x16x4_f32): lane l brings X(l % 16, k) and Y(k, l % 16) with
+// k = l / 16, and register r of lane l holds D(4 (l / 16) + r, l % 16).  TRANS (the 128-bit
+// variants): X from B and Y from A, so register r of lane l holds C(m0 + l % 16, n0 + 4 (l / 16)
+// + r) -- four consecutive columns, one 128-bit access.  Otherwise X from A and Y from B, and
+// register r holds C(m0 + 4 (l / 16) + r, n0 + l % 16): 16 lanes along a row of C.
+template <bool TRANS>
+__device__ __attribute__((always_inline)) inline f32x4 mfma16_step(float a, float b, const f32x4& c) {
+    return TRANS ? __builtin_amdgcn_mfma_f32_16x16x4f32(b, a, c, 0, 0, 0)
+                 : __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The C values of a wave's 16x16 blocks in the accumulators' layout (li = lane % 16,
+// lh = lane / 16; entries outside the matrix are left unset).
+template <int FM, int FN, bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma16_load_c(int M, int N, const float* __restrict__ C,
+                                                                    long ldc, f32x4 (&cv)[FM][FN], int m_base,
+                                                                    int n_base, int li, int lh) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if (VEC) {
+                const int row = m_base + i * 16 + li, col = n_base + j * 16 + 4 * lh;
+                if (row < M && col < N) cv[i][j] = *reinterpret_cast<const f32x4*>(C + (long)row * ldc + col);
+            } else {
+                const int row = m_base + i * 16 + 4 * lh, col = n_base + j * 16 + li;
+                if (col >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (row + r < M) cv[i][j][r] = C[(long)(row + r) * ldc + col];
+            }
+        }
+}
+
+// C := alpha * acc + beta * C over a wave's 16x16 blocks (C not read when beta == 0).  All C
+// values are loaded before the first store (four registers a block), or come from cv (PRE).
+template <int FM, int FN, bool VEC, bool PRE = false>
+__device__ __attribute__((always_inline)) inline void mfma16_epilogue(int M, int N, float alpha, float beta,
+                                                                      float* __restrict__ C, long ldc,
+                                                                      const f32x4 (&acc)[FM][FN], int m_base,
+                                                                      int n_base, int li, int lh,
+                                                                      const f32x4 (*cv)[FN] = nullptr) {
+    f32x4 cl[FM][FN];
+    if (!PRE && beta != 0.f) mfma16_load_c<FM, FN, VEC>(M, N, C, ldc, cl, m_base, n_base, li, lh);
+    const f32x4 (*cs)[FN] = PRE ? cv : cl;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if (VEC) {
+                // N % 4 == 0 and col % 4 == 0: the 4 columns are all inside or all outside
+                const int row = m_base + i * 16 + li, col = n_base + j * 16 + 4 * lh;
+                if (row >= M || col >= N) continue;
+                f32x4 v = alpha * acc[i][j];
+                if (beta != 0.f) v += beta * cs[i][j];
+                *reinterpret_cast<f32x4*>(C + (long)row * ldc + col) = v;
+            } else {
+                const int row = m_base + i * 16 + 4 * lh, col = n_base + j * 16 + li;
+                if (col >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (row + r < M) {
+                        float x = alpha * acc[i][j][r];
+                        if (beta != 0.f) x += beta * cs[i][j][r];
+                        C[(long)(row + r) * ldc + col] = x;
+                    }
+            }
+        }
+}
+
+// The accumulator type and the step, C load and epilogue of MFMA blocks of edge MB.
+template <int MB>
+struct MfmaBlock;
+template <>
+struct MfmaBlock<32> {
+    using acc_t = f32x16;
+    static constexpr int NR = 16;  // accumulator registers per block
+};
+template <>
+struct MfmaBlock<16> {
+    using acc_t = f32x4;
+    static constexpr int NR = 4;
+};
+template <int MB, bool TRANS>
+__device__ __attribute__((always_inline)) inline typename MfmaBlock<MB>::acc_t mfma_block_step(
+    float a, float b, const typename MfmaBlock<MB>::acc_t& c) {
+    if constexpr (MB == 32)
+        return mfma_step<TRANS>(a, b, c);
+    else
+        return mfma16_step<TRANS>(a, b, c);
+}
+template <int MB, int FM, int FN, bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma_block_load_c(int M, int N, const float* __restrict__ C,
+                                                                        long ldc,
+                                                                        typename MfmaBlock<MB>::acc_t (&cv)[FM][FN],
+                                                                        int m_base, int n_base, int li, int lh) {
+    if constexpr (MB == 32)
+        mfma_load_c<FM, FN, VEC>(M, N, C, ldc, cv, m_base, n_base, li, lh);
+    else
+        mfma16_load_c<FM, FN, VEC>(M, N, C, ldc, cv, m_base, n_base, li, lh);
+}
+template <int MB, int FM, int FN, bool VEC, bool PRE = false>
+__device__ __attribute__((always_inline)) inline void mfma_block_epilogue(
+    int M, int N, float alpha, float beta, float* __restrict__ C, long ldc,
+    const typename MfmaBlock<MB>::acc_t (&acc)[FM][FN], int m_base, int n_base, int li, int lh,
+    const typename MfmaBlock<MB>::acc_t (*cv)[FN] = nullptr) {
+    if constexpr (MB == 32)
+        mfma_epilogue<FM, FN, VEC, PRE>(M, N, alpha, beta, C, ldc, acc, m_base, n_base, li, lh, cv);
+    else
+        mfma16_epilogue<FM, FN, VEC, PRE>(M, N, alpha, beta, C, ldc, acc, m_base, n_base, li, lh, cv);
+}
+
 // Drain ordering.  A SIMD issues from its highest-priority ready wave, oldest first among equals,
 // so of the workgroups sharing a CU the oldest runs nearly alone and finishes first; in a grid's
 // last round nothing refills the freed slots, and the last workgroup ends up alone on its CU, where

@@ -38,13 +38,25 @@ __device__ __host__ inline int dl_swz_a(int r) {  // swizzle of A row r (QPR qua
     return QPR == 16 ? r & 15
                      : QPR == 8 ? ((r & 15) + ((r >> 3) & 1)) & 7 : (((r >> 1) & 7) + ((r >> 3) & 1)) & 3;
 }
-__device__ __host__ inline int dl_swz_b(int k) { return ((k >> 2) & 1) * 8; }  // swizzle of B row k, in quads
+// Swizzle of B row k, in quads, for MFMA blocks of MB columns: a B fragment read takes rows
+// 4 h + t (t fixed) of the 64 / MB lane groups h at MB consecutive columns, and the swizzle
+// flips the column by MB h on those rows (quad bit 3 for 32x32 blocks; quad bits 2-3 for
+// 16x16 blocks), putting the groups on distinct banks.
+template <int MB = 32>
+__device__ __host__ inline int dl_swz_b(int k) {
+    static_assert(MB == 32 || MB == 16, "32x32 or 16x16 MFMA blocks");
+    return ((k >> 2) & (64 / MB - 1)) * (MB / 4);
+}
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W = 16>
+// MB: edge of the MFMA blocks (32: v_mfma_f32_32x32x2_f32; 16: v_mfma_f32_16x16x4_f32, whose
+// smaller wave tiles let a workgroup of one tile hold more waves).  A fragment group spans
+// KG = 4 (64 / MB) k: each of the 64 / MB lane groups of a wave brings one k-quad.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W = 16, int MB = 32>
 struct DlCfg {
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
-    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int FM = WM / MB, FN = WN / MB;
+    static constexpr int KG = 4 * (64 / MB);                      // k of one fragment group
     static constexpr int QPR_A = BK / 4, QPR_B = BN / 4;           // 16-byte quads per row
     static constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;     // floats
     static constexpr int CH = 16 * W;                              // floats one wave's load fills
@@ -56,7 +68,9 @@ struct DlCfg {
     static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
     static_assert(A_STAGE % (CH * NW) == 0 && B_STAGE % (CH * NW) == 0, "whole loads per wave");
     static_assert(BN % 64 == 0, "the B swizzle needs rows of 16 quads or more");
-    static_assert(BK % 8 == 0 && BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiling");
+    static_assert(MB == 32 || MB == 16, "32x32 or 16x16 MFMA blocks");
+    static_assert(BK % KG == 0 && BM % WM == 0 && BN % WN == 0 && WM % MB == 0 && WN % MB == 0, "tiling");
+    static_assert(NT <= 1024, "workgroup size");
     static_assert(LPW * D < 64, "vmcnt counts at most 63 loads in flight");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
@@ -141,15 +155,17 @@ __device__ __attribute__((always_inline)) inline const float* uniform_ptr(const 
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
-          bool SPREAD = false>
-__global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT))
+          bool SPREAD = false, int MB = 32>
+__global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / 8, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>;
+    using Acc = typename MfmaBlock<MB>::acc_t;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / Cfg::KG, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
     constexpr int QA = Cfg::QPR_A, QB = Cfg::QPR_B, CH = Cfg::CH, E = W / 4;  // E: floats per lane load
+    constexpr int G = 64 / MB;                                                // lane groups of a wave
     constexpr bool VEC = W == 16;
-    static_assert(KK % 2 == 0 || KK == 1, "fragment buffers alternate per 8-deep group");
+    static_assert(KK % 2 == 0 || KK == 1, "fragment buffers alternate per fragment group");
     __shared__ __attribute__((aligned(1024))) float lds_a[STAGES * Cfg::A_STAGE];
     __shared__ __attribute__((aligned(1024))) float lds_b[STAGES * Cfg::B_STAGE];
 
@@ -161,7 +177,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / Cfg::WAVES_N) * WM;
     const int wn0 = (wave % Cfg::WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
+    const int li = lane % MB, lh = lane / MB;  // lane within its group, lane group
     const int M = g.M, N = g.N, K = g.K;
     const long lda = g.lda, ldb = g.ldb;
 
@@ -187,7 +203,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     for (int j = 0; j < LB; ++j) {
         const int f = (wave * LB + j) * CH + E * lane;
         const int k = f / BN, u = (f % BN) / 4;
-        const int n = imin(n0 + 4 * (u ^ dl_swz_b(k)) + f % 4, N - E) - n0;
+        const int n = imin(n0 + 4 * (u ^ dl_swz_b<MB>(k)) + f % 4, N - E) - n0;
         b_off[j] = (uint32_t)(((long)k * ldb + n) * 4);
     }
     const float* a_tile = g.A + (long)m0 * lda;  // A(m0, 0)
@@ -255,43 +271,43 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             }
     };
 
-    // Fragment reads: A's quad 2 kk + h of row wm0 + 32 fi + li sits at quad ((2 kk + h) ^ swz) of
-    // that row (the swizzle depends on the row's low four bits only, so not on fi); B's element
-    // (k, n) with k = 8 kk + 4 h + t sits at column n ^ 32 h of row k (the B swizzle flips quad bit
-    // 3, i.e. column bit 5, on rows with bit 2 set).
+    // Fragment reads (fragment group kk: k = KG kk + 4 h + t for lane group h and step t): A's
+    // quad G kk + h of row wm0 + MB fi + li sits at quad ((G kk + h) ^ swz) of that row (the
+    // swizzle depends on the row's low four bits only, so not on fi); B's element (k, n) sits at
+    // column n ^ MB h of row k (the B swizzle of row k is MB ((k >> 2) % G) columns).
     int a_frag[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-        a_frag[kk] = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
+        a_frag[kk] = (wm0 + li) * BK + 4 * ((G * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
     int b_frag[FN];
 #pragma unroll
-    for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh));
+    for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * MB + li) ^ (MB * lh));
     auto read_frag = [&](MfmaFrag<FM, FN>& f, int st, int kk) {
         const float* sa = lds_a + st * Cfg::A_STAGE;
         const float* sb = lds_b + st * Cfg::B_STAGE;
 #pragma unroll
         for (int fi = 0; fi < FM; ++fi)
-            f.a[fi] = *reinterpret_cast<const f32x4*>(sa + a_frag[kk] + fi * 32 * BK);
+            f.a[fi] = *reinterpret_cast<const f32x4*>(sa + a_frag[kk] + fi * MB * BK);
 #pragma unroll
         for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (8 * kk + t) * BN];
+            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (Cfg::KG * kk + t) * BN];
     };
 
-    f32x16 acc[FM][FN];
+    Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < MfmaBlock<MB>::NR; ++r) acc[i][j][r] = 0.f;
     auto mfma_frag = [&](const MfmaFrag<FM, FN>& f) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_block_step<MB, VEC>(f.a[i][t], f.b[j][t], acc[i][j]);
     };
 
     const int nslab = (K + BK - 1) / BK;
@@ -299,8 +315,8 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Tail = std::integral_constant<bool, true>;
     using Whole = std::integral_constant<bool, false>;
     // the C values of the beta term first: the oldest loads, consumed only by the epilogue
-    f32x16 cv[FM][FN];
-    if (CPRE && g.beta != 0.f) mfma_load_c<FM, FN, VEC>(M, N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
+    Acc cv[FM][FN];
+    if (CPRE && g.beta != 0.f) mfma_block_load_c<MB, FM, FN, VEC>(M, N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
     // prologue: slabs 0 .. D-1 requested; wait for slab 0 (the later ones may stay in flight)
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -321,7 +337,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     // Slab s (stage ST = s % STAGES when known at compile time, else -1).  FULL: slab s + D exists
     // and is whole, so the wait before the next barrier leaves exactly D - 1 slabs in flight.
     // SPREAD (whole slabs, rings of three or more stages): the requests for slab s + D are issued
-    // LPG at a time after each 8-deep group's MFMAs instead of all at the top of the slab, so that
+    // LPG at a time after each fragment group's MFMAs instead of all at the top of the slab, so that
     // they issue in the matrix pipe's shadow.  It pays at one wave per SIMD on L2-resident operands
     // (per-wave timestamps at 1024^3: 1103 against 1169 cycles per 16-MFMA slab), and costs where
     // the last requests, issued at the end of the slab, then have one slab instead of two to land
@@ -389,7 +405,8 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     }
     for (; s < nslab; ++s) slab(s, std::integral_constant<int, -1>{}, Checked{});
 
-    mfma_epilogue<FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
+    mfma_block_epilogue<MB, FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh,
+                                              cv);
 }
 
 // ---------------------------------------------------------------------------------

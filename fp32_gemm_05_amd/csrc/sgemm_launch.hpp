@@ -24,6 +24,7 @@ struct Variant {
     int bq;    // B loaded in k-quads and staged n-major in LDS (KQuadLoader; 32-bit loads only)
     int dl;    // operands loaded straight into LDS (global_load_lds), a ring of `dl` LDS stages
     int ps;    // persistent: one workgroup per resident slot, looping over tiles
+    int mb;    // MFMA block edge: 0 for 32x32 blocks (or a VALU kernel), 16 for 16x16 blocks
 };
 
 // 64-bit sum: a + b - 1 would overflow int for a near INT_MAX.
@@ -106,10 +107,10 @@ hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
-          bool SPREAD = false>
+          bool SPREAD = false, int MB = 32>
 hipError_t launch_mfma_dl(const GemmArgs& g, hipStream_t stream) {
-    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
-    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SPREAD>;
+    using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>;
+    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SPREAD, MB>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -283,6 +284,17 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
     DL_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, FAIR, CPRE, false, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_vec")
 #define DL_SCALAR(BM, BN, BK, WM, WN, STAGES, OCC, FAIR, CPRE, SUFFIX) \
     DL_ROW(BM, BN, BK, WM, WN, STAGES, 4, OCC, FAIR, CPRE, false, DL_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_scalar")
+// 16x16x4 MFMA blocks ("mfma16l_"): the same kernel with smaller wave tiles, so that a one-tile
+// workgroup holds 8 or 16 waves
+#define DL16_ROW(BM, BN, BK, WM, WN, STAGES, W, OCC, CPRE, SP, NAME)                                      \
+    {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W, 16>::NT, W == 16,              \
+     DlCfg<BM, BN, BK, WM, WN, STAGES, W, 16>::LDS_BYTES,                                                 \
+     &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, W, OCC, 0, CPRE, SP, 16>, 0, 0, 0, 0, 0, STAGES, 0, 16}
+#define DL16_NAME(BM, BN, BK, WM, WN, STAGES) "mfma16l_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #STAGES
+#define DL16_VARIANT(BM, BN, BK, WM, WN, STAGES, OCC, CPRE, SP, SUFFIX) \
+    DL16_ROW(BM, BN, BK, WM, WN, STAGES, 16, OCC, CPRE, SP, DL16_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_vec")
+#define DL16_SCALAR(BM, BN, BK, WM, WN, STAGES, OCC, CPRE, SP, SUFFIX) \
+    DL16_ROW(BM, BN, BK, WM, WN, STAGES, 4, OCC, CPRE, SP, DL16_NAME(BM, BN, BK, WM, WN, STAGES) SUFFIX "_scalar")
 // persistent grid-stride form ("_ps"): one workgroup per resident slot, tiles in a loop
 #define DLP_ROW(BM, BN, BK, WM, WN, STAGES, W, OCC, SP, NAME)                                            \
     {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT, W == 16,                  \
@@ -428,5 +440,17 @@ const Variant kVariants[] = {
     DLP_ROW(128, 128, 16, 64, 64, 4, 16, 0, true, DL_NAME(128, 128, 16, 64, 64, 4) "_ps_sp_vec"),
     DLP_ROW(128, 128, 16, 64, 64, 4, 16, 0, false, DL_NAME(128, 128, 16, 64, 64, 4) "_ps_vec"),
     DLP_ROW(128, 64, 32, 64, 32, 3, 16, 0, true, DL_NAME(128, 64, 32, 64, 32, 3) "_ps_sp_vec"),
+    // 16x16x4 blocks: 64x64 tiles of 8 waves (two per SIMD) or 16 waves, and 128-wide tiles of 8 or
+    // 16 waves of 32x32
+    DL16_VARIANT(64, 64, 32, 32, 16, 3, 0, true, false, "_cp"),
+    DL16_VARIANT(64, 64, 32, 16, 32, 3, 0, true, false, "_cp"),
+    DL16_VARIANT(64, 64, 32, 32, 16, 3, 0, true, true, "_cp_sp"),
+    DL16_VARIANT(64, 64, 32, 32, 16, 2, 0, true, false, "_cp"),
+    DL16_VARIANT(64, 64, 64, 16, 16, 3, 0, true, false, "_cp"),
+    DL16_VARIANT(64, 64, 32, 32, 32, 3, 0, true, false, "_cp"),
+    DL16_VARIANT(128, 64, 32, 32, 32, 3, 0, false, false, ""),
+    DL16_VARIANT(128, 128, 32, 32, 32, 3, 0, false, false, ""),
+    DL16_SCALAR(64, 64, 32, 32, 16, 3, 0, false, false, ""),
+    DL16_SCALAR(64, 64, 32, 32, 16, 3, 0, false, true, "_sp"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

@@ -144,7 +144,7 @@ SGEMM_API int sgemm_num_variants(void);
 SGEMM_API const char *sgemm_variant_name(int variant);
 
 /* Tile parameters of a variant, written to info[0 .. n-1] (n >= 9):
- *   info[0] kind (0 = MFMA 32x32x2 f32, 1 = vector FMA), info[1] BM, info[2] BN,
+ *   info[0] kind (0 = MFMA, 1 = vector FMA), info[1] BM, info[2] BN,
  *   info[3] BK, info[4] WM (MFMA wave tile rows) or TM (VALU microtile rows),
  *   info[5] WN or TN, info[6] threads per workgroup, info[7] vector loads (0/1),
  *   info[8] LDS bytes per workgroup (0 for the LDS-free variants "mfma32r_", whose BK
@@ -156,7 +156,9 @@ SGEMM_API const char *sgemm_variant_name(int variant);
  *   the number of LDS stages of a variant that loads its operands straight from global memory
  *   into LDS (0: loads go through registers; "mfma32l_" variants); when n >= 16, info[15]:
  *   the variant is persistent, launching one workgroup per resident slot that loops over
- *   output tiles ("_ps"; 0/1).
+ *   output tiles ("_ps"; 0/1); when n >= 17, info[16]: the edge of the MFMA blocks, 32
+ *   (v_mfma_f32_32x32x2_f32) or 16 (v_mfma_f32_16x16x4_f32, "mfma16l_" variants), 0 for
+ *   the vector-FMA variants.
  *   Variants with info[11] or info[12] set serve only sgemm_op / sgemm_op_ex.
  * Returns 0, or -1 for a bad id or n < 9. */
 SGEMM_API int sgemm_variant_info(int variant, int *info, int n);

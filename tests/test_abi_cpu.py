@@ -46,7 +46,12 @@ def test_version_and_variants():
     for i in range(n):
         info = sg.sgemm_variant_info(i)
         kinds.add(info["kind"])
-        assert info["name"].startswith("mfma32" if info["kind"] == "mfma" else "valu_")
+        if info["kind"] == "mfma":
+            # the name's prefix gives the MFMA block edge
+            assert info["name"].startswith(f"mfma{info['mfma_block']}")
+            assert info["mfma_block"] in (32, 16)
+        else:
+            assert info["name"].startswith("valu_") and info["mfma_block"] == 0
         assert f"{info['BM']}x{info['BN']}x{info['BK']}" in info["name"]
         assert info["name"].endswith("_vec") == bool(info["vec"])
         assert info["threads"] % 64 == 0 and info["threads"] <= 1024
@@ -173,15 +178,15 @@ def _name(v):
     (333, 555, 777, True, "direct"),
     (1554, 64, 5093, True, "direct"),     # skinny with few tiles joins the small classes
     (1024, 1024, 1024, False, "lds"),     # small, aligned: 64x64 workgroups fill the CUs
-    (1001, 1003, 777, True, "direct"),    # small, unaligned
+    (1001, 1003, 777, True, "lds"),       # small, unaligned: 16x16-block workgroups of 8 waves
     (1111, 1113, 1001, True, "lds"),      # small_full: more than one 64x64 tile per CU
-    (1089, 728, 5752, False, "direct"),   # small_longk, aligned
+    (1089, 728, 5752, False, "lds"),      # small_longk, aligned: the direct-to-LDS ring
     (4096, 4096, 4096, False, "lds"),
     (65536, 64, 1024, False, "lds"),      # skinny
 ])
 def test_dispatch_families(M, N, K, ld_odd, family):
-    """Which kernel family the shape classes pick: the LDS-free kernel (mfma32r_) for tiny grids,
-    unaligned small ones and long-K small aligned ones; LDS kernels elsewhere."""
+    """Which kernel family the shape classes pick: the LDS-free kernel (mfma32r_) for tiny grids
+    and skinny ones with few tiles; LDS kernels elsewhere."""
     lda, ldb = (K | 1, N | 1) if ld_odd else (K, N)
     v = sg.sgemm_select_variant(M, N, K, FAKE_A, lda, FAKE_B, ldb, FAKE_C, ldb)
     assert v >= 0

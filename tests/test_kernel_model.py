@@ -116,6 +116,11 @@ def check_loads_in_bounds(v, M, N, K):
             assert (r >= 0).all() and (r < rows).all() and (c >= 0).all() and (c + W <= cols).all()
 
 
+def mfma_block(v):
+    """Edge of a variant's MFMA blocks (32 or 16)."""
+    return v.get("mfma_block") or 32
+
+
 def stored_elements(v, M, N):
     """All (row, col) the epilogue stores, over every workgroup of the launch.
 
@@ -131,15 +136,25 @@ def stored_elements(v, M, N):
         waves_n = BN // WN
         lane, wave = tid % 64, tid // 64
         wm0, wn0 = (wave // waves_n) * WM, (wave % waves_n) * WN
-        li, lh = lane % 32, lane // 32
         local = []
-        for i, j, r in itertools.product(range(WM // 32), range(WN // 32), range(16)):
-            if v["vec"]:
-                # blocks accumulated transposed: register r holds row li, column 8*(r/4) + 4*lh + r%4
-                local.append((wm0 + i * 32 + li, wn0 + j * 32 + (r // 4) * 8 + lh * 4 + (r % 4)))
-            else:
-                # upright blocks: register r holds row 8*(r/4) + 4*lh + r%4, column li
-                local.append((wm0 + i * 32 + (r // 4) * 8 + lh * 4 + (r % 4), wn0 + j * 32 + li))
+        if mfma_block(v) == 32:
+            li, lh = lane % 32, lane // 32
+            for i, j, r in itertools.product(range(WM // 32), range(WN // 32), range(16)):
+                if v["vec"]:
+                    # blocks accumulated transposed: register r holds row li, column 8*(r/4) + 4*lh + r%4
+                    local.append((wm0 + i * 32 + li, wn0 + j * 32 + (r // 4) * 8 + lh * 4 + (r % 4)))
+                else:
+                    # upright blocks: register r holds row 8*(r/4) + 4*lh + r%4, column li
+                    local.append((wm0 + i * 32 + (r // 4) * 8 + lh * 4 + (r % 4), wn0 + j * 32 + li))
+        else:
+            li, lh = lane % 16, lane // 16
+            for i, j, r in itertools.product(range(WM // 16), range(WN // 16), range(4)):
+                if v["vec"]:
+                    # 16x16 blocks transposed: register r holds row li, column 4*lh + r
+                    local.append((wm0 + i * 16 + li, wn0 + j * 16 + 4 * lh + r))
+                else:
+                    # upright: register r holds row 4*lh + r, column li
+                    local.append((wm0 + i * 16 + 4 * lh + r, wn0 + j * 16 + li))
     else:
         TM, TN = v["WM_or_TM"], v["WN_or_TN"]
         TX = BN // TN
@@ -272,8 +287,11 @@ def dl_swz_a(r, qpr):
     return ((r & 15) + ((r >> 3) & 1)) & 7 if qpr == 8 else (((r >> 1) & 7) + ((r >> 3) & 1)) & 3
 
 
-def dl_swz_b(k):
-    return ((np.asarray(k) >> 2) & 1) * 8
+def dl_swz_b(k, mb=32):
+    """B row k's swizzle in quads for MFMA blocks of edge mb: column flip of mb * ((k >> 2) % G),
+    G = 64 / mb lane groups."""
+    return ((np.asarray(k) >> 2) & (64 // mb - 1)) * (mb // 4)
+
 
 
 DL = [v for v in VARIANTS if v.get("dl_stages")]
@@ -286,6 +304,7 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
     operand.  128-bit variants load W = 16 bytes per lane (a quad), 32-bit ones W = 4."""
     BM, BN, BK, NT = v["BM"], v["BN"], v["BK"], v["threads"]
     NW = NT // 64
+    MB = mfma_block(v)
     E = 4 if v["vec"] else 1          # floats per lane load
     CH = 64 * E                       # floats one wave's load fills
     QA = BK // 4
@@ -312,7 +331,7 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
             f = (wave * LB + j) * CH + E * lane
             kr = f // BN
             u = (f % BN) // 4
-            n = np.minimum(n0 + 4 * (u ^ dl_swz_b(kr)) + f % 4, N - E)
+            n = np.minimum(n0 + 4 * (u ^ dl_swz_b(kr, MB)) + f % 4, N - E)
             k = k0 + kr
             kl = np.minimum(k, K - 1) if tail else k
             assert (kl >= 0).all() and (kl < K).all() and (n >= 0).all() and (n + E <= N).all()
@@ -327,15 +346,18 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
 def test_dl_kernel_loads_and_fragments(v):
     """sgemm_mfma_dl_kernel's loads stay inside A and B (rows past M and columns past N clamped, k
     of the slab that crosses K clamped), every LDS element of a stage is written, and the fragment
-    read of lane (i, h), block (fi, fj), 8-deep group kk and step t -- at the kernel's swizzled
-    offsets -- returns A(m0 + wm0 + 32 fi + i, k) and B(k, n0 + wn0 + 32 fj + i) with
-    k = k0 + 8 kk + 4 h + t (rows/columns clamped at the edges), or a zero past K."""
+    read of lane (i, h) (i = lane % MB, h = lane / MB for MFMA blocks of edge MB), block (fi, fj),
+    fragment group kk and step t -- at the kernel's swizzled offsets -- returns
+    A(m0 + wm0 + MB fi + i, k) and B(k, n0 + wn0 + MB fj + i) with k = k0 + KG kk + 4 h + t
+    (KG = 4 * 64 / MB; rows/columns clamped at the edges), or a zero past K."""
     BM, BN, BK, NT = v["BM"], v["BN"], v["BK"], v["threads"]
     WM, WN = v["WM_or_TM"], v["WN_or_TN"]
+    MB = mfma_block(v)
+    G, KG = 64 // MB, 4 * 64 // MB
     waves_n = BN // WN
     QA = BK // 4
     lane = np.arange(64)
-    li, lh = lane % 32, lane // 32
+    li, lh = lane % MB, lane // MB
     for (M, N, K) in [(64, 64, 32), (200, 136, 100), (131, 68, 36), (257, 260, 8), (1, 4, 4), (70, 67, 37),
                       (3, 130, 1), (129, 65, 130)]:
         if v["vec"] and (N % 4 or K % 4):
@@ -348,26 +370,26 @@ def test_dl_kernel_loads_and_fragments(v):
                     k0 = s * BK
                     for wave in range(NT // 64):
                         wm0, wn0 = (wave // waves_n) * WM, (wave % waves_n) * WN
-                        for kk in range(BK // 8):
-                            a_frag = (wm0 + li) * BK + 4 * ((2 * kk + lh) ^ dl_swz_a(wm0 + li, QA))
-                            for fi in range(WM // 32):
+                        for kk in range(BK // KG):
+                            a_frag = (wm0 + li) * BK + 4 * ((G * kk + lh) ^ dl_swz_a(wm0 + li, QA))
+                            for fi in range(WM // MB):
                                 for t in range(4):
-                                    got = a_lds[a_frag + fi * 32 * BK + t]
-                                    k = k0 + 8 * kk + 4 * lh + t
-                                    row = np.minimum(tm * BM + wm0 + 32 * fi + li, M - 1)
+                                    got = a_lds[a_frag + fi * MB * BK + t]
+                                    k = k0 + KG * kk + 4 * lh + t
+                                    row = np.minimum(tm * BM + wm0 + MB * fi + li, M - 1)
                                     want_r = np.where(k < K, row, -1)
                                     want_k = np.where(k < K, k, -1)
                                     assert (got[:, 0] == want_r).all() and (got[:, 1] == want_k).all()
-                            for fj in range(WN // 32):
-                                b_frag = 4 * lh * BN + ((wn0 + fj * 32 + li) ^ (32 * lh))
+                            for fj in range(WN // MB):
+                                b_frag = 4 * lh * BN + ((wn0 + fj * MB + li) ^ (MB * lh))
                                 for t in range(4):
-                                    got = b_lds[b_frag + (8 * kk + t) * BN]
-                                    k = k0 + 8 * kk + 4 * lh + t
-                                    col = np.minimum(tn * BN + wn0 + 32 * fj + li, N - 1)
+                                    got = b_lds[b_frag + (KG * kk + t) * BN]
+                                    k = k0 + KG * kk + 4 * lh + t
+                                    col = np.minimum(tn * BN + wn0 + MB * fj + li, N - 1)
                                     # columns past N read a clamped column of the last 4-column
                                     # group (128-bit loads) or column N - 1 (32-bit loads)
                                     ok = (got[:, 1] == col) | \
-                                         ((tn * BN + wn0 + 32 * fj + li >= N) & (got[:, 1] >= N - 4))
+                                         ((tn * BN + wn0 + MB * fj + li >= N) & (got[:, 1] >= N - 4))
                                     assert (np.where(k < K, ok, got[:, 1] == -1)).all()
                                     assert (got[:, 0] == np.where(k < K, k, -1)).all()
 
@@ -376,8 +398,57 @@ def test_dl_swizzles_are_row_permutations():
     for qpr in (4, 8, 16):
         for r in range(64):
             assert sorted((np.arange(qpr) ^ dl_swz_a(r, qpr)).tolist()) == list(range(qpr))
-    for k in range(64):
-        assert sorted((np.arange(16) ^ dl_swz_b(k)).tolist()) == list(range(16))
+    for mb in (32, 16):
+        for k in range(64):
+            assert sorted((np.arange(16) ^ dl_swz_b(k, mb)).tolist()) == list(range(16))
+
+
+def lds_read_passes(addr_bytes, width, banks):
+    """Bank conflicts of one LDS read by 64 lanes: lanes go through in passes of
+    banks * 4 / width lanes; within a pass, the extra cycles are the largest number of distinct
+    4-byte words that one bank must deliver, minus one, summed over the passes."""
+    per_pass = banks * 4 // width
+    extra = 0
+    for p0 in range(0, 64, per_pass):
+        words = {}
+        for a in addr_bytes[p0:p0 + per_pass]:
+            for w in range(width // 4):
+                word = a // 4 + w
+                words.setdefault(word % banks, set()).add(word)
+        extra += max(len(x) for x in words.values()) - 1
+    return extra
+
+
+@pytest.mark.parametrize("banks", [64, 32])
+@pytest.mark.parametrize("v", DL, ids=[v["name"] for v in DL])
+def test_dl_fragment_reads_are_conflict_free(v, banks):
+    """Every fragment read of sgemm_mfma_dl_kernel -- the 128-bit A reads (MB consecutive rows of
+    a lane group at one quad) and the 32-bit B reads (rows KG kk + 4 h + t of the lane groups at
+    MB consecutive columns) -- is free of bank conflicts, with 64 banks and 16 lanes per 128-bit
+    pass and with 32 banks and 8 lanes per pass."""
+    BN, BK, WM, WN = v["BN"], v["BK"], v["WM_or_TM"], v["WN_or_TN"]
+    MB = mfma_block(v)
+    G, KG = 64 // MB, 4 * 64 // MB
+    lane = np.arange(64)
+    li, lh = lane % MB, lane // MB
+    for wave in range(v["threads"] // 64):
+        wm0, wn0 = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
+        for kk in range(BK // KG):
+            for fi in range(WM // MB):
+                a = 4 * ((wm0 + li + MB * fi) * BK + 4 * ((G * kk + lh) ^ dl_swz_a(wm0 + li, BK // 4)))
+                assert lds_read_passes(a.tolist(), 16, banks) == 0
+            for fj in range(WN // MB):
+                for t in range(4):
+                    b = 4 * ((KG * kk + 4 * lh + t) * BN + ((wn0 + fj * MB + li) ^ (MB * lh)))
+                    assert lds_read_passes(b.tolist(), 4, banks) == 0
+
+
+def test_lds_bank_model_sees_a_conflict():
+    """The bank model above reports the conflict of the unswizzled 16x16 B read (rows 4 h + t of
+    four lane groups at the same 16 columns of 64-float rows share their banks)."""
+    lane = np.arange(64)
+    b = 4 * ((4 * (lane // 16)) * 64 + lane % 16)
+    assert lds_read_passes(b.tolist(), 4, 64) == 3
 
 
 # ------------------------------------------------------------------------------------------
