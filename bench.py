@@ -69,6 +69,17 @@ def stored_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def resolve_variant(sg, spec: str) -> int:
+    """A --variant argument as a variant id: an id, a variant name, or -1 (dispatch)."""
+    spec = str(spec).strip()
+    if spec.lstrip("-").isdigit():
+        return int(spec)
+    for i in range(sg.sgemm_num_variants()):
+        if sg.sgemm_variant_name(i) == spec:
+            return i
+    raise SystemExit(f"bench.py: no kernel variant named {spec!r}")
+
+
 def host_cpu_model() -> str | None:
     try:
         with open("/proc/cpuinfo") as f:
@@ -234,7 +245,7 @@ def main() -> int:
     ap.add_argument("--preroll", type=float, default=1.0, metavar="SECONDS",
                     help="seconds of back-to-back steps before the warmup (reported in the line; 0: none)")
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant id (default: dispatch)")
+    ap.add_argument("--variant", default="-1", help="force a kernel variant, by id or name (default: dispatch)")
     ap.add_argument("--op", default="NN", choices=["NN", "NT", "TN", "TT"],
                     help="storage of A and B: op(A) op(B), T = stored transposed (sgemm_op)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -288,8 +299,8 @@ def main() -> int:
     dA = torch.from_numpy(As).to(dev)
     dB = torch.from_numpy(Bs).to(dev)
     dC = torch.from_numpy(C0).to(dev)
-    vid = args.variant if args.variant >= 0 else sg.sgemm_op_select_variant(
-        ta, tb, w.M, w.N, w.K, dA, lda, dB, ldb, dC, w.N)
+    forced = resolve_variant(sg, args.variant)
+    vid = forced if forced >= 0 else sg.sgemm_op_select_variant(ta, tb, w.M, w.N, w.K, dA, lda, dB, ldb, dC, w.N)
     vname = sg.sgemm_variant_name(vid)
     info = sg.sgemm_variant_info(vid)
     log(f"variant: {vname} {info}")
@@ -298,11 +309,11 @@ def main() -> int:
     if args.op == "NN":
         def step():
             sg.sgemm_ex(w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, w.beta,
-                        dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
+                        dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=forced)
     else:
         def step():
             sg.sgemm_op_ex(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, w.beta,
-                           dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=args.variant)
+                           dC.data_ptr(), w.N, stream=stream.cuda_stream, variant=forced)
 
     from fp32_gemm_05_amd.profiling import SclkProbe, launch_floor_ms
 

@@ -31,6 +31,11 @@ HBM_READ_LIB = os.path.join(HERE, "libhbm_read.so")
 HBM_READ_SOURCES = [os.path.join(CSRC, "hbm_read.hip")]
 
 
+# The profiling build of libsgemm: the same sources with the kernels' phase stamps compiled in
+# (read by `python -m fp32_gemm_05_amd.profiling phases`; never loaded by the product path).
+STAMPS_LIB = os.path.join(HERE, "libsgemm_stamps.so")
+
+
 # The launch-floor and engine-clock reference kernels of the bench (not part of libsgemm).
 LAUNCH_REFS_LIB = os.path.join(HERE, "liblaunch_refs.so")
 LAUNCH_REFS_SOURCES = [os.path.join(CSRC, "launch_refs.hip")]
@@ -39,6 +44,11 @@ LAUNCH_REFS_SOURCES = [os.path.join(CSRC, "launch_refs.hip")]
 def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> str:
     """Compile libsgemm's HIP sources into one shared library; returns its path."""
     return _compile(SOURCES, out or LIB, verbose, extra_flags)
+
+
+def build_stamps(verbose: bool = False) -> str:
+    """Compile the phase-stamp profiling build of libsgemm (libsgemm_stamps.so); returns its path."""
+    return _compile(SOURCES, STAMPS_LIB, verbose, ["-DSGEMM_PHASE_STAMPS"])
 
 
 def build_hbm_read(verbose: bool = False) -> str:

@@ -78,6 +78,34 @@ __host__ __device__ inline void tile_of(int wg, int nwg, int tiles_m, int tiles_
 }
 
 __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+
+// Phase stamps, compiled only into the profiling build (SGEMM_PHASE_STAMPS: libsgemm_stamps.so,
+// read by `python -m fp32_gemm_05_amd.profiling phases`).  Lane 0 of every wave writes the shader
+// clock (s_memtime) and the constant-rate real-time clock (s_memrealtime) at the kernel's phase
+// boundaries -- slot 0 the kernel starts, 1 the first slab has landed and the K loop begins, 2 the
+// K loop has ended, 3 the epilogue's stores are issued -- and, with slot 0, the wave's HW_ID
+// register (its SIMD, CU, shader array and engine) in slot 4: g_phase_stamps[(w * 5 + slot) * 2]
+// and [... + 1] for the grid's wave w = blockIdx.x * (waves per workgroup) + wave,
+// w < g_phase_stamp_waves.  In every other build the hook is empty.
+#ifdef SGEMM_PHASE_STAMPS
+__device__ unsigned long long* g_phase_stamps;
+__device__ unsigned g_phase_stamp_waves;
+__device__ __attribute__((always_inline)) inline void phase_stamp(int slot) {
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long c = clock64(), r = wall_clock64();
+    unsigned long long* buf = g_phase_stamps;
+    const unsigned w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if ((threadIdx.x & 63) == 0 && buf != nullptr && w < g_phase_stamp_waves) {
+        buf[(w * 5 + slot) * 2] = c;
+        buf[(w * 5 + slot) * 2 + 1] = r;
+        if (slot == 0) buf[(w * 5 + 4) * 2] = (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4);  // HW_ID
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+#define SGEMM_PHASE_STAMP(slot) phase_stamp(slot)
+#else
+#define SGEMM_PHASE_STAMP(slot) ((void)0)
+#endif
 __device__ inline int imax(int a, int b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------------------------

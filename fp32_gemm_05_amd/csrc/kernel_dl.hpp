@@ -159,6 +159,7 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, in
 __global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    SGEMM_PHASE_STAMP(0);
     using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>;
     using Acc = typename MfmaBlock<MB>::acc_t;
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / Cfg::KG, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
@@ -394,6 +395,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Checked = std::integral_constant<bool, false>;
     DrainPhases drain;
     if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
+    SGEMM_PHASE_STAMP(1);
     int s = 0;
     // STAGES slabs per trip, so that every stage offset is a constant
     for (; s + STAGES - 1 + D < nfull; s += STAGES) {
@@ -404,9 +406,11 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         if (STAGES > 3) slab(s + 3, std::integral_constant<int, 3 % STAGES>{}, Full{});
     }
     for (; s < nslab; ++s) slab(s, std::integral_constant<int, -1>{}, Checked{});
+    SGEMM_PHASE_STAMP(2);
 
     mfma_block_epilogue<MB, FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh,
                                               cv);
+    SGEMM_PHASE_STAMP(3);
 }
 
 // ---------------------------------------------------------------------------------

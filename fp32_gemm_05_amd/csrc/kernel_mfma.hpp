@@ -10,6 +10,7 @@ template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, bool WIDE, 
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    SGEMM_PHASE_STAMP(0);
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC, TA, TB, BQ>;
     constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
     constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
@@ -122,6 +123,7 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Dyn = std::integral_constant<int, -1>;
     DrainPhases drain;
     if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
+    SGEMM_PHASE_STAMP(1);
     int s = 0;
     // main loop, two slabs per trip so that both LDS stage offsets are constants
     for (; s + 2 < nfull; s += 2) {
@@ -132,8 +134,10 @@ sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     for (; s + 1 < nfull; ++s) slab(s, Full{}, Dyn{});
     for (; s + 1 < nslab; ++s) slab(s, std::integral_constant<int, 2>{}, Dyn{});
     slab(s, std::integral_constant<int, 0>{}, Dyn{});
+    SGEMM_PHASE_STAMP(2);
 
     mfma_epilogue<FM, FN, VEC>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh);
+    SGEMM_PHASE_STAMP(3);
 }
 
 }  // namespace libsgemm

@@ -8,13 +8,63 @@
 //   * sclk_probe: reads the shader-clock counter (s_memtime) and the constant-rate real-time
 //     counter (s_memrealtime) at the start and end of a bounded spin, so that their ratio gives
 //     the engine clock at the moment the probe ran, on the stream it ran on.
+//   * mfma_chain: one wave per SIMD issues a dependent chain of MFMAs of one shape and times it
+//     in shader cycles: the cycles one MFMA of that shape occupies the matrix pipe, the unit of
+//     the ideal K-loop time in the phase profiles.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 __global__ void empty_kernel() {}
+
+// Four waves per workgroup; wave w of the grid issues n (a multiple of 8) MFMAs of shape `kind`
+// (32: v_mfma_f32_32x32x2_f32, 16: v_mfma_f32_16x16x4_f32) as `ilp` interleaved dependent chains
+// (1, 2 or 4 accumulators) and writes the shader cycles they took to cycles[w]; every lane writes
+// a sum of its accumulators to sink, which keeps the chains from being optimised away.
+template <int KIND, int ILP>
+__device__ __attribute__((always_inline)) inline float mfma_chain_run(int n, float a, float b) {
+    typedef typename std::conditional<KIND == 32, f32x16, f32x4>::type acc_t;
+    acc_t acc[ILP];
+#pragma unroll
+    for (int c = 0; c < ILP; ++c) acc[c] = acc_t{};
+    for (int i = 0; i < n; i += 8)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc_t& x = acc[u % ILP];
+            if constexpr (KIND == 32)
+                x = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, x, 0, 0, 0);
+            else
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+        }
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < ILP; ++c)
+#pragma unroll
+        for (int r = 0; r < (KIND == 32 ? 16 : 4); ++r) sum += acc[c][r];
+    return sum;
+}
+
+__global__ void __launch_bounds__(256) mfma_chain_kernel(int n, int kind, int ilp, unsigned long long* __restrict__ cycles,
+                                                        float* __restrict__ sink) {
+    const float a = (float)(threadIdx.x & 63) * 1e-3f, b = 1.0f;
+    const unsigned long long t0 = clock64();
+    float sum;
+    if (kind == 32)
+        sum = ilp == 1 ? mfma_chain_run<32, 1>(n, a, b) : ilp == 2 ? mfma_chain_run<32, 2>(n, a, b)
+                                                                   : mfma_chain_run<32, 4>(n, a, b);
+    else
+        sum = ilp == 1 ? mfma_chain_run<16, 1>(n, a, b) : ilp == 2 ? mfma_chain_run<16, 2>(n, a, b)
+                                                                   : mfma_chain_run<16, 4>(n, a, b);
+    const unsigned long long t1 = clock64();
+    if ((threadIdx.x & 63) == 0) cycles[blockIdx.x * 4 + (threadIdx.x >> 6)] = t1 - t0;
+    sink[blockIdx.x * 256 + threadIdx.x] = sum;
+}
 
 // One lane per workgroup times a spin of `ticks` real-time ticks.  The loop ends once the
 // real-time counter has advanced by `ticks`, which it always does.
@@ -61,6 +111,21 @@ __attribute__((visibility("default"))) int sclk_probe(int nblocks, long ticks, u
     void* args[] = {&t, &out};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sclk_probe_kernel), dim3((unsigned)nblocks),
                                    dim3(64), args, 0, stream);
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+// Launch the MFMA chains: nblocks workgroups of 4 waves (nblocks = the CU count gives one wave per
+// SIMD), each wave n MFMAs of shape kind (32 or 16) in ilp (1, 2 or 4) interleaved dependent
+// chains; cycles: device buffer of 4 * nblocks 64-bit values, sink: device buffer of 256 * nblocks
+// floats.  Returns 0, -1 on invalid arguments, or the hipError_t of the launch.
+__attribute__((visibility("default"))) int mfma_chain(int nblocks, int n, int kind, int ilp, unsigned long long* cycles,
+                                                      float* sink, hipStream_t stream) {
+    if (nblocks <= 0 || nblocks > 4096 || n <= 0 || n % 8 != 0 || n > (1 << 20) || (kind != 32 && kind != 16) ||
+        (ilp != 1 && ilp != 2 && ilp != 4) || cycles == nullptr || sink == nullptr)
+        return -1;
+    void* args[] = {&n, &kind, &ilp, &cycles, &sink};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mfma_chain_kernel), dim3((unsigned)nblocks),
+                                   dim3(256), args, 0, stream);
     return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -15,7 +15,11 @@
         per-dispatch means of any collected counters for one kernel.
     python -m fp32_gemm_05_amd.profiling series <kernel_trace.csv> --log BENCH_STDERR --command "..." --out X.md
         per-phase durations of a traced bench run (first call, pre-roll, warmup, timed region, ...).
-    python -m fp32_gemm_05_amd.profiling collect --dir D --workload W [--warmup N] [--out-dir profiles]
+    python -m fp32_gemm_05_amd.profiling phases --workload W [--variant NAME]
+        per-wave prologue / K loop / epilogue cycles of one launch from the phase-stamp build
+        (libsgemm_stamps.so), next to the back-to-back launch time, the launch floor and the K
+        loop's MFMA ideal (runs on the GPU itself, not under a profiler).
+    python -m fp32_gemm_05_amd.profiling collect --dir D --workload W [--variant NAME] [--warmup N] [--out-dir profiles]
         runs every rocprofv3 pass below (each as a child process with its own time limit) and then
         `report`: the one command behind each committed summary.
     python -m fp32_gemm_05_amd.profiling report --dir D --workload W --out-dir profiles
@@ -52,7 +56,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_COMMON = ("kernel_common.hpp", "sgemm_launch.hpp")
 # kernel family of a variant, by its name's prefix
 KERNEL_FAMILIES = (("mfma32p_", "kernel_pipe.hpp"), ("mfma32d_", "kernel_deep.hpp"), ("mfma32k", "kernel_splitk.hpp"),
-                   ("mfma32r_", "kernel_direct.hpp"), ("mfma32l_", "kernel_dl.hpp"), ("mfma32_", "kernel_mfma.hpp"),
+                   ("mfma32r_", "kernel_direct.hpp"), ("mfma32l_", "kernel_dl.hpp"), ("mfma16l_", "kernel_dl.hpp"),
+                   ("mfma32_", "kernel_mfma.hpp"),
                    ("valu_", "kernel_valu.hpp"))
 
 
@@ -130,7 +135,27 @@ def launch_refs_lib():
     lib.sclk_probe.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
     lib.wall_clock_khz.restype = ctypes.c_int
     lib.wall_clock_khz.argtypes = []
+    lib.mfma_chain.restype = ctypes.c_int
+    lib.mfma_chain.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p]
     return lib
+
+
+def mfma_cycles(kind: int, stream, ilp: int = 4, n: int = 4096, nblocks: int = 256):
+    """Shader cycles per MFMA of shape kind (32: 32x32x2, 16: 16x16x4 f32) at one wave per SIMD,
+    issued as `ilp` interleaved dependent chains (ilp = 4: the issue rate, with no wait for a
+    previous result): (median, min, max) over the waves of the chain kernel."""
+    import torch
+    lib = launch_refs_lib()
+    cyc = torch.zeros(4 * nblocks, dtype=torch.int64, device="cuda")
+    sink = torch.empty(256 * nblocks, dtype=torch.float32, device="cuda")
+    for _ in range(3):  # the last launch's cycles are kept
+        rc = lib.mfma_chain(nblocks, n, kind, ilp, cyc.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"mfma_chain returned {rc}")
+    torch.cuda.synchronize()
+    c = sorted(x / n for x in cyc.cpu().tolist())
+    return c[len(c) // 2], c[0], c[-1]
 
 
 class SclkProbe:
@@ -367,20 +392,21 @@ def _workload_figures(workload):
     return w, gemm_flops(w.M, w.N, w.K), algorithmic_bytes(w.M, w.N, w.K, w.beta)
 
 
-def _variant_tile(name):
-    """(BM, BN) of the named kernel variant in the built library, or None."""
+def _variant_info(name):
+    """sgemm_variant_info of the named kernel variant in the built library, or None."""
     from . import _binding as sg
     for i in range(sg.sgemm_num_variants()):
         if sg.sgemm_variant_name(i) == name:
-            info = sg.sgemm_variant_info(i)
-            return info["BM"], info["BN"]
+            return sg.sgemm_variant_info(i)
     return None
 
 
 def cmd_report(args) -> None:
     d, W = args.dir, args.workload
+    tag = getattr(args, "run_tag", None) or W  # raw-output directory suffix (workload[__variant])
+    forced = f" --variant {args.variant}" if tag != W else ""
     w, flops, alg_bytes = _workload_figures(W)
-    rows = _stats_rows(os.path.join(d, f"trace_{W}", "run_kernel_stats.csv"))
+    rows = _stats_rows(os.path.join(d, f"trace_{tag}", "run_kernel_stats.csv"))
     kern = [r for r in rows if "sgemm" in r["Name"]]
     if len(kern) != 1:
         raise SystemExit(f"expected one sgemm kernel in the trace of {W}, found {len(kern)}")
@@ -389,7 +415,7 @@ def cmd_report(args) -> None:
     avg_ns = float(k["AverageNs"])
     # the bench's launches: the first call, the warmup, the timed region (`steps` back-to-back
     # launches) and a pass of min(steps, 50) individually timed launches
-    with open(os.path.join(d, f"trace_{W}", "run_kernel_trace.csv")) as f:
+    with open(os.path.join(d, f"trace_{tag}", "run_kernel_trace.csv")) as f:
         disp = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in csv.DictReader(f)
                 if r["Kernel_Name"] == name]
     spread = min(args.steps, 50)
@@ -397,10 +423,10 @@ def cmd_report(args) -> None:
     timed_ns = _mean(timed)
     # variant name from the kernel signature is not unique; take it from the bench log
     variant = args.variant
-    sq = {c: _mean(v) for c, v in _read_counters(os.path.join(d, f"sq_{W}", "run_counter_collection.csv"), "sgemm").items()}
-    fetch = _mean_counter(os.path.join(d, f"fetch_{W}", "run_counter_collection.csv"), "sgemm", "FETCH_SIZE")
-    write = _mean_counter(os.path.join(d, f"write_{W}", "run_counter_collection.csv"), "sgemm", "WRITE_SIZE")
-    rd = {c: _mean(v) for c, v in _read_counters(os.path.join(d, f"rdreq_{W}", "run_counter_collection.csv"), "sgemm").items()}
+    sq = {c: _mean(v) for c, v in _read_counters(os.path.join(d, f"sq_{tag}", "run_counter_collection.csv"), "sgemm").items()}
+    fetch = _mean_counter(os.path.join(d, f"fetch_{tag}", "run_counter_collection.csv"), "sgemm", "FETCH_SIZE")
+    write = _mean_counter(os.path.join(d, f"write_{tag}", "run_counter_collection.csv"), "sgemm", "WRITE_SIZE")
+    rd = {c: _mean(v) for c, v in _read_counters(os.path.join(d, f"rdreq_{tag}", "run_counter_collection.csv"), "sgemm").items()}
     cfetch = _mean_counter(os.path.join(d, "copy_fetch", "run_counter_collection.csv"), "copyBuffer", "FETCH_SIZE")
     cwrite = _mean_counter(os.path.join(d, "copy_write", "run_counter_collection.csv"), "copyBuffer", "WRITE_SIZE")
     copy_bytes = 1024.0 ** 3
@@ -413,32 +439,36 @@ def cmd_report(args) -> None:
     mfma_util = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (N_SIMD * gui)
     # the last dispatch of the counter run (after its warmup): engine clock = active cycles per XCD
     # over the dispatch's duration, and that dispatch's MFMA busy fraction
-    last_c, last_ns = _dispatches(os.path.join(d, f"sq_{W}", "run_counter_collection.csv"), "sgemm")[-1]
+    last_c, last_ns = _dispatches(os.path.join(d, f"sq_{tag}", "run_counter_collection.csv"), "sgemm")[-1]
     last_gui = last_c.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
     sclk_last = last_gui / last_ns if last_ns > 0 else float("nan")  # cycles per ns = GHz
     mfma_last = last_c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (N_SIMD * last_gui)
     lds_conf = sq.get("SQ_LDS_BANK_CONFLICT", float("nan")) / (N_CU * gui)
-    expect_mfma = w.M * w.N * w.K / 2048.0  # 32x32x2 MFMAs of the exact problem (no tile padding)
+    info = _variant_info(variant)
+    mb = info.get("mfma_block", 32) if info else 32
+    # MFMAs of the exact problem (no tile padding): 32x32x2 = 2048 and 16x16x4 = 1024 multiply-adds each
+    expect_mfma = w.M * w.N * w.K / (2048.0 if mb == 32 else 1024.0) if mb else 0.0
+    mfma_desc = {32: "v_mfma_f32_32x32x2_f32", 16: "v_mfma_f32_16x16x4_f32"}.get(mb, "(a vector-FMA kernel: none)")
     tflops = flops / (avg_ns * 1e-9) / 1e12
     tflops_timed = flops / (timed_ns * 1e-9) / 1e12
-    tile = _variant_tile(variant)
+    tile = (info["BM"], info["BN"]) if info else None
     panel = panel_read_bytes(w.M, w.N, w.K, *tile) if tile else float("nan")
-    bench = "python -u bench.py --workload %s" % W
+    bench = "python -u bench.py --workload %s%s" % (W, forced)
     trace_opt = f"--trace-args='{args.trace_args}' " if args.trace_args else ""
     sq_warm = args.sq_warmup
     cmds = [
-        f"python -m fp32_gemm_05_amd.profiling collect --dir <dir> --workload {W} "
-        f"{'--warmup ' + args.trace_args.split()[-1] + ' ' if args.trace_args.startswith('--warmup') else ''}"
+        f"python -m fp32_gemm_05_amd.profiling collect --dir <dir> --workload {W}{forced} "
+        f"{'--warmup ' + args.trace_args.split()[1] + ' ' if args.trace_args.startswith('--warmup') else ''}"
         f"(runs all of the following)",
-        f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{W} -o run -- {bench} "
-        f"{args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline --no-sclk",
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
-        f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{W} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
-        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{W} -o run -- {bench} --steps 3 --warmup {sq_warm} --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{tag} -o run -- python -u bench.py "
+        f"--workload {W} {args.trace_args + ' ' if args.trace_args else ''}--no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_{tag} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_{tag} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum --output-format csv -d <dir>/rdreq_{tag} -o run -- {bench} --steps 3 --warmup 1 --no-cpu-baseline --no-sclk",
+        f"rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE --output-format csv -d <dir>/sq_{tag} -o run -- {bench} --steps 3 --warmup {sq_warm} --no-cpu-baseline --no-sclk",
         "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE, then the three TCC_EA0_RDREQ_*_sum) --output-format csv -d <dir>/copy_fetch (copy_write, copy_rdreq) -o run -- python -u -m fp32_gemm_05_amd.profiling copy --mib 1024 --reps 3",
         f"python -m fp32_gemm_05_amd.profiling report --dir <dir> --workload {W} --variant {variant} "
-        f"{trace_opt}--out-dir profiles",
+        f"{'--run-tag ' + tag + ' ' if tag != W else ''}{trace_opt}--out-dir profiles",
     ]
     lines = [
         f"# `{variant}` on {W}", "",
@@ -463,8 +493,8 @@ def cmd_report(args) -> None:
         lines.append(f"| {c} | {rd[c]:.6g} |")
     lines += [
         "", "## Derived", "",
-        f"* MFMA instructions: {sq.get('SQ_INSTS_MFMA', float('nan')):.6g} (the problem needs M*N*K/2048 = "
-        f"{expect_mfma:.6g} v_mfma_f32_32x32x2_f32; the rest is tile padding at ragged edges)",
+        f"* MFMA instructions: {sq.get('SQ_INSTS_MFMA', float('nan')):.6g} (the problem needs "
+        f"{expect_mfma:.6g} {mfma_desc}; the rest is tile padding at ragged edges)",
         f"* MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) = {100 * mfma_util:.1f} % "
         f"(mean over the counter run's dispatches); {100 * mfma_last:.1f} % in its last dispatch",
         (f"* Engine clock in the counter run's last dispatch: GRBM_GUI_ACTIVE / 8 XCDs / duration = "
@@ -500,6 +530,166 @@ def cmd_report(args) -> None:
     with open(os.path.join(args.out_dir, f"traffic_{variant}_{W}.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print("\n".join(lines))
+
+
+def cmd_phases(args) -> None:
+    """Where one launch's time goes, per wave, from the phase-stamp build of libsgemm: the cycles of
+    the prologue (kernel start until the first slab has landed), the K loop and the epilogue, each
+    wave's start and end on the real-time clock, and the engine clock over the wave.  Next to them:
+    the same variant's time per launch back to back (libsgemm.so, after a clock pre-roll), the
+    launch floor of its grid, and the K loop's ideal -- the wave's MFMAs at the cycles one MFMA
+    takes in a dependent chain (mfma_chain).  Runs on the GPU in this process."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from . import _binding as sg
+    from . import build as hb
+    from .workloads import WORKLOADS, make_inputs
+
+    for path in (hb.LIB, hb.STAMPS_LIB):
+        if not os.path.exists(path):
+            raise SystemExit(f"{path} is not built (__graft_entry__.build())")
+    prod = sg.load_library()
+    st = sg.load_library(hb.STAMPS_LIB)
+    st.sgemm_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+    st.sgemm_phase_stamps.restype = ctypes.c_int
+    refs = launch_refs_lib()
+    W = args.workload
+    w = WORKLOADS[W]
+    A, B, C0 = make_inputs(w)
+    dev = torch.device("cuda:0")
+    dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C0))
+    stream = torch.cuda.current_stream()
+    if args.variant:
+        vid = next((i for i in range(sg.sgemm_num_variants()) if sg.sgemm_variant_name(i) == args.variant), -1)
+        if vid < 0:
+            raise SystemExit(f"no variant named {args.variant}")
+    else:
+        vid = prod.sgemm_select_variant(w.M, w.N, w.K, dA.data_ptr(), w.K, dB.data_ptr(), w.N, dC.data_ptr(), w.N)
+    name = sg.sgemm_variant_name(vid)
+    if st.sgemm_variant_name(vid).decode() != name:
+        raise SystemExit("libsgemm.so and libsgemm_stamps.so were built from different sources")
+    info = sg.sgemm_variant_info(vid)
+    print(f"[phases] {W}: variant {name}", flush=True)
+
+    def call(lib):
+        rc = lib.sgemm_ex(w.M, w.N, w.K, w.alpha, dA.data_ptr(), w.K, dB.data_ptr(), w.N, w.beta, dC.data_ptr(),
+                          w.N, stream.cuda_stream, vid)
+        if rc != 0:
+            raise RuntimeError(f"sgemm_ex returned {rc}")
+
+    def preroll(lib, seconds):
+        import time
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            for _ in range(50):
+                call(lib)
+            torch.cuda.synchronize()
+
+    # back to back, as the bench times it
+    preroll(prod, args.preroll)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call(prod)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b_us = e0.elapsed_time(e1) / args.steps * 1e3
+    tiles = -(-w.M // info["BM"]) * -(-w.N // info["BN"])
+    floor_us = launch_floor_ms(tiles, info["threads"], info["lds_bytes"], args.steps, stream) * 1e3
+    print(f"[phases] back to back {b2b_us:.2f} us per launch; launch floor {floor_us:.2f} us", flush=True)
+
+    # the stamped launches
+    wpg = info["threads"] // 64
+    waves = tiles * wpg
+    buf = torch.zeros(waves * 10, dtype=torch.int64, device=dev)
+    preroll(st, args.preroll / 2)
+    if st.sgemm_phase_stamps(buf.data_ptr(), waves) != 0:
+        raise RuntimeError("sgemm_phase_stamps failed")
+    for _ in range(3):
+        call(st)
+    torch.cuda.synchronize()
+    st.sgemm_phase_stamps(None, 0)
+    x = buf.cpu().numpy().reshape(waves, 5, 2).astype(np.int64)
+    if (x[:, :4, 0] == 0).any():
+        raise SystemExit(f"{name}: its kernel family records no phase stamps (dl and plain MFMA kernels do)")
+    c, r, hw = x[:, :4, 0], x[:, :4, 1], x[:, 4, 0]
+    pro, loop, epi = c[:, 1] - c[:, 0], c[:, 2] - c[:, 1], c[:, 3] - c[:, 2]
+    rate_mhz = refs.wall_clock_khz() / 1000.0
+    mhz = (c[:, 3] - c[:, 0]) / np.maximum(r[:, 3] - r[:, 0], 1) * rate_mhz
+    start_us = (r[:, 0] - r[:, 0].min()) / rate_mhz
+    end_us = (r[:, 3] - r[:, 0].min()) / rate_mhz
+    span_us = float(end_us.max())
+    mb = info.get("mfma_block") or 32
+    nslab = -(-w.K // info["BK"])
+    fm, fn = info["WM_or_TM"] // mb, info["WN_or_TN"] // mb
+    mfmas = nslab * fm * fn * info["BK"] * mb // 64  # per wave: BK*MB/64 MFMAs per block and slab
+    issue = mfma_cycles(mb, stream, ilp=4)  # the issue rate (independent chains)
+    dep = mfma_cycles(mb, stream, ilp=1)    # one dependent chain
+    cyc = issue[0]
+    ideal = mfmas * cyc
+    clk = float(np.median(mhz))
+    # waves per SIMD: HW_ID holds SIMD_ID [5:4], CU_ID [11:8], SH_ID [12], SE_ID [15:13]; workgroup g
+    # runs on XCD g % 8 (round-robin dispatch over the XCDs)
+    wg = np.arange(waves) // wpg
+    key = ((wg % 8) << 16) | (((hw >> 13) & 7) << 8) | (((hw >> 12) & 1) << 7) | (((hw >> 8) & 15) << 2) | ((hw >> 4) & 3)
+    simd_busy, simd_waves = [], []
+    for k in np.unique(key):
+        sel = key == k
+        window_us = (r[sel, 3].max() - r[sel, 0].min()) / rate_mhz
+        simd_waves.append(int(sel.sum()))
+        simd_busy.append(sel.sum() * ideal / max(window_us * clk, 1e-9))
+    nsimd = len(simd_busy)
+    total_ideal_us = waves * ideal / clk / 1024.0  # all the MFMAs spread over the chip's 1024 SIMDs
+
+    def q(a, us=False):
+        a = np.asarray(a, dtype=np.float64)
+        f = (lambda v: f"{v:.0f} ({v / clk:.2f} us)") if us else (lambda v: f"{v:.2f}")
+        return f"{f(np.median(a))} | {f(a.min())} | {f(a.max())}"
+
+    def pct(a):
+        a = 100 * np.asarray(a, dtype=np.float64)
+        return f"{np.median(a):.1f} % | {a.min():.1f} % | {a.max():.1f} %"
+
+    shape = {32: "v_mfma_f32_32x32x2_f32", 16: "v_mfma_f32_16x16x4_f32"}[mb]
+    lines = [
+        f"# Phase stamps: `{name}` on {W}", "",
+        f"Workload: {w.describe()}.  Grid: {tiles} workgroups of {info['threads']} threads ({waves} waves), "
+        f"{mfmas} {shape} per wave.", "",
+        "| Per launch | us |", "|---|---|",
+        f"| back to back (libsgemm.so, {args.steps} launches after a {args.preroll:.1f} s pre-roll) | {b2b_us:.2f} |",
+        f"| launch floor of the grid (empty kernel, same grid, timed the same way) | {floor_us:.2f} |",
+        f"| wave span of one stamped launch (first wave start to last wave end) | {span_us:.2f} |",
+        f"| back to back - span: launch gap and the grid's ramp-up | {b2b_us - span_us:.2f} |",
+        f"| every MFMA of the launch at the issue rate, spread evenly over 1024 SIMDs | {total_ideal_us:.2f} |", "",
+        f"MFMA issue cost (mfma_chain at one wave per SIMD): {cyc:.1f} cycles with four interleaved "
+        f"chains (min {issue[1]:.1f}, max {issue[2]:.1f}), {dep[0]:.1f} cycles in one dependent chain.", "",
+        "| Per wave (stamped launch) | median | min | max |", "|---|---|---|---|",
+        f"| engine clock (MHz) | {q(mhz)} |",
+        f"| prologue cycles (start to first slab landed) | {q(pro, True)} |",
+        f"| K loop cycles | {q(loop, True)} |",
+        f"| epilogue cycles | {q(epi, True)} |",
+        f"| start after the first wave (us) | {q(start_us)} |",
+        f"| end after the first wave's start (us) | {q(end_us)} |",
+        f"| K loop at the issue rate: ideal {ideal:.0f} cycles / loop cycles (one wave per SIMD only) | "
+        f"{pct(ideal / loop)} |", "",
+        f"| Per SIMD ({nsimd} SIMDs ran waves) | median | min | max |", "|---|---|---|---|",
+        f"| waves | {q(simd_waves)} |",
+        f"| matrix-pipe busy: its waves' MFMAs at the issue rate / (last wave end - first wave start) | "
+        f"{pct(simd_busy)} |", "",
+        "## Command", "", "```",
+        f"python -m fp32_gemm_05_amd.profiling phases --workload {W}"
+        f"{' --variant ' + args.variant if args.variant else ''} --steps {args.steps} --preroll {args.preroll}",
+        "```", "",
+    ]
+    if args.note:
+        lines += [args.note, ""]
+    os.makedirs(args.out_dir, exist_ok=True)
+    out = os.path.join(args.out_dir, f"phases_{name}__{W}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines), flush=True)
 
 
 # Counter passes of one summary: each rocprofv3 --pmc run stays within one pass's limits
@@ -538,20 +728,25 @@ def cmd_collect(args) -> None:
             _run(rp + ["--pmc", *counters, "-d", os.path.join(d, tag), "-o", "run", "--", *copy],
                  os.path.join(d, tag + ".log"), 120)
     bench = [py, "-u", os.path.join(ROOT, "bench.py"), "--workload", W]
-    _run(rp + ["--kernel-trace", "--stats", "-d", os.path.join(d, f"trace_{W}"), "-o", "run", "--", *bench,
-               "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-sclk"], os.path.join(d, f"trace_{W}.log"), 300)
+    if args.variant:
+        bench += ["--variant", args.variant]  # a forced variant instead of the dispatched one
+    tag_w = f"{W}__{args.variant}" if args.variant else W  # raw-output directories of this run
+    _run(rp + ["--kernel-trace", "--stats", "-d", os.path.join(d, f"trace_{tag_w}"), "-o", "run", "--", *bench,
+               "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-sclk"], os.path.join(d, f"trace_{tag_w}.log"), 300)
     variant = None
-    with open(os.path.join(d, f"trace_{W}.log")) as f:
+    with open(os.path.join(d, f"trace_{tag_w}.log")) as f:
         for line in f:
             if line.startswith("variant: "):
                 variant = line.split()[1]
     if variant is None:
         raise SystemExit("the bench did not report its variant")
     for tag, counters in PMC_PASSES:
-        _run(rp + ["--pmc", *counters, "-d", os.path.join(d, f"{tag}_{W}"), "-o", "run", "--", *bench,
-                   "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-sclk"], os.path.join(d, f"{tag}_{W}.log"), 120)
-    report = argparse.Namespace(dir=d, workload=W, variant=variant, steps=200, sq_warmup=1,
-                                trace_args=f"--warmup {args.warmup}", out_dir=args.out_dir, note="")
+        _run(rp + ["--pmc", *counters, "-d", os.path.join(d, f"{tag}_{tag_w}"), "-o", "run", "--", *bench,
+                   "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-sclk"],
+             os.path.join(d, f"{tag}_{tag_w}.log"), 120)
+    extra = f"--warmup {args.warmup}" + (f" --variant {args.variant}" if args.variant else "")
+    report = argparse.Namespace(dir=d, workload=W, variant=variant, steps=200, sq_warmup=1, trace_args=extra,
+                                out_dir=args.out_dir, note="", run_tag=tag_w)
     cmd_report(report)
 
 
@@ -605,7 +800,15 @@ def main(argv=None) -> int:
     p.add_argument("--dir", required=True, help="where the raw rocprofv3 output goes")
     p.add_argument("--workload", required=True)
     p.add_argument("--warmup", type=int, default=100, help="bench warmup of the traced run")
+    p.add_argument("--variant", default=None, help="profile this variant (by name) instead of the dispatched one")
     p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    p = sub.add_parser("phases", help="per-wave phase breakdown from the phase-stamp build (runs on the GPU)")
+    p.add_argument("--workload", required=True)
+    p.add_argument("--variant", default=None, help="a variant by name (default: the dispatched one)")
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--preroll", type=float, default=1.0, help="seconds of launches before timing")
+    p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    p.add_argument("--note", default="")
     p = sub.add_parser("report")
     p.add_argument("--dir", required=True)
     p.add_argument("--workload", required=True)
@@ -615,6 +818,8 @@ def main(argv=None) -> int:
     p.add_argument("--trace-args", default="", help="extra bench.py arguments of the traced run (e.g. a longer "
                    "warmup, so that short kernels are traced at the ramped-up engine clock)")
     p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    p.add_argument("--run-tag", default=None, help="directory suffix of a collect run with a forced variant "
+                   "(<workload>__<variant>)")
     p.add_argument("--note", default="")
     args = ap.parse_args(argv)
     if args.cmd == "report":
@@ -633,6 +838,8 @@ def main(argv=None) -> int:
         cmd_counters(args)
     elif args.cmd == "series":
         cmd_series(args)
+    elif args.cmd == "phases":
+        cmd_phases(args)
     return 0
 
 
