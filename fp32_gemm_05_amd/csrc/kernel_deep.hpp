@@ -26,6 +26,7 @@ template <int BM, int BN, int BK, int WM, int WN, bool VEC, int OCC, int FAIR = 
 __global__ void __launch_bounds__((MfmaCfg<BM, BN, BK, WM, WN, VEC>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    SGEMM_PHASE_STAMP(0);
     using Cfg = MfmaCfg<BM, BN, BK, WM, WN, VEC>;
     constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
     constexpr int AP = Cfg::A_PITCH, BP = Cfg::B_PITCH;
@@ -157,6 +158,7 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     using Checked = std::integral_constant<bool, false>;
     DrainPhases drain;
     if (FAIR > 0) drain.init(FAIR, nslab, g.drain_from);
+    SGEMM_PHASE_STAMP(1);
     int s = 0;
     for (; s + 3 < nfull; s += 2) {  // two slabs per trip: the buffer and stage of each are constants
         if (FAIR > 0) drain.step(s);
@@ -169,6 +171,7 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         slab(s, Odd{}, Checked{});
         ++s;
     }
+    SGEMM_PHASE_STAMP(2);
 
     if (ACC2) {
 #pragma unroll
@@ -177,6 +180,7 @@ sgemm_mfma_deep_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
             for (int j = 0; j < FN; ++j) acc[i][j] += acc2[i][j];
     }
     mfma_epilogue<FM, FN, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li, lh, cv);
+    SGEMM_PHASE_STAMP(3);
 }
 
 }  // namespace libsgemm

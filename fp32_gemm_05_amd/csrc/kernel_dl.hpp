@@ -32,16 +32,22 @@ namespace libsgemm {
 // loads have landed and before the barrier.  W = 16 needs the 128-bit variants' precondition
 // (16-byte aligned rows; K and N multiples of 4).
 // ---------------------------------------------------------------------------------
-template <int QPR>
+// The LDS serves a 128-bit access of 64 lanes in four passes of 16 lanes: lanes of one half-wave
+// (lane / 32) whose bits 2-4 have the same parity (lanes 0-3, 12-15, 20-23, 24-27 and lanes 4-11,
+// 16-19, 28-31, then the same in the upper half) -- measured lane pair by lane pair with the
+// SQ_LDS_BANK_CONFLICT counter.  A pass is conflict-free when its 16 accesses cover the 64 banks.
+// 32x32 blocks: a pass holds 16 rows of one quad; 16x16 blocks: 8 rows of one lane group's quad and
+// the complementary 8 rows of the next group's, which these swizzles keep apart.
+template <int QPR, int MB = 32>
 __device__ __host__ inline int dl_swz_a(int r) {  // swizzle of A row r (QPR quads per row)
     static_assert(QPR == 4 || QPR == 8 || QPR == 16, "A rows of 16, 32 or 64 floats");
-    return QPR == 16 ? r & 15
-                     : QPR == 8 ? ((r & 15) + ((r >> 3) & 1)) & 7 : (((r >> 1) & 7) + ((r >> 3) & 1)) & 3;
+    if (MB == 16) return QPR == 16 ? r & 15 : QPR == 8 ? (r >> 1) & 7 : ((r >> 3) & 1) * 2;
+    return QPR == 16 ? r & 15 : QPR == 8 ? ((r & 15) + ((r >> 3) & 1)) & 7 : (((r >> 1) & 7) + ((r >> 3) & 1)) & 3;
 }
-// Swizzle of B row k, in quads, for MFMA blocks of MB columns: a B fragment read takes rows
-// 4 h + t (t fixed) of the 64 / MB lane groups h at MB consecutive columns, and the swizzle
-// flips the column by MB h on those rows (quad bit 3 for 32x32 blocks; quad bits 2-3 for
-// 16x16 blocks), putting the groups on distinct banks.
+// Swizzle of B row k, in quads, for MFMA blocks of MB columns: a B fragment read (32-bit, one pass
+// of 64 lanes) takes row 4 h + t (t fixed) of each of the 64 / MB lane groups h at MB consecutive
+// columns, and the swizzle flips the column by MB h on those rows (quad bit 3 for 32x32 blocks;
+// quad bits 2-3 for 16x16 blocks), putting the groups on distinct banks.
 template <int MB = 32>
 __device__ __host__ inline int dl_swz_b(int k) {
     static_assert(MB == 32 || MB == 16, "32x32 or 16x16 MFMA blocks");
@@ -190,7 +196,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     // crosses K uses it, and keeping it live would cost registers throughout the loop).
     auto a_kin = [&](int j) {
         const int f = (wave * LA + j) * CH + E * lane;
-        return 4 * (((f % BK) / 4) ^ dl_swz_a<QA>(f / BK)) + f % 4;
+        return 4 * (((f % BK) / 4) ^ dl_swz_a<QA, MB>(f / BK)) + f % 4;
     };
     auto b_kin = [&](int j) { return ((wave * LB + j) * CH + E * lane) / BN; };
     uint32_t a_off[LA], b_off[LB];  // byte offsets from the slab's first element
@@ -279,7 +285,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     int a_frag[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-        a_frag[kk] = (wm0 + li) * BK + 4 * ((G * kk + lh) ^ dl_swz_a<QA>(wm0 + li));
+        a_frag[kk] = (wm0 + li) * BK + 4 * ((G * kk + lh) ^ dl_swz_a<QA, MB>(wm0 + li));
     int b_frag[FN];
 #pragma unroll
     for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * MB + li) ^ (MB * lh));

@@ -8,6 +8,9 @@
 //   * sclk_probe: reads the shader-clock counter (s_memtime) and the constant-rate real-time
 //     counter (s_memrealtime) at the start and end of a bounded spin, so that their ratio gives
 //     the engine clock at the moment the probe ran, on the stream it ran on.
+//   * lds_probe: one wave reads LDS at per-lane word offsets from a table; run under rocprofv3
+//     with SQ_LDS_BANK_CONFLICT, pairs of lanes that conflict show how the LDS groups the lanes
+//     of an access into passes.
 //   * mfma_chain: one wave per SIMD issues a dependent chain of MFMAs of one shape and times it
 //     in shader cycles: the cycles one MFMA of that shape occupies the matrix pipe, the unit of
 //     the ideal K-loop time in the phase profiles.
@@ -18,6 +21,7 @@
 
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -64,6 +68,35 @@ __global__ void __launch_bounds__(256) mfma_chain_kernel(int n, int kind, int il
     const unsigned long long t1 = clock64();
     if ((threadIdx.x & 63) == 0) cycles[blockIdx.x * 4 + (threadIdx.x >> 6)] = t1 - t0;
     sink[blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
+// One wave: lane l reads `width` bytes (4, 8 or 16) of a 64 KiB LDS array at float offset idx[l]
+// (clamped into the array and to the access's alignment), `reps` times, and writes a sum of what it
+// read to out[l].  Each read waits for itself inside its asm block.
+__global__ void __launch_bounds__(64) lds_probe_kernel(const int* __restrict__ idx, int width, int reps,
+                                                       float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) float lds[16384];
+    for (int i = threadIdx.x; i < 16384; i += 64) lds[i] = (float)i;
+    __syncthreads();
+    const int f = min(max(idx[threadIdx.x], 0), 16380) & ~3;
+    const unsigned a = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float*)(lds + f);
+    float s = 0.f;
+    for (int r = 0; r < reps; ++r) {
+        if (width == 16) {
+            f32x4 v;
+            asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+            s += v.x + v.y + v.z + v.w;
+        } else if (width == 8) {
+            f32x2 v;
+            asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+            s += v.x + v.y;
+        } else {
+            float v;
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+            s += v;
+        }
+    }
+    out[threadIdx.x] = s;
 }
 
 // One lane per workgroup times a spin of `ticks` real-time ticks.  The loop ends once the
@@ -126,6 +159,17 @@ __attribute__((visibility("default"))) int mfma_chain(int nblocks, int n, int ki
     void* args[] = {&n, &kind, &ilp, &cycles, &sink};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mfma_chain_kernel), dim3((unsigned)nblocks),
                                    dim3(256), args, 0, stream);
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+// Launch the LDS probe: one wave; idx: device table of 64 float offsets, out: device buffer of 64
+// floats.  Returns 0, -1 on invalid arguments, or the hipError_t of the launch.
+__attribute__((visibility("default"))) int lds_probe(const int* idx, int width, int reps, float* out,
+                                                     hipStream_t stream) {
+    if (idx == nullptr || out == nullptr || (width != 4 && width != 8 && width != 16) || reps <= 0 || reps > 4096)
+        return -1;
+    void* args[] = {&idx, &width, &reps, &out};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&lds_probe_kernel), dim3(1), dim3(64), args, 0, stream);
     return e == hipSuccess ? 0 : (int)e;
 }
 

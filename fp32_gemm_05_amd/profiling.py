@@ -19,6 +19,9 @@
         per-wave prologue / K loop / epilogue cycles of one launch from the phase-stamp build
         (libsgemm_stamps.so), next to the back-to-back launch time, the launch floor and the K
         loop's MFMA ideal (runs on the GPU itself, not under a profiler).
+    python -m fp32_gemm_05_amd.profiling lds-probe   (under rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS)
+    python -m fp32_gemm_05_amd.profiling lds-passes <counter_collection.csv> --out X.md
+        which lanes of one 32-, 64- or 128-bit LDS access share a pass, from lane-pair patterns.
     python -m fp32_gemm_05_amd.profiling collect --dir D --workload W [--variant NAME] [--warmup N] [--out-dir profiles]
         runs every rocprofv3 pass below (each as a child process with its own time limit) and then
         `report`: the one command behind each committed summary.
@@ -135,6 +138,8 @@ def launch_refs_lib():
     lib.sclk_probe.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
     lib.wall_clock_khz.restype = ctypes.c_int
     lib.wall_clock_khz.argtypes = []
+    lib.lds_probe.restype = ctypes.c_int
+    lib.lds_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.mfma_chain.restype = ctypes.c_int
     lib.mfma_chain.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
@@ -587,15 +592,35 @@ def cmd_phases(args) -> None:
                 call(lib)
             torch.cuda.synchronize()
 
-    # back to back, as the bench times it
+    # cold: a 512 MiB read (more than the Infinity Cache and every L2) before a launch evicts its
+    # operands, as the bench's --cold does
+    flush = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev) if args.cold else None
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def evict():
+        if flush is not None:
+            torch.sum(flush, dim=0, out=flush_out)
+
+    # back to back, as the bench times it (cold: each launch between its own events, after a flush)
     preroll(prod, args.preroll)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        call(prod)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    b2b_us = e0.elapsed_time(e1) / args.steps * 1e3
+    if args.cold:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            evict()
+            a.record(stream)
+            call(prod)
+            b.record(stream)
+        torch.cuda.synchronize()
+        b2b_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
+    else:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call(prod)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b2b_us = e0.elapsed_time(e1) / args.steps * 1e3
     tiles = -(-w.M // info["BM"]) * -(-w.N // info["BN"])
     floor_us = launch_floor_ms(tiles, info["threads"], info["lds_bytes"], args.steps, stream) * 1e3
     print(f"[phases] back to back {b2b_us:.2f} us per launch; launch floor {floor_us:.2f} us", flush=True)
@@ -608,12 +633,14 @@ def cmd_phases(args) -> None:
     if st.sgemm_phase_stamps(buf.data_ptr(), waves) != 0:
         raise RuntimeError("sgemm_phase_stamps failed")
     for _ in range(3):
+        evict()
         call(st)
     torch.cuda.synchronize()
     st.sgemm_phase_stamps(None, 0)
     x = buf.cpu().numpy().reshape(waves, 5, 2).astype(np.int64)
     if (x[:, :4, 0] == 0).any():
-        raise SystemExit(f"{name}: its kernel family records no phase stamps (dl and plain MFMA kernels do)")
+        raise SystemExit(f"{name}: its kernel family records no phase stamps (the direct-to-LDS, plain and "
+                         f"deep MFMA kernels do)")
     c, r, hw = x[:, :4, 0], x[:, :4, 1], x[:, 4, 0]
     pro, loop, epi = c[:, 1] - c[:, 0], c[:, 2] - c[:, 1], c[:, 3] - c[:, 2]
     rate_mhz = refs.wall_clock_khz() / 1000.0
@@ -654,14 +681,17 @@ def cmd_phases(args) -> None:
 
     shape = {32: "v_mfma_f32_32x32x2_f32", 16: "v_mfma_f32_16x16x4_f32"}[mb]
     lines = [
-        f"# Phase stamps: `{name}` on {W}", "",
+        f"# Phase stamps: `{name}` on {W}{' (cold caches)' if args.cold else ''}", "",
         f"Workload: {w.describe()}.  Grid: {tiles} workgroups of {info['threads']} threads ({waves} waves), "
         f"{mfmas} {shape} per wave.", "",
         "| Per launch | us |", "|---|---|",
-        f"| back to back (libsgemm.so, {args.steps} launches after a {args.preroll:.1f} s pre-roll) | {b2b_us:.2f} |",
+        (f"| cold: mean of {args.steps} launches each timed alone after a 512 MiB flush (libsgemm.so) | {b2b_us:.2f} |"
+         if args.cold else
+         f"| back to back (libsgemm.so, {args.steps} launches after a {args.preroll:.1f} s pre-roll) | {b2b_us:.2f} |"),
         f"| launch floor of the grid (empty kernel, same grid, timed the same way) | {floor_us:.2f} |",
         f"| wave span of one stamped launch (first wave start to last wave end) | {span_us:.2f} |",
-        f"| back to back - span: launch gap and the grid's ramp-up | {b2b_us - span_us:.2f} |",
+        f"| {'launch time' if args.cold else 'back to back'} - span: launch gap and the grid's ramp-up | "
+        f"{b2b_us - span_us:.2f} |",
         f"| every MFMA of the launch at the issue rate, spread evenly over 1024 SIMDs | {total_ideal_us:.2f} |", "",
         f"MFMA issue cost (mfma_chain at one wave per SIMD): {cyc:.1f} cycles with four interleaved "
         f"chains (min {issue[1]:.1f}, max {issue[2]:.1f}), {dep[0]:.1f} cycles in one dependent chain.", "",
@@ -680,14 +710,100 @@ def cmd_phases(args) -> None:
         f"{pct(simd_busy)} |", "",
         "## Command", "", "```",
         f"python -m fp32_gemm_05_amd.profiling phases --workload {W}"
-        f"{' --variant ' + args.variant if args.variant else ''} --steps {args.steps} --preroll {args.preroll}",
+        f"{' --variant ' + args.variant if args.variant else ''}{' --cold' if args.cold else ''} --steps {args.steps} "
+        f"--preroll {args.preroll}",
         "```", "",
     ]
     if args.note:
         lines += [args.note, ""]
     os.makedirs(args.out_dir, exist_ok=True)
-    out = os.path.join(args.out_dir, f"phases_{name}__{W}.md")
+    out = os.path.join(args.out_dir, f"phases_{name}__{W}{'_cold' if args.cold else ''}.md")
     with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines), flush=True)
+
+
+# Lane-pair patterns of the LDS pass probe: lanes i and j read two different words of the same
+# banks (float offsets 0 and 64, 256 bytes apart) and every other lane one broadcast word in other
+# banks (float 32), so a dispatch has bank-conflict cycles exactly when i and j share a pass.
+LDS_PROBE_WIDTHS = (16, 8, 4)
+LDS_PROBE_LANES = (0, 8, 16, 32)
+
+
+def lds_probe_plan():
+    plan = []
+    for width in LDS_PROBE_WIDTHS:
+        for i in LDS_PROBE_LANES:
+            for j in range(64):
+                if j != i:
+                    idx = [32] * 64
+                    idx[i], idx[j] = 0, 64
+                    plan.append((width, i, j, idx))
+    return plan
+
+
+def cmd_lds_probe(args) -> None:
+    """Launch every lane-pair pattern once (one wave, `reps` reads each); run it under
+    `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS`.  The dispatches follow lds_probe_plan()."""
+    import torch
+    lib = launch_refs_lib()
+    plan = lds_probe_plan()
+    tabs = torch.tensor([p[3] for p in plan], dtype=torch.int32, device="cuda")
+    out = torch.zeros(64, device="cuda")
+    stream = torch.cuda.current_stream()
+    for n, (width, i, j, idx) in enumerate(plan):
+        rc = lib.lds_probe(tabs[n].data_ptr(), width, args.reps, out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"lds_probe returned {rc}")
+    torch.cuda.synchronize()
+    print(f"lds-probe: {len(plan)} dispatches of {args.reps} reads", flush=True)
+
+
+def cmd_lds_passes(args) -> None:
+    """The LDS pass grouping from a counter run of `lds-probe`: for each access width and probe
+    lane i, the lanes j whose pattern has bank-conflict cycles."""
+    per = defaultdict(dict)
+    with open(args.csv) as f:
+        for row in csv.DictReader(f):
+            if "lds_probe" in row["Kernel_Name"]:
+                per[int(row["Dispatch_Id"])][row["Counter_Name"]] = float(row["Counter_Value"])
+    plan = lds_probe_plan()
+    ids = sorted(per)
+    if len(ids) != len(plan):
+        raise SystemExit(f"expected {len(plan)} probe dispatches, found {len(ids)}")
+    shared = defaultdict(list)
+    cycles = defaultdict(set)
+    for d, (width, i, j, _) in zip(ids, plan):
+        c = per[d].get("SQ_LDS_BANK_CONFLICT", 0.0)
+        if c > 0:
+            shared[(width, i)].append(j)
+        cycles[width].add(c)
+
+    def ranges(xs):
+        xs, out = sorted(xs), []
+        for x in xs:
+            if out and x == out[-1][1] + 1:
+                out[-1][1] = x
+            else:
+                out.append([x, x])
+        return ", ".join(f"{a}-{b}" if a != b else f"{a}" for a, b in out) or "none"
+
+    lines = ["# LDS passes: which lanes of one access share a pass (MI355X)", "",
+             "Lanes i and j read two different words of the same four banks, every other lane one "
+             "broadcast word in other banks; the dispatch counts SQ_LDS_BANK_CONFLICT cycles exactly "
+             f"when i and j go through the LDS in the same pass ({args.reps} reads per dispatch).", "",
+             "| Access | Lane i | Lanes j sharing its pass |", "|---|---|---|"]
+    for width in LDS_PROBE_WIDTHS:
+        for i in LDS_PROBE_LANES:
+            lines.append(f"| {width * 8}-bit | {i} | {ranges(shared[(width, i)])} |")
+    lines += ["", "Conflict-cycle values seen per dispatch: " +
+              "; ".join(f"{w * 8}-bit {sorted(v)}" for w, v in cycles.items()), "",
+              "## Commands", "", "```",
+              f"rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS --output-format csv -d <dir> -o run -- "
+              f"python -u -m fp32_gemm_05_amd.profiling lds-probe --reps {args.reps}",
+              "python -m fp32_gemm_05_amd.profiling lds-passes <dir>/run_counter_collection.csv --out profiles/lds_passes.md",
+              "```", ""]
+    with open(args.out, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines), flush=True)
 
@@ -807,8 +923,15 @@ def main(argv=None) -> int:
     p.add_argument("--variant", default=None, help="a variant by name (default: the dispatched one)")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--preroll", type=float, default=1.0, help="seconds of launches before timing")
+    p.add_argument("--cold", action="store_true", help="evict the caches before every timed and stamped launch")
     p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     p.add_argument("--note", default="")
+    p = sub.add_parser("lds-probe", help="launch the LDS lane-pair patterns (run under rocprofv3 --pmc)")
+    p.add_argument("--reps", type=int, default=64)
+    p = sub.add_parser("lds-passes", help="the LDS pass grouping from a counter run of lds-probe")
+    p.add_argument("csv")
+    p.add_argument("--reps", type=int, default=64)
+    p.add_argument("--out", required=True)
     p = sub.add_parser("report")
     p.add_argument("--dir", required=True)
     p.add_argument("--workload", required=True)
@@ -840,6 +963,10 @@ def main(argv=None) -> int:
         cmd_series(args)
     elif args.cmd == "phases":
         cmd_phases(args)
+    elif args.cmd == "lds-probe":
+        cmd_lds_probe(args)
+    elif args.cmd == "lds-passes":
+        cmd_lds_passes(args)
     return 0
 
 

@@ -280,8 +280,10 @@ def test_direct_kernel_loads_in_bounds(v):
 # the direct-to-LDS kernel (sgemm_mfma_dl_kernel): swizzled 16-byte loads straight into LDS
 # ------------------------------------------------------------------------------------------
 
-def dl_swz_a(r, qpr):
+def dl_swz_a(r, qpr, mb=32):
     r = np.asarray(r)
+    if mb == 16:
+        return r & 15 if qpr == 16 else (r >> 1) & 7 if qpr == 8 else ((r >> 3) & 1) * 2
     if qpr == 16:
         return r & 15
     return ((r & 15) + ((r >> 3) & 1)) & 7 if qpr == 8 else (((r >> 1) & 7) + ((r >> 3) & 1)) & 3
@@ -319,7 +321,7 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
             f = (wave * LA + j) * CH + E * lane
             r = f // BK
             u = (f % BK) // 4
-            kin = 4 * (u ^ dl_swz_a(r, QA)) + f % 4
+            kin = 4 * (u ^ dl_swz_a(r, QA, MB)) + f % 4
             row = np.minimum(m0 + r, M - 1)
             k = k0 + kin
             kl = np.minimum(k, K - E) if tail else k
@@ -371,7 +373,7 @@ def test_dl_kernel_loads_and_fragments(v):
                     for wave in range(NT // 64):
                         wm0, wn0 = (wave // waves_n) * WM, (wave % waves_n) * WN
                         for kk in range(BK // KG):
-                            a_frag = (wm0 + li) * BK + 4 * ((G * kk + lh) ^ dl_swz_a(wm0 + li, QA))
+                            a_frag = (wm0 + li) * BK + 4 * ((G * kk + lh) ^ dl_swz_a(wm0 + li, QA, MB))
                             for fi in range(WM // MB):
                                 for t in range(4):
                                     got = a_lds[a_frag + fi * MB * BK + t]
@@ -397,58 +399,124 @@ def test_dl_kernel_loads_and_fragments(v):
 def test_dl_swizzles_are_row_permutations():
     for qpr in (4, 8, 16):
         for r in range(64):
-            assert sorted((np.arange(qpr) ^ dl_swz_a(r, qpr)).tolist()) == list(range(qpr))
+            for mb in (32, 16):
+                assert sorted((np.arange(qpr) ^ dl_swz_a(r, qpr, mb)).tolist()) == list(range(qpr))
     for mb in (32, 16):
         for k in range(64):
             assert sorted((np.arange(16) ^ dl_swz_b(k, mb)).tolist()) == list(range(16))
 
 
-def lds_read_passes(addr_bytes, width, banks):
-    """Bank conflicts of one LDS read by 64 lanes: lanes go through in passes of
-    banks * 4 / width lanes; within a pass, the extra cycles are the largest number of distinct
-    4-byte words that one bank must deliver, minus one, summed over the passes."""
-    per_pass = banks * 4 // width
+# How the LDS serves one access of 64 lanes (64 banks of 4 bytes), as measured on MI355X: two
+# lanes reading different words of the same banks add conflict cycles exactly when they share a
+# pass (SQ_LDS_BANK_CONFLICT over lane pairs, `python -m fp32_gemm_05_amd.profiling lds-passes`):
+#   * 32-bit accesses: one pass of all 64 lanes;
+#   * 64-bit accesses: two passes, lanes 0-31 and 32-63;
+#   * 128-bit accesses: four passes of 16 lanes -- the lanes of one half-wave whose bits 2-4 have
+#     the same parity (lanes 0-3, 12-15, 20-23, 24-27 / 4-11, 16-19, 28-31 / the same + 32).
+# ds_read2st64_b32 goes through as two 32-bit accesses (its two words per lane are 64 words apart,
+# the same bank, and the 32x32 kernels that use it measure no conflict cycles).
+def lds_passes(width):
+    lane = np.arange(64)
+    if width == 16:
+        par = np.array([bin(int(x) >> 2 & 7).count("1") & 1 for x in lane])
+        return [list(lane[(lane >> 5 == h) & (par == p)]) for h in (0, 1) for p in (0, 1)]
+    if width == 8:
+        return [list(range(32)), list(range(32, 64))]
+    return [list(range(64))]
+
+
+def lds_extra_cycles(addr_bytes, width):
+    """Bank-conflict cycles of one LDS access by 64 lanes: per pass, the largest number of distinct
+    4-byte words one bank must serve, minus one, summed over the passes."""
     extra = 0
-    for p0 in range(0, 64, per_pass):
+    for lanes in lds_passes(width):
         words = {}
-        for a in addr_bytes[p0:p0 + per_pass]:
+        for ln in lanes:
             for w in range(width // 4):
-                word = a // 4 + w
-                words.setdefault(word % banks, set()).add(word)
+                word = int(addr_bytes[ln]) // 4 + w
+                words.setdefault(word % 64, set()).add(word)
         extra += max(len(x) for x in words.values()) - 1
     return extra
 
 
-@pytest.mark.parametrize("banks", [64, 32])
-@pytest.mark.parametrize("v", DL, ids=[v["name"] for v in DL])
-def test_dl_fragment_reads_are_conflict_free(v, banks):
-    """Every fragment read of sgemm_mfma_dl_kernel -- the 128-bit A reads (MB consecutive rows of
-    a lane group at one quad) and the 32-bit B reads (rows KG kk + 4 h + t of the lane groups at
-    MB consecutive columns) -- is free of bank conflicts, with 64 banks and 16 lanes per 128-bit
-    pass and with 32 banks and 8 lanes per pass."""
+def dl_fragment_addresses(v, swz_a=dl_swz_a):
+    """Byte addresses of every fragment read of sgemm_mfma_dl_kernel, one 64-lane array per read:
+    ("a", addresses) for the 128-bit A reads and ("b", ...) for the 32-bit B reads (rows
+    KG kk + 4 h + t of the lane groups at MB consecutive columns)."""
     BN, BK, WM, WN = v["BN"], v["BK"], v["WM_or_TM"], v["WN_or_TN"]
     MB = mfma_block(v)
     G, KG = 64 // MB, 4 * 64 // MB
     lane = np.arange(64)
     li, lh = lane % MB, lane // MB
+    out = []
     for wave in range(v["threads"] // 64):
         wm0, wn0 = (wave // (BN // WN)) * WM, (wave % (BN // WN)) * WN
         for kk in range(BK // KG):
             for fi in range(WM // MB):
-                a = 4 * ((wm0 + li + MB * fi) * BK + 4 * ((G * kk + lh) ^ dl_swz_a(wm0 + li, BK // 4)))
-                assert lds_read_passes(a.tolist(), 16, banks) == 0
+                out.append(("a", 4 * ((wm0 + li + MB * fi) * BK + 4 * ((G * kk + lh) ^ swz_a(wm0 + li, BK // 4, MB)))))
             for fj in range(WN // MB):
                 for t in range(4):
-                    b = 4 * ((KG * kk + 4 * lh + t) * BN + ((wn0 + fj * MB + li) ^ (MB * lh)))
-                    assert lds_read_passes(b.tolist(), 4, banks) == 0
+                    out.append(("b", 4 * ((KG * kk + 4 * lh + t) * BN + ((wn0 + fj * MB + li) ^ (MB * lh)))))
+    return out
 
 
-def test_lds_bank_model_sees_a_conflict():
-    """The bank model above reports the conflict of the unswizzled 16x16 B read (rows 4 h + t of
-    four lane groups at the same 16 columns of 64-float rows share their banks)."""
+@pytest.mark.parametrize("v", DL, ids=[v["name"] for v in DL])
+def test_dl_fragment_reads_are_conflict_free(v):
+    """Every fragment read of sgemm_mfma_dl_kernel is free of bank conflicts under the measured
+    pass grouping."""
+    for kind, addr in dl_fragment_addresses(v):
+        assert lds_extra_cycles(addr, 16 if kind == "a" else 4) == 0, kind
+
+
+def test_lds_bank_model_matches_measured_conflicts():
+    """The pass model reproduces SQ_LDS_BANK_CONFLICT as measured on MI355X (the counter summaries of
+    the kernels):
+      * the 32x32-block direct-load kernels: 0 conflict cycles;
+      * the 16x16-block kernel with the 32x32 blocks' A swizzle: 16384 cycles over 8192 LDS
+        instructions on 256^3 (half of them 128-bit A reads), and the same count again after lane
+        groups 1 and 2 swapped their k-quads -- 4 extra cycles per A read either way;
+      * the plain kernel (128x128x16 tiles, A rows of BK + 4 = 20 floats, B rows of BN + 8): exactly
+        1 conflict cycle per LDS instruction on 4096^3 -- its two 128-bit A stores per wave and slab
+        take 8 each, and the other 14 of the wave's 16 LDS instructions (A reads, B stores and B
+        reads) none."""
+    by_name = {v["name"]: v for v in DL}
+    for n in ("mfma32l_128x128x16_w64x64_s4_d3_vec", "mfma32l_64x64x32_w32x32_s3_cp_sp_vec",
+              "mfma32l_64x64x16_w32x32_s3_sp_scalar"):
+        assert all(lds_extra_cycles(a, 16 if k == "a" else 4) == 0 for k, a in dl_fragment_addresses(by_name[n]))
+    v16 = by_name["mfma16l_64x64x32_w32x16_s3_cp_sp_vec"]
+    swz32 = lambda r, qpr, mb: dl_swz_a(r, qpr, 32)  # the 32x32 blocks' swizzle
+    old = dl_fragment_addresses(v16, swz_a=swz32)
+    assert {lds_extra_cycles(a, 16) for k, a in old if k == "a"} == {4}
+    assert {lds_extra_cycles(a, 4) for k, a in old if k == "b"} == {0}
+    lane = np.arange(64)
+    li, lh = lane % 16, lane // 16
+    for kk in range(2):  # lane groups 1 and 2 swapped
+        q = ((lh & 1) << 1) | (lh >> 1)
+        for fi in range(2):
+            a = 4 * ((li + 16 * fi) * 32 + 4 * ((4 * kk + q) ^ dl_swz_a(li, 8, 32)))
+            assert lds_extra_cycles(a, 16) == 4
+    # the plain kernel: A stores, thread t -> row t / 4 (+ 64 per pass), quad t % 4, rows of 20
+    # floats; B stores, thread t -> row t / 32, quad t % 32, rows of 136; A reads row li + 32 i at
+    # quad 2 kk + h; B reads row 4 h + t (+ 8 kk) at column li (+ 32 j)
+    li, lh = lane % 32, lane // 32
+    for wave in range(4):
+        tid = 64 * wave + lane
+        for l in range(2):
+            assert lds_extra_cycles(4 * ((tid // 4 + 64 * l) * 20 + 4 * (tid % 4)), 16) == 8
+            assert lds_extra_cycles(4 * ((tid // 32 + 8 * l) * 136 + 4 * (tid % 32)), 16) == 0
+    for kk in range(2):
+        for i in range(4):
+            assert lds_extra_cycles(4 * ((li + 32 * i) * 20 + 4 * (2 * kk + lh)), 16) == 0
+        for t in range(4):
+            assert lds_extra_cycles(4 * ((8 * kk + 4 * lh + t) * 136 + li), 4) == 0
+
+
+def test_lds_bank_model_sees_a_b_conflict():
+    """The bank model reports the conflict of an unswizzled 16x16 B read (rows 4 h + t of four lane
+    groups at the same 16 columns of 64-float rows share their banks)."""
     lane = np.arange(64)
     b = 4 * ((4 * (lane // 16)) * 64 + lane % 16)
-    assert lds_read_passes(b.tolist(), 4, 64) == 3
+    assert lds_extra_cycles(b, 4) == 3
 
 
 # ------------------------------------------------------------------------------------------

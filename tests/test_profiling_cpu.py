@@ -1,14 +1,18 @@
-"""The profile summary (`profiling report`) from synthetic rocprofv3 output: the copy calibration,
-the HBM bytes per launch, the MFMA count the problem needs for the variant's block size, the busy
-fractions, and the command list of a forced-variant run.  No GPU: the CSV files are written here.
+"""The profiling summaries from synthetic rocprofv3 output: `report` (the copy calibration, the HBM
+bytes per launch, the MFMA count the problem needs for the variant's block size, the busy fractions,
+the command list of a forced-variant run) and `lds-passes` (the LDS pass grouping from lane-pair
+counters).  No GPU: the CSV files are written here.
 """
 import csv
 import json
 import os
+import sys
 
 import pytest
 
 from fp32_gemm_05_amd import profiling
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
 
 def _write(path, header, rows):
@@ -117,3 +121,48 @@ def test_stamps_build_matches_the_library():
     assert hasattr(st, "sgemm_phase_stamps")
     with pytest.raises(AttributeError):
         ctypes.CDLL(hb.LIB).sgemm_phase_stamps
+
+
+def _lds_model_passes(width):
+    """The pass grouping of the kernel model (tests/test_kernel_model.py)."""
+    from test_kernel_model import lds_passes
+    return lds_passes(width)
+
+
+def test_lds_passes_report_round_trip(tmp_path):
+    """`profiling lds-passes` recovers a pass grouping from the counters of the lane-pair probe:
+    synthetic counters that conflict exactly when the two lanes share a pass of the kernel model."""
+    plan = profiling.lds_probe_plan()
+    rows = []
+    for d, (width, i, j, _) in enumerate(plan):
+        same = any(i in p and j in p for p in _lds_model_passes(width))
+        rows.append([d + 1, "lds_probe_kernel", "SQ_LDS_BANK_CONFLICT", 64.0 if same else 0.0, 0, 1])
+    path = str(tmp_path / "c.csv")
+    _write(path, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                  "End_Timestamp"], rows)
+    out = str(tmp_path / "lds.md")
+    profiling.cmd_lds_passes(profiling.argparse.Namespace(csv=path, reps=64, out=out))
+    md = open(out).read()
+    assert "| 128-bit | 0 | 1-3, 12-15, 20-27 |" in md
+    assert "| 64-bit | 32 | 33-63 |" in md and "| 32-bit | 8 | 0-7, 9-63 |" in md
+
+
+def test_lds_model_matches_the_committed_measurement():
+    """The kernel model's pass grouping is the one the committed probe summary measured."""
+    import re
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles", "lds_passes.md")
+    if not os.path.exists(path):
+        pytest.skip("no committed LDS pass summary")
+    table = {}
+    for m in re.finditer(r"^\| (\d+)-bit \| (\d+) \| ([^|]*) \|$", open(path).read(), re.M):
+        lanes = set()
+        for part in m.group(3).split(","):
+            part = part.strip()
+            if part and part != "none":
+                a, _, b = part.partition("-")
+                lanes |= set(range(int(a), int(b or a) + 1))
+        table[(int(m.group(1)) // 8, int(m.group(2)))] = lanes
+    assert table, "no table rows in the summary"
+    for (width, i), lanes in table.items():
+        (mine,) = [set(p) - {i} for p in _lds_model_passes(width) if i in p]
+        assert lanes == mine, (width, i)
