@@ -440,6 +440,8 @@ const Variant kVariants[] = {
     DLP_ROW(128, 128, 16, 64, 64, 4, 16, 0, true, DL_NAME(128, 128, 16, 64, 64, 4) "_ps_sp_vec"),
     DLP_ROW(128, 128, 16, 64, 64, 4, 16, 0, false, DL_NAME(128, 128, 16, 64, 64, 4) "_ps_vec"),
     DLP_ROW(128, 64, 32, 64, 32, 3, 16, 0, true, DL_NAME(128, 64, 32, 64, 32, 3) "_ps_sp_vec"),
+    DLP_ROW(64, 64, 16, 32, 32, 3, 4, 0, true, DL_NAME(64, 64, 16, 32, 32, 3) "_ps_sp_scalar"),
+    DLP_ROW(64, 64, 32, 32, 32, 3, 4, 0, true, DL_NAME(64, 64, 32, 32, 32, 3) "_ps_sp_scalar"),
     // 16x16x4 blocks: 64x64 tiles of 8 waves (two per SIMD) or 16 waves, and 128-wide tiles of 8 or
     // 16 waves of 32x32
     DL16_VARIANT(64, 64, 32, 32, 16, 3, 0, true, false, "_cp"),
