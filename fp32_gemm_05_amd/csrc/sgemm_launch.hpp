@@ -454,5 +454,12 @@ const Variant kVariants[] = {
     DL16_VARIANT(128, 128, 32, 32, 32, 3, 0, false, false, ""),
     DL16_SCALAR(64, 64, 32, 32, 16, 3, 0, false, false, ""),
     DL16_SCALAR(64, 64, 32, 32, 16, 3, 0, false, true, "_sp"),
+    // 32x64 tiles of four 32x16 waves: a 1024^2 grid has 512 of them, two workgroups per CU, so a
+    // SIMD's two waves belong to different workgroups and wait at different barriers
+    DL16_VARIANT(32, 64, 32, 32, 16, 3, 0, true, true, "_cp_sp"),
+    DL16_VARIANT(32, 64, 32, 32, 16, 3, 0, true, false, "_cp"),
+    DL16_VARIANT(32, 64, 32, 16, 32, 3, 0, true, false, "_cp"),
+    DL16_VARIANT(32, 64, 32, 32, 16, 4, 0, true, false, "_cp"),
+    DL16_SCALAR(32, 64, 32, 32, 16, 3, 0, false, false, ""),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

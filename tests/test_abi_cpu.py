@@ -171,27 +171,27 @@ def _name(v):
     return sg.sgemm_variant_name(v)
 
 
-@pytest.mark.parametrize("M,N,K,ld_odd,family", [
-    (256, 256, 256, False, "lds"),        # small_shortk: K < 512 keeps the LDS kernels
-    (822, 124, 88, False, "lds"),
-    (512, 512, 512, False, "direct"),     # tiny: under 128 64x64 tiles
-    (333, 555, 777, True, "direct"),
-    (1554, 64, 5093, True, "direct"),     # skinny with few tiles joins the small classes
-    (1024, 1024, 1024, False, "lds"),     # small, aligned: 64x64 workgroups fill the CUs
-    (1001, 1003, 777, True, "lds"),       # small, unaligned: 16x16-block workgroups of 8 waves
-    (1111, 1113, 1001, True, "lds"),      # small_full: more than one 64x64 tile per CU
-    (1089, 728, 5752, False, "lds"),      # small_longk, aligned: the direct-to-LDS ring
-    (4096, 4096, 4096, False, "lds"),
-    (65536, 64, 1024, False, "lds"),      # skinny
+@pytest.mark.parametrize("M,N,K,ld_odd,prefix", [
+    (256, 256, 256, False, "mfma16l_32x64"),   # small_shortk: 32x64 tiles, two workgroups a CU
+    (822, 124, 88, False, "mfma16l_32x64"),
+    (512, 512, 512, False, "mfma16l_32x64"),   # tiny: under 128 64x64 tiles
+    (333, 555, 777, True, "mfma16l_32x64"),
+    (1554, 64, 5093, True, "mfma16l_32x64"),   # skinny with few tiles joins the small classes
+    (1024, 1024, 1024, False, "mfma32l_64x64"),  # small, aligned: 64x64 workgroups fill the CUs
+    (1001, 1003, 777, True, "mfma16l_64x64"),  # small, unaligned: 16x16-block workgroups of 8 waves
+    (1111, 1113, 1001, True, "mfma16l_32x64"),  # small_full, unaligned
+    (1089, 728, 5752, False, "mfma32l_64x64"),  # small_longk, aligned: the direct-to-LDS ring
+    (4096, 4096, 4096, False, "mfma32_128x128"),
+    (65536, 64, 1024, False, "mfma32_128x64"),  # skinny
 ])
-def test_dispatch_families(M, N, K, ld_odd, family):
-    """Which kernel family the shape classes pick: the LDS-free kernel (mfma32r_) for tiny grids
-    and skinny ones with few tiles; LDS kernels elsewhere."""
+def test_dispatch_families(M, N, K, ld_odd, prefix):
+    """Which kernel family and workgroup tile the shape classes pick; the 128-bit forms exactly
+    when the operands allow them."""
     lda, ldb = (K | 1, N | 1) if ld_odd else (K, N)
     v = sg.sgemm_select_variant(M, N, K, FAKE_A, lda, FAKE_B, ldb, FAKE_C, ldb)
     assert v >= 0
-    assert _name(v).startswith("mfma32r_") == (family == "direct"), _name(v)
-    assert bool(sg.sgemm_variant_info(v)["vec"]) == (not ld_odd) or family == "lds"
+    assert _name(v).startswith(prefix), _name(v)
+    assert bool(sg.sgemm_variant_info(v)["vec"]) == (not ld_odd)
 
 
 @pytest.mark.parametrize("ta,tb,M,N,K,odd,direct", [
@@ -242,15 +242,18 @@ def test_tile_order_gives_each_xcd_a_compact_block():
 def test_huge_leading_dimension_uses_wide_offsets():
     """A workgroup panel spanning >= 4 GiB cannot use 32-bit offsets: sgemm picks a _wide variant,
     and a forced narrow variant is refused before any launch."""
-    lda = 20_000_000  # (64 - 1) * lda * 4 bytes > 2^32
+    lda = 40_000_000  # (32 - 1) * lda * 4 bytes > 2^32: no narrow tile height fits
     vid = sg.sgemm_select_variant(200, 64, 64, FAKE_A, lda, FAKE_B, 64, FAKE_C, 64)
     info = sg.sgemm_variant_info(vid)
     assert info["wide"] == 1 and info["name"].endswith("_wide_vec")
-    narrow = [i for i in range(sg.sgemm_num_variants())
-              if not sg.sgemm_variant_info(i)["wide"] and sg.sgemm_variant_info(i)["BM"] >= 64]
+    narrow = [i for i in range(sg.sgemm_num_variants()) if not sg.sgemm_variant_info(i)["wide"]
+              and not sg.sgemm_variant_info(i)["trans_a"] and not sg.sgemm_variant_info(i)["trans_b"]]
     big_a = 0x100000000  # far from C, so no overlap
     for v in narrow:
         assert _call(200, 64, 64, lda, 64, 64, A=big_a, variant=v) == -13
+    # 32-row tiles still fit where 64-row ones would not: (32 - 1) * 20e6 * 4 bytes < 2^32
+    vid = sg.sgemm_select_variant(200, 64, 64, FAKE_A, 20_000_000, FAKE_B, 64, FAKE_C, 64)
+    assert sg.sgemm_variant_info(vid)["wide"] == 0 and sg.sgemm_variant_info(vid)["BM"] == 32
     # an ordinary leading dimension keeps the narrow variant
     vid = sg.sgemm_select_variant(4096, 4096, 4096, FAKE_A, 4096, FAKE_B, 4096, FAKE_C, 4096)
     assert sg.sgemm_variant_info(vid)["wide"] == 0
