@@ -58,7 +58,11 @@ def test_bench_line_headline_fields():
     # the reported pre-roll, and the launch floor of the dispatched grid
     assert d["preroll"]["seconds"] >= 0 and d["preroll"]["steps"] >= 0
     lf = d["launch_floor"]
-    assert lf["us"] > 0 and lf["workgroups"] == 16 and lf["threads"] % 64 == 0  # 64x64 tiles of 256^2
+    from fp32_gemm_05_amd import _binding as sg
+    info = next(sg.sgemm_variant_info(i) for i in range(sg.sgemm_num_variants())
+                if sg.sgemm_variant_name(i) == d["config"]["variant"])
+    tiles = -(-256 // info["BM"]) * -(-256 // info["BN"])
+    assert lf["us"] > 0 and lf["workgroups"] == tiles and lf["threads"] == info["threads"]
     assert abs(lf["floor_over_launch"] - lf["us"] * 1e-3 / d["ms_per_step"]) <= 0.01 * lf["floor_over_launch"] + 1e-3
 
 

@@ -281,11 +281,14 @@ def test_error_codes_no_launch():
     assert e.value.code == -13
 
 
-def test_huge_leading_dimension_wide_variant():
-    """lda = 20,000,000 (a 12 GB strided A): the workgroup panel spans more than 4 GiB, so the
-    dispatcher must use 64-bit offsets; the result must still match the oracle exactly."""
+@pytest.mark.parametrize("M,lda,wide", [(40, 40_000_000, 1), (150, 20_000_000, 0)])
+def test_huge_leading_dimension_wide_variant(M, lda, wide):
+    """A strided A of 6.4 or 12 GB.  lda = 40,000,000: even a 32-row workgroup panel spans more
+    than 4 GiB, so the dispatcher must use 64-bit offsets.  lda = 20,000,000: a 32-row panel spans
+    2.5 GB and the dispatched narrow variant's 32-bit offsets still reach every row.  Either way
+    the result must match the oracle exactly."""
     w = WORKLOADS["square1024_beta"].as_int()
-    M, N, K, lda = 150, 64, 68, 20_000_000
+    N, K = 64, 68
     A, B, C = make_inputs(w, M=M, N=N, K=K)
     bufA = torch.empty(M * lda, dtype=torch.float32, device="cuda")
     vA = bufA.as_strided((M, K), (lda, 1))
@@ -293,8 +296,8 @@ def test_huge_leading_dimension_wide_variant():
     dB = torch.from_numpy(B).cuda()
     dC = torch.from_numpy(C).cuda()
     vid = sg.sgemm_select_variant(M, N, K, vA, lda, dB, N, dC, N)
-    assert sg.sgemm_variant_info(vid)["wide"] == 1
-    _say(f"[huge-ld] variant={sg.sgemm_variant_name(vid)}")
+    _say(f"[huge-ld] M={M} lda={lda} variant={sg.sgemm_variant_name(vid)}")
+    assert sg.sgemm_variant_info(vid)["wide"] == wide
     sg.sgemm(M, N, K, 1.0, vA, lda, dB, N, 0.5, dC, N)
     torch.cuda.synchronize()
     ref, _ = oracle.ref_rows(A, B, C, 1.0, 0.5)
@@ -501,21 +504,26 @@ def test_large_extents_elementwise(label, M, N, K, dist, alpha, beta):
 
 
 # ------------------------------------------------------------------------------------------
-# the LDS-free kernel at its 32-bit offset limits: leading dimensions just under the limit run
-# it, just over fall back to the 64-bit-offset variant; both exact on integer data
+# 32-bit offsets at their limits: leading dimensions just under a kernel's limit run it, just
+# over are refused (a forced variant) or fall back to the 64-bit-offset variant (the dispatcher);
+# every run exact on integer data
 # ------------------------------------------------------------------------------------------
 
+FREE_G8 = "mfma32r_32x32x128_w32x32_g8_cp_vec"  # LDS-free: a 32-row A panel, a 128-deep B panel
 OFFSET_LIMITS = [
-    # (label, lda, ldb, expected family): M, N, K = 40, 36, 600 (the tiny class)
-    ("lda_under_limit", 33_000_000, 36, "mfma32r_"),    # (31*lda + 128)*4 < 2^32
-    ("lda_over_limit", 35_000_000, 36, "_wide"),
-    ("ldb_under_limit", 600, 8_000_000, "mfma32r_"),    # (127*ldb + 32)*4 < 2^32
-    ("ldb_over_limit", 600, 8_500_000, "_wide"),
+    # (label, lda, ldb, forced variant or None, expected family or None for "refused");
+    # M, N, K = 40, 36, 600 (the tiny class)
+    ("free_lda_under", 33_000_000, 36, FREE_G8, "mfma32r_"),    # (31*lda + 128)*4 < 2^32
+    ("free_lda_over", 35_000_000, 36, FREE_G8, None),
+    ("free_ldb_under", 600, 8_000_000, FREE_G8, "mfma32r_"),    # (127*ldb + 32)*4 < 2^32
+    ("free_ldb_over", 600, 8_500_000, FREE_G8, None),
+    ("tiny_lda_under", 34_000_000, 36, None, "mfma16l_32x64"),  # 32x64x32 tiles: (31*lda + 32)*4 < 2^32
+    ("tiny_lda_over", 35_000_000, 36, None, "_wide"),
 ]
 
 
-@pytest.mark.parametrize("label,lda,ldb,family", OFFSET_LIMITS, ids=[x[0] for x in OFFSET_LIMITS])
-def test_direct_kernel_offset_limits(label, lda, ldb, family):
+@pytest.mark.parametrize("label,lda,ldb,forced,family", OFFSET_LIMITS, ids=[x[0] for x in OFFSET_LIMITS])
+def test_offset_limits(label, lda, ldb, forced, family):
     M, N, K = 40, 36, 600
     rng = np.random.default_rng(lda + ldb)
     A = rng.integers(-2, 3, (M, K)).astype(np.float32)
@@ -525,13 +533,22 @@ def test_direct_kernel_offset_limits(label, lda, ldb, family):
     bufB, vB, ldb_ = device_matrix(B, pad_cols=ldb - N)
     bufC, vC, ldc = device_matrix(C, fill=SENTINEL)
     assert (lda_, ldb_) == (lda, ldb)
-    vid = sg.sgemm_select_variant(M, N, K, vA.data_ptr(), lda, vB.data_ptr(), ldb, vC.data_ptr(), ldc)
+    if forced is None:
+        vid = sg.sgemm_select_variant(M, N, K, vA.data_ptr(), lda, vB.data_ptr(), ldb, vC.data_ptr(), ldc)
+    else:
+        vid = next(i for i in range(sg.sgemm_num_variants()) if sg.sgemm_variant_name(i) == forced)
     name = sg.sgemm_variant_name(vid)
     _say(f"[offset limits] {label}: lda={lda} ldb={ldb} variant={name}")
-    assert family in name
-    sg.sgemm(M, N, K, 1.0, vA.data_ptr(), lda, vB.data_ptr(), ldb, 0.0, vC.data_ptr(), ldc)
-    torch.cuda.synchronize()
-    ref, _ = oracle.ref_rows(A, B, C, 1.0, 0.0)
-    check_exact(vC.cpu().numpy(), ref, label)
+    if family is None:
+        with pytest.raises(sg.SgemmError) as e:
+            sg.sgemm_ex(M, N, K, 1.0, vA.data_ptr(), lda, vB.data_ptr(), ldb, 0.0, vC.data_ptr(), ldc, variant=vid)
+        assert e.value.code == -13
+    else:
+        assert family in name
+        sg.sgemm_ex(M, N, K, 1.0, vA.data_ptr(), lda, vB.data_ptr(), ldb, 0.0, vC.data_ptr(), ldc, variant=vid)
+        torch.cuda.synchronize()
+        assert sg.sgemm_last_variant() == vid
+        ref, _ = oracle.ref_rows(A, B, C, 1.0, 0.0)
+        check_exact(vC.cpu().numpy(), ref, label)
     del bufA, bufB, bufC, vA, vB, vC
     torch.cuda.empty_cache()
