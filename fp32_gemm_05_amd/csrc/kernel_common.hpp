@@ -354,132 +354,123 @@ __device__ __attribute__((always_inline)) inline f32x16 mfma_step(float a, float
 // upright (32 lanes along a row: coalesced 32-bit stores).
 // (Scalars are passed by value: taking the argument struct by reference makes the compiler
 // keep an addressable copy of it, which it may place in LDS.)
-// The C values a wave's output blocks need for the beta term, in the accumulators' layout
-// (entries outside the matrix are left unset; the epilogue skips them).  Kernels of one-round
-// grids read them at the start of the tile, after their first operand loads, so that the
-// read's latency hides under the K loop instead of stalling the epilogue.
-template <int FM, int FN, bool VEC>
-__device__ __attribute__((always_inline)) inline void mfma_load_c(int M, int N, const float* __restrict__ C,
-                                                                  long ldc, f32x16 (&cv)[FM][FN], int m_base,
-                                                                  int n_base, int li, int lh) {
+// The beta term's C values and the stores of one 32x32 block whose top-left element is (r0, c0),
+// in the accumulators' layout.  Addresses are a wave-uniform row base plus a 32-bit per-lane byte
+// offset (one register however many values are in flight; the block spans 32 rows, so the offset
+// fits when ldc < 2^25 -- else `wide` takes 64-bit addresses, one value at a time).  At an edge
+// the loads' rows and columns are clamped into the matrix (the values read for positions outside
+// are never stored): no load sits under a per-lane condition.  A load under a per-lane branch makes
+// the compiler, which cannot count the memory operations in flight across such branches, wait for
+// every one of them before each later use of a loaded value -- one memory round trip per store.
+template <bool VEC>
+__device__ __attribute__((always_inline)) inline f32x16 mfma_block_c(int M, int N, const float* __restrict__ C,
+                                                                     long ldc, int r0, int c0, int li, int lh) {
+    f32x16 c;
+    // (r0, c0) is the same in every lane; said so, the row base lives in scalar registers
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    // rows min(r0 + rr, M - 1): offsets from row rb = min(r0, M - 1) are >= 0 even for a block
+    // wholly below the matrix
+    const int rb = imin(r0, M - 1), rlim = M - 1 - rb, rd = r0 - rb;
+    const char* base = reinterpret_cast<const char*>(C + (long)rb * ldc);
+    if (ldc >= (1L << 25)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = VEC ? li : (r >> 2) * 8 + (r & 3) + 4 * lh;
+            const int cc = VEC ? imin(c0 + (r >> 2) * 8 + lh * 4, N - 4) + (r & 3) : imin(c0 + li, N - 1);
+            c[r] = C[((long)rb + imin(rd + rr, rlim)) * ldc + cc];
+            asm volatile("" ::: "memory");  // one value at a time: no 64-bit address held across loads
+        }
+        return c;
+    }
     if (VEC) {
+        const uint32_t row_off = (uint32_t)(imin(rd + li, rlim) * ldc) * 4u;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m_base + i * 32 + li;
-            if (row >= M) continue;
-            const float* prow = C + (long)row * ldc;
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t off = row_off + 4u * (uint32_t)imin(c0 + q * 8 + lh * 4, N - 4);  // N % 4 == 0
+            const f32x4 v = *reinterpret_cast<const f32x4*>(base + off);
+            asm volatile("" ::: "memory");  // in program order: each offset computed just before its load
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = n_base + j * 32 + q * 8 + lh * 4;
-                    if (col >= N) continue;
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(prow + col);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cv[i][j][4 * q + e] = v[e];
-                }
+            for (int e = 0; e < 4; ++e) c[4 * q + e] = v[e];
         }
     } else {
+        // register r holds row 8*(r/4) + 4*lh + r%4 of the block
+        const uint32_t col_off = 4u * (uint32_t)imin(c0 + li, N - 1);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int lrow = m_base + i * 32 + lh * 4;
+        for (int r = 0; r < 16; ++r) {
+            const int rr = imin(rd + (r >> 2) * 8 + (r & 3) + 4 * lh, rlim);
+            c[r] = *reinterpret_cast<const float*>(base + ((uint32_t)(rr * ldc) * 4u + col_off));
+            asm volatile("" ::: "memory");
+        }
+    }
+    return c;
+}
+template <bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma_block_store(int M, int N, float* __restrict__ C, long ldc,
+                                                                       int r0, int c0, int li, int lh,
+                                                                       const f32x16& x) {
+    if (VEC) {
+        const int row = r0 + li;
+        if (row >= M) return;
+        float* prow = C + (long)row * ldc;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n_base + j * 32 + li;
-                if (col >= N) continue;
-                const float* pl = C + (long)lrow * ldc + col;
+        for (int q = 0; q < 4; ++q) {
+            const int col = c0 + q * 8 + lh * 4;  // the 4 columns are all inside or all outside
+            if (col < N)
+                *reinterpret_cast<f32x4*>(prow + col) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        }
+    } else {
+        const int lrow = r0 + lh * 4, col = c0 + li;
+        if (col >= N) return;
+        float* pl = C + (long)lrow * ldc + col;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dr = (r >> 2) * 8 + (r & 3);
-                    if (lrow + dr < M) cv[i][j][r] = pl[dr * ldc];
-                }
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int dr = (r >> 2) * 8 + (r & 3);
+            if (lrow + dr < M) pl[dr * ldc] = x[r];
         }
     }
 }
 
-// C := alpha * acc + beta * C over a wave's output blocks.  With beta != 0 the C values of a
-// block are loaded before its first store: the row stride is a run-time value, so the compiler
-// cannot tell a later load from an earlier store's address and would otherwise wait out one
-// memory round trip per loaded value.  (The 128-bit path's loads of one row differ by constant
-// offsets and already issue together; with several blocks per wave it keeps them that way,
-// which needs no extra registers.)  With PRE the C values come from cv instead, filled by
-// mfma_load_c at the start of the tile.
+// The C values of a wave's output blocks for the beta term, in the accumulators' layout.  Kernels
+// of one-round grids read them at the start of the tile, after their first operand loads, so that
+// the read's latency hides under the K loop instead of stalling the epilogue.
+template <int FM, int FN, bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma_load_c(int M, int N, const float* __restrict__ C,
+                                                                  long ldc, f32x16 (&cv)[FM][FN], int m_base,
+                                                                  int n_base, int li, int lh) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) cv[i][j] = mfma_block_c<VEC>(M, N, C, ldc, m_base + i * 32, n_base + j * 32, li, lh);
+}
+
+// C := alpha * acc + beta * C over a wave's output blocks (C not read when beta == 0).  The C
+// values come from cv (PRE), or are read here a block at a time, all of a block's reads before
+// its first store (16 registers, whatever the number of blocks).
 template <int FM, int FN, bool VEC, bool PRE = false>
 __device__ __attribute__((always_inline)) inline void mfma_epilogue(int M, int N, float alpha, float beta,
                                                                     float* __restrict__ C, long ldc,
                                                                     const f32x16 (&acc)[FM][FN], int m_base,
                                                                     int n_base, int li, int lh,
                                                                     const f32x16 (*cv)[FN] = nullptr) {
-    if (VEC) {
-        constexpr bool BATCH = PRE || FM * FN == 1;  // C values taken from registers
-        f32x16 cl[FM][FN];
-        if (BATCH && !PRE && beta != 0.f) mfma_load_c<FM, FN, VEC>(M, N, C, ldc, cl, m_base, n_base, li, lh);
-        const f32x16 (*cs)[FN] = PRE ? cv : cl;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m_base + i * 32 + li;
-            if (row >= M) continue;
-            float* prow = C + (long)row * ldc;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j) {
+            const int r0 = m_base + i * 32, c0 = n_base + j * 32;
+            // alpha * acc rounded, then beta * C added by one fused multiply-add, in the C values'
+            // own registers
+            f32x16 x;
+            if (beta != 0.f) {
+                x = PRE ? cv[i][j] : mfma_block_c<VEC>(M, N, C, ldc, r0, c0, li, lh);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // N % 4 == 0 and col % 4 == 0: the 4 columns are all inside or all outside
-                    const int col = n_base + j * 32 + q * 8 + lh * 4;
-                    if (col >= N) continue;
-                    f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                               acc[i][j][4 * q + 3]};
-                    v *= alpha;
-                    f32x4* pc = reinterpret_cast<f32x4*>(prow + col);
-                    if (beta != 0.f) {
-                        if (BATCH) {
-                            const f32x4 c = {cs[i][j][4 * q + 0], cs[i][j][4 * q + 1], cs[i][j][4 * q + 2],
-                                             cs[i][j][4 * q + 3]};
-                            v += beta * c;
-                        } else {
-                            v += beta * *pc;
-                        }
-                    }
-                    *pc = v;
-                }
+                for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(beta, x[r], alpha * acc[i][j][r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = alpha * acc[i][j][r];
             }
+            mfma_block_store<VEC>(M, N, C, ldc, r0, c0, li, lh, x);
         }
-    } else {
-        // register r holds row 8*(r/4) + 4*lh + r%4 of the block: one per-lane pointer per block,
-        // and a wave-uniform row step (8*(r/4) + r%4) * ldc per register
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int lrow = m_base + i * 32 + lh * 4;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n_base + j * 32 + li;
-                if (col >= N) continue;
-                float* pl = C + (long)lrow * ldc + col;
-                f32x16 c;
-                if (beta != 0.f) {
-                    if (PRE) {
-                        c = cv[i][j];
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int dr = (r >> 2) * 8 + (r & 3);
-                            if (lrow + dr < M) c[r] = pl[dr * ldc];
-                        }
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dr = (r >> 2) * 8 + (r & 3);
-                    if (lrow + dr < M) {
-                        float x = alpha * acc[i][j][r];
-                        if (beta != 0.f) x += beta * c[r];
-                        pl[dr * ldc] = x;
-                    }
-                }
-            }
-        }
-    }
 }
 
 // 16x16x4 blocks (v_mfma_f32_16x16x4_f32): lane l brings X(l % 16, k) and Y(k, l % 16) with
@@ -493,8 +484,57 @@ __device__ __attribute__((always_inline)) inline f32x4 mfma16_step(float a, floa
                  : __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// The C values of a wave's 16x16 blocks in the accumulators' layout (li = lane % 16,
-// lh = lane / 16; entries outside the matrix are left unset).
+// The beta term's C values and the stores of one 16x16 block at (r0, c0), in the accumulators'
+// layout, under the same rules as the 32x32 blocks' (a uniform row base and 32-bit per-lane byte
+// offsets; clamped rows and columns at an edge, no load under a per-lane condition).
+template <bool VEC>
+__device__ __attribute__((always_inline)) inline f32x4 mfma16_block_c(int M, int N, const float* __restrict__ C,
+                                                                      long ldc, int r0, int c0, int li, int lh) {
+    f32x4 c;
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    const int rb = imin(r0, M - 1), rlim = M - 1 - rb, rd = r0 - rb;  // as for the 32x32 blocks
+    const char* base = reinterpret_cast<const char*>(C + (long)rb * ldc);
+    if (ldc >= (1L << 25)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = VEC ? li : 4 * lh + r;
+            const int cc = VEC ? imin(c0 + 4 * lh, N - 4) + r : imin(c0 + li, N - 1);
+            c[r] = C[((long)rb + imin(rd + rr, rlim)) * ldc + cc];
+            asm volatile("" ::: "memory");
+        }
+        return c;
+    }
+    if (VEC) {
+        const uint32_t off = (uint32_t)(imin(rd + li, rlim) * ldc) * 4u + 4u * (uint32_t)imin(c0 + 4 * lh, N - 4);
+        return *reinterpret_cast<const f32x4*>(base + off);  // N % 4 == 0
+    }
+    const uint32_t col_off = 4u * (uint32_t)imin(c0 + li, N - 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        c[r] = *reinterpret_cast<const float*>(base + ((uint32_t)(imin(rd + 4 * lh + r, rlim) * ldc) * 4u + col_off));
+        asm volatile("" ::: "memory");
+    }
+    return c;
+}
+template <bool VEC>
+__device__ __attribute__((always_inline)) inline void mfma16_block_store(int M, int N, float* __restrict__ C,
+                                                                         long ldc, int r0, int c0, int li, int lh,
+                                                                         const f32x4& x) {
+    if (VEC) {
+        // N % 4 == 0 and col % 4 == 0: the 4 columns are all inside or all outside
+        const int row = r0 + li, col = c0 + 4 * lh;
+        if (row < M && col < N) *reinterpret_cast<f32x4*>(C + (long)row * ldc + col) = x;
+    } else {
+        const int row = r0 + 4 * lh, col = c0 + li;
+        if (col >= N) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (row + r < M) C[(long)(row + r) * ldc + col] = x[r];
+    }
+}
+
+// The C values of a wave's 16x16 blocks in the accumulators' layout (li = lane % 16, lh = lane / 16).
 template <int FM, int FN, bool VEC>
 __device__ __attribute__((always_inline)) inline void mfma16_load_c(int M, int N, const float* __restrict__ C,
                                                                     long ldc, f32x4 (&cv)[FM][FN], int m_base,
@@ -502,22 +542,11 @@ __device__ __attribute__((always_inline)) inline void mfma16_load_c(int M, int N
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            if (VEC) {
-                const int row = m_base + i * 16 + li, col = n_base + j * 16 + 4 * lh;
-                if (row < M && col < N) cv[i][j] = *reinterpret_cast<const f32x4*>(C + (long)row * ldc + col);
-            } else {
-                const int row = m_base + i * 16 + 4 * lh, col = n_base + j * 16 + li;
-                if (col >= N) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (row + r < M) cv[i][j][r] = C[(long)(row + r) * ldc + col];
-            }
-        }
+        for (int j = 0; j < FN; ++j) cv[i][j] = mfma16_block_c<VEC>(M, N, C, ldc, m_base + i * 16, n_base + j * 16, li, lh);
 }
 
 // C := alpha * acc + beta * C over a wave's 16x16 blocks (C not read when beta == 0).  All C
-// values are loaded before the first store (four registers a block), or come from cv (PRE).
+// values are read before the first store (four registers a block), or come from cv (PRE).
 template <int FM, int FN, bool VEC, bool PRE = false>
 __device__ __attribute__((always_inline)) inline void mfma16_epilogue(int M, int N, float alpha, float beta,
                                                                       float* __restrict__ C, long ldc,
@@ -531,24 +560,11 @@ __device__ __attribute__((always_inline)) inline void mfma16_epilogue(int M, int
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            if (VEC) {
-                // N % 4 == 0 and col % 4 == 0: the 4 columns are all inside or all outside
-                const int row = m_base + i * 16 + li, col = n_base + j * 16 + 4 * lh;
-                if (row >= M || col >= N) continue;
-                f32x4 v = alpha * acc[i][j];
-                if (beta != 0.f) v += beta * cs[i][j];
-                *reinterpret_cast<f32x4*>(C + (long)row * ldc + col) = v;
-            } else {
-                const int row = m_base + i * 16 + 4 * lh, col = n_base + j * 16 + li;
-                if (col >= N) continue;
+            f32x4 x;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (row + r < M) {
-                        float x = alpha * acc[i][j][r];
-                        if (beta != 0.f) x += beta * cs[i][j][r];
-                        C[(long)(row + r) * ldc + col] = x;
-                    }
-            }
+            for (int r = 0; r < 4; ++r)
+                x[r] = beta != 0.f ? __builtin_fmaf(beta, cs[i][j][r], alpha * acc[i][j][r]) : alpha * acc[i][j][r];
+            mfma16_block_store<VEC>(M, N, C, ldc, m_base + i * 16, n_base + j * 16, li, lh, x);
         }
 }
 

@@ -209,6 +209,71 @@ def test_every_output_stored_exactly_once(v):
         assert counts.min() == 1 and counts.max() == 1, (v["name"], M, N)
 
 
+def c_reads(v, M, N, ldc):
+    """For every register of every MFMA block the epilogue handles (mfma_block_c / mfma16_block_c
+    restated): the (row, col) it would store and the (row, col) its beta-term read loads, and
+    the read's byte offset from its row base where the 32-bit form applies (ldc < 2^25).  Arrays
+    over (block, lane), one entry per register."""
+    BM, BN, NT = v["BM"], v["BN"], v["threads"] // v["ksplit"]
+    WM, WN = v["WM_or_TM"], v["WN_or_TN"]
+    MB = mfma_block(v)
+    waves_n = BN // WN
+    r0s, c0s = [], []
+    for tm, tn in itertools.product(range(-(-M // BM)), range(-(-N // BN))):
+        for wave in range(NT // 64):
+            wm0, wn0 = (wave // waves_n) * WM, (wave % waves_n) * WN
+            for i, j in itertools.product(range(WM // MB), range(WN // MB)):
+                r0s.append(tm * BM + wm0 + i * MB)
+                c0s.append(tn * BN + wn0 + j * MB)
+    r0 = np.array(r0s)[:, None]
+    c0 = np.array(c0s)[:, None]
+    lane = np.arange(64)[None, :]
+    li, lh = lane % MB, lane // MB
+    rb = np.minimum(r0, M - 1)
+    rlim, rd = M - 1 - rb, r0 - rb
+    out = []
+    for r in range(MB * MB // 64):
+        if MB == 32 and v["vec"]:
+            srow, scol = r0 + li, c0 + (r // 4) * 8 + lh * 4 + r % 4
+            rr = np.minimum(rd + li, rlim)
+            col = np.minimum(c0 + (r // 4) * 8 + lh * 4, N - 4) + r % 4
+        elif MB == 32:
+            srow, scol = r0 + (r // 4) * 8 + r % 4 + 4 * lh, c0 + li
+            rr = np.minimum(rd + (r // 4) * 8 + r % 4 + 4 * lh, rlim)
+            col = np.minimum(c0 + li, N - 1)
+        elif v["vec"]:
+            srow, scol = r0 + li, c0 + 4 * lh + r
+            rr = np.minimum(rd + li, rlim)
+            col = np.minimum(c0 + 4 * lh, N - 4) + r
+        else:
+            srow, scol = r0 + 4 * lh + r, c0 + li
+            rr = np.minimum(rd + 4 * lh + r, rlim)
+            col = np.minimum(c0 + li, N - 1)
+        off = (rr.astype(np.int64) * ldc + col) * 4 if ldc < (1 << 25) else None
+        out.append((srow, scol, rb + rr, np.broadcast_to(col, srow.shape), off))
+    return out
+
+
+@pytest.mark.parametrize("v", [v for v in VARIANTS if v["kind"] == "mfma"],
+                         ids=[v["name"] for v in VARIANTS if v["kind"] == "mfma"])
+def test_epilogue_c_reads_in_bounds(v):
+    """The beta term's reads of C never leave the matrix (rows and columns clamped at an edge,
+    a row base inside the matrix even for a block wholly below it), read exactly the element the
+    same register stores wherever that element exists, and keep the 32-bit offsets of the
+    ldc < 2^25 form non-negative and under 2^32."""
+    cases = [(M, N, ldc) for (M, N, _) in SHAPES for ldc in (N, N + 4 if v["vec"] else N + 3)]
+    cases += [(M, N, ldc) for (M, N, _) in SHAPES[3:8] for ldc in ((1 << 25) - 4, (1 << 25) + 4)]
+    for M, N, ldc in cases:
+        if v["vec"] and N % 4:
+            continue
+        for srow, scol, row, col, off in c_reads(v, M, N, ldc):
+            assert (row >= 0).all() and (row < M).all() and (col >= 0).all() and (col < N).all()
+            inside = (srow < M) & (scol < N)
+            assert (row[inside] == srow[inside]).all() and (col[inside] == scol[inside]).all()
+            if off is not None:
+                assert (off >= 0).all() and (off < (1 << 32)).all()
+
+
 @pytest.mark.parametrize("ks", [2, 4])
 @pytest.mark.parametrize("K,BK", [(1, 16), (16, 16), (17, 16), (777, 16), (96, 32), (4096, 32)])
 def test_splitk_slab_assignment_covers_k_once(ks, K, BK):
