@@ -161,7 +161,7 @@ __device__ __attribute__((always_inline)) inline const float* uniform_ptr(const 
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
-          bool SPREAD = false, int MB = 32>
+          bool SPREAD = false, int MB = 32, int EB = 0>
 __global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -324,6 +324,107 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     // the C values of the beta term first: the oldest loads, consumed only by the epilogue
     Acc cv[FM][FN];
     if (CPRE && g.beta != 0.f) mfma_block_load_c<MB, FM, FN, VEC>(M, N, g.C, g.ldc, cv, m0 + wm0, n0 + wn0, li, lh);
+    if constexpr (EB > 0) {
+        // Early barrier (EB = P): the barrier that opens slab s + 1 sits P fragment groups before
+        // the end of slab s.  Fragment reads run P groups ahead of the MFMAs (P + 1 register
+        // buffers, buffer (s KK + kk) % (P + 1) for group kk of slab s), so every read of slab s has
+        // been issued, and is waited for, before that barrier; the stage of slab s is free right
+        // after it, and slab s + STAGES is requested there.  The barrier's wait for the slowest wave
+        // then overlaps the P groups of MFMAs still to issue, and each slab's loads are requested
+        // P groups earlier than in the form above.
+        constexpr int P = EB, NB = EB + 1;
+        static_assert(P < KK, "the barrier sits inside the slab");
+        static_assert((STAGES * KK) % NB == 0, "the fragment buffers follow the ring's stages");
+        static_assert(FAIR == 0, "no drain ordering with the early barrier");
+        static_assert(Cfg::LPW * STAGES < 64, "vmcnt counts at most 63 loads in flight");
+        using IC0 = std::integral_constant<int, 0>;
+        using IC1 = std::integral_constant<int, 1 % STAGES>;
+        using IC2 = std::integral_constant<int, 2 % STAGES>;
+        using IC3 = std::integral_constant<int, 3 % STAGES>;
+        // prologue: the whole ring requested (every stage is free); wait for slab 0
+#pragma unroll
+        for (int t = 0; t < STAGES; ++t) {
+            if (t < nfull)
+                issue(t, Whole{});
+            else if (t < nslab)
+                issue(t, Tail{});
+        }
+        wait_slabs<Cfg::LPW>(imin(STAGES, nslab) - 1);
+        if (nfull == 0) {
+            fix_tail(0);
+            wait_vm_lgkm0<0>();
+        }
+        dl_barrier();
+        MfmaFrag<FM, FN> F[NB];
+#pragma unroll
+        for (int q = 0; q < P; ++q) read_frag(F[q], 0, q);
+        constexpr int LPG = (Cfg::LPW + P - 1) / P;  // spread requests per fragment group after the barrier
+        // Slab s, stage STC = s % STAGES.  FULL: slabs s + 1 .. s + STAGES exist and are whole.
+        auto slab_eb = [&](int s, auto stage, auto full) {
+            constexpr int STC = decltype(stage)::value;
+            constexpr bool FULL = decltype(full)::value;
+            constexpr bool SP = SPREAD && FULL;
+            const bool next = FULL || s + 1 < nslab;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                if (kk == KK - P && next) {
+                    // slabs requested after slab s + 1: s + 2 .. min(s + STAGES - 1, nslab - 1)
+                    if (FULL) {
+                        wait_vm_lgkm0<Cfg::LPW * (STAGES - 2)>();
+                    } else {
+                        wait_slabs<Cfg::LPW>(imin(s + STAGES - 1, nslab - 1) - (s + 1));
+                        if (s + 1 >= nfull) {
+                            fix_tail(s + 1);
+                            wait_vm_lgkm0<0>();
+                        }
+                    }
+                    dl_barrier();
+                    if (!SP) {
+                        if (FULL || s + STAGES < nfull)
+                            issue(s + STAGES, Whole{});
+                        else if (s + STAGES < nslab)
+                            issue(s + STAGES, Tail{});
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int gn = kk + P;  // the group read now, counted from slab s's first
+                if (gn < KK)
+                    read_frag(F[(STC * KK + gn) % NB], STC, gn);
+                else if (next)
+                    read_frag(F[(STC * KK + gn) % NB], (STC + 1) % STAGES, gn - KK);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_frag(F[(STC * KK + kk) % NB]);
+                if (SP && kk >= KK - P) {
+#pragma unroll
+                    for (int q = (kk - (KK - P)) * LPG; q < (kk - (KK - P) + 1) * LPG && q < Cfg::LPW; ++q)
+                        issue_one(s + STAGES, q);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        using Full = std::integral_constant<bool, true>;
+        using Checked = std::integral_constant<bool, false>;
+        SGEMM_PHASE_STAMP(1);
+        int s = 0;
+        for (; s + 2 * STAGES - 1 < nfull; s += STAGES) {
+            slab_eb(s, IC0{}, Full{});
+            slab_eb(s + 1, IC1{}, Full{});
+            if (STAGES > 2) slab_eb(s + 2, IC2{}, Full{});
+            if (STAGES > 3) slab_eb(s + 3, IC3{}, Full{});
+        }
+        // the last slabs, still STAGES to a trip so that every stage is known (s % STAGES == 0 here)
+        for (; s < nslab; s += STAGES) {
+            slab_eb(s, IC0{}, Checked{});
+            if (s + 1 < nslab) slab_eb(s + 1, IC1{}, Checked{});
+            if (STAGES > 2 && s + 2 < nslab) slab_eb(s + 2, IC2{}, Checked{});
+            if (STAGES > 3 && s + 3 < nslab) slab_eb(s + 3, IC3{}, Checked{});
+        }
+        SGEMM_PHASE_STAMP(2);
+        mfma_block_epilogue<MB, FM, FN, VEC, CPRE>(M, N, g.alpha, g.beta, g.C, g.ldc, acc, m0 + wm0, n0 + wn0, li,
+                                                  lh, cv);
+        SGEMM_PHASE_STAMP(3);
+        return;
+    }
     // prologue: slabs 0 .. D-1 requested; wait for slab 0 (the later ones may stay in flight)
 #pragma unroll
     for (int s = 0; s < D; ++s) {

@@ -621,15 +621,49 @@ def dl_ring_events(stages, nslab, nfull, mine):
     return ev
 
 
-def check_dl_ring(stages, nslab, nfull, mine):
+def dl_ring_events_eb(stages, nslab, nfull, KK, P):
+    """The same for the early-barrier form (EB = P) of sgemm_mfma_dl_kernel, one tile: the whole
+    ring requested up front; in slab s, P fragment groups before its end, the wait for slab s + 1,
+    its fix-up, the barrier and the request of slab s + STAGES; fragment groups read P ahead of
+    their MFMAs, so ("read", t) once per 8-deep group of slab t."""
+    ev = []
+    for t in range(min(stages, nslab)):
+        ev.append(("issue", t))
+    ev.append(("wait", min(stages, nslab) - 1))
+    if nfull == 0:
+        ev.append(("fix", 0))
+        ev.append(("wait", 0))
+    ev.append(("barrier",))
+    for q in range(P):
+        ev.append(("read", 0))
+    for s in range(nslab):
+        for kk in range(KK):
+            if kk == KK - P and s + 1 < nslab:
+                ev.append(("wait", min(s + stages - 1, nslab - 1) - (s + 1)))
+                if s + 1 >= nfull:
+                    ev.append(("fix", s + 1))
+                    ev.append(("wait", 0))
+                ev.append(("barrier",))
+                if s + stages < nslab:
+                    ev.append(("issue", s + stages))
+            g = s * KK + kk + P
+            if g < nslab * KK:
+                ev.append(("read", g // KK))
+    ev.append(("epilogue", 0))
+    return ev
+
+
+def check_dl_ring(stages, nslab, nfull, mine, ev=None):
     """Every wave runs the same sequence, so a barrier orders each wave's operations before it
     against every wave's operations after it.  Checks: a slab's loads have landed (and, if it
     crosses K, been fixed up) before the barrier that precedes its first read; a stage is requested
     again only after a barrier that follows the last read of its previous slab; every slab is
     requested once, and read; the epilogues come once per tile, in order."""
-    ev = dl_ring_events(stages, nslab, nfull, mine)
+    if ev is None:
+        ev = dl_ring_events(stages, nslab, nfull, mine)
     total = mine * nslab
     inflight, landed, fixed = [], set(), set()
+    landed_at, fixed_at = {}, {}
     last_read = {}          # slab -> index of its last read
     last_barrier = -1
     stage_of_req = {}       # stage -> slab last requested into it
@@ -648,10 +682,13 @@ def check_dl_ring(stages, nslab, nfull, mine):
         elif kind == "wait":
             n = e[1]
             while len(inflight) > max(n, 0):
-                landed.add(inflight.pop(0))
+                gs = inflight.pop(0)
+                landed.add(gs)
+                landed_at[gs] = idx
         elif kind == "fix":
             assert e[1] in landed and e[1] % nslab >= nfull
             fixed.add(e[1])
+            fixed_at[e[1]] = idx
         elif kind == "barrier":
             last_barrier = idx
         elif kind == "read":
@@ -659,9 +696,11 @@ def check_dl_ring(stages, nslab, nfull, mine):
             assert gs in landed, (stages, nslab, nfull, mine, gs)
             if gs % nslab >= nfull:
                 assert gs in fixed
-            # the slab's data must have landed before the last barrier (other waves' loads)
+            # every wave's loads (and fix-ups) of the slab are done before the last barrier
             if gs not in last_read:
-                assert ev.index(("issue", gs)) < last_barrier
+                assert landed_at[gs] < last_barrier, (stages, nslab, nfull, mine, gs)
+                if gs % nslab >= nfull:
+                    assert fixed_at[gs] < last_barrier
             last_read[gs] = idx
         elif kind == "epilogue":
             epis.append(e[1])
@@ -676,6 +715,36 @@ def test_dl_ring_protocol(stages):
             nfull = nslab - 1 if tail else nslab
             for mine in (1, 2, 3, 5):
                 check_dl_ring(stages, nslab, nfull, mine)
+
+
+@pytest.mark.parametrize("stages", [2, 3, 4])
+def test_dl_ring_protocol_early_barrier(stages):
+    """The early-barrier form for every P the kernel accepts (P < KK, (STAGES KK) % (P + 1) == 0)."""
+    n = 0
+    for KK in (1, 2, 4, 8):
+        for P in range(1, KK):
+            if (stages * KK) % (P + 1):
+                continue
+            for nslab in (1, 2, 3, 4, 5, 7, 9, 12):
+                for tail in (False, True):
+                    nfull = nslab - 1 if tail else nslab
+                    check_dl_ring(stages, nslab, nfull, 1, dl_ring_events_eb(stages, nslab, nfull, KK, P))
+                    n += 1
+    assert n > 0
+
+
+def test_dl_ring_early_barrier_model_catches_mistakes():
+    """Requesting slab s + STAGES before the early barrier, or reading slab s + 1's first group
+    before the barrier that publishes it, is caught."""
+    ev = dl_ring_events_eb(3, 8, 8, 4, 2)
+    i = next(k for k, e in enumerate(ev) if e[0] == "issue" and e[1] >= 3)
+    j = max(k for k in range(i) if ev[k][0] == "barrier")
+    with pytest.raises(AssertionError):
+        check_dl_ring(3, 8, 8, 1, ev[:j] + [ev[i]] + ev[j:i] + ev[i + 1:])
+    b = next(k for k, e in enumerate(ev) if e[0] == "barrier" and k > 6)  # the first one in the loop
+    r = next(k for k in range(b, len(ev)) if ev[k] == ("read", 1))
+    with pytest.raises(AssertionError):
+        check_dl_ring(3, 8, 8, 1, ev[:b] + [ev[r]] + ev[b:r] + ev[r + 1:])
 
 
 def test_dl_ring_model_catches_a_short_wait():
