@@ -182,7 +182,7 @@ def _name(v):
     (1111, 1113, 1001, True, "mfma16l_32x64"),  # small_full, unaligned
     (1089, 728, 5752, False, "mfma32l_64x64"),  # small_longk, aligned: the direct-to-LDS ring
     (4096, 4096, 4096, False, "mfma32_128x128"),
-    (65536, 64, 1024, False, "mfma32_128x64"),  # skinny
+    (65536, 64, 1024, False, "mfma32d_128x64"),  # skinny: the deep 128x64 kernel
 ])
 def test_dispatch_families(M, N, K, ld_odd, prefix):
     """Which kernel family and workgroup tile the shape classes pick; the 128-bit forms exactly
