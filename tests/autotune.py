@@ -45,6 +45,8 @@ CASES = [
     ("ragged2500x3500x1000", "shallow", "ragged3001x5003x777", 2500, 3500, 1000, None, None, None, False),
     ("shallow4096x4096x512", "shallow", "square4096", 4096, 4096, 512, None, None, None, True),
     ("shallow3072x3072x768", "shallow", "square1024_beta", 3072, 3072, 768, None, None, None, True),
+    ("shallow2560x3584x320", "shallow", "square256", 2560, 3584, 320, None, None, None, True),
+    ("shallow2048x2048x896", "shallow", "square1024_beta", 2048, 2048, 896, None, None, None, True),
     ("medium2585x6716x2000", "medium", "square4096", 2585, 6716, 2000, None, None, None, True),
     ("medium3000x3000x3000", "medium", "square4096", 3000, 3000, 3000, None, None, None, True),
     ("shard1024x4096x4096", "medium", "square4096", 1024, 4096, 4096, None, None, None, True),
@@ -66,9 +68,12 @@ CASES = [
     ("longk777x1501x3001", "small_full", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
     ("longk1199x587x3229", "small_longk", "ragged3001x5003x777", 1199, 587, 3229, None, None, None, False),
     ("longk1003x777x2503", "small_longk", "ragged3001x5003x777", 1003, 777, 2503, None, None, None, False),
-    ("square256", "small_shortk", "square256", None, None, None, None, None, None, True),
-    ("shortk822x124x88", "small_shortk", "square256", 822, 124, 88, None, None, None, True),
-    ("shortk2664x180x284", "small_shortk", "square256", 2664, 180, 284, None, None, None, True),
+    ("square256", "tiny", "square256", None, None, None, None, None, None, True),
+    ("shortk822x124x88", "tiny", "square256", 822, 124, 88, None, None, None, True),
+    ("shortk2664x180x284", "tiny", "square256", 2664, 180, 284, None, None, None, True),
+    ("shortk700x100x333", "tiny", "ragged3001x5003x777", 700, 100, 333, None, None, None, False),
+    ("shortk2048x1536x384", "small_shortk", "square1024_beta", 2048, 1536, 384, None, None, None, True),
+    ("shortk1536x1024x256", "small_shortk", "square256", 1536, 1024, 256, None, None, None, True),
     ("shortk7195x426x167", "small_shortk", "ragged3001x5003x777", 7195, 426, 167, None, None, None, False),
     ("shortk516x1306x236", "small_shortk", "ragged3001x5003x777", 516, 1306, 236, None, None, None, False),
     ("tiny1554x64x5093", "tiny", "ragged3001x5003x777", 1554, 64, 5093, None, None, None, False),
@@ -77,6 +82,7 @@ CASES = [
     ("full1111x1113x1001", "small_full", "ragged3001x5003x777", 1111, 1113, 1001, None, None, None, False),
     ("full900x1500x833", "small_full", "ragged3001x5003x777", 900, 1500, 833, None, None, None, False),
     ("full1200x1300x700", "small_full", "square1024_beta", 1200, 1300, 700, None, None, None, True),
+    ("full1400x1000x1400", "small_full", "square256", 1400, 1000, 1400, None, None, None, True),
     ("small892x1083x609", "small", "ragged3001x5003x777", 892, 1083, 609, None, None, None, False),
     ("small1000x800x1000", "small", "square1024_beta", 1000, 800, 1000, None, None, None, True),
     ("small512x512x512", "tiny", "square256", 512, 512, 512, None, None, None, True),
@@ -122,6 +128,51 @@ def read_table():
         for m in re.finditer(r'\{(k\w+), (\d), "([\w]+)"\},\s*//[^\n]*?best ([\d.]+)[^\n]*$', open(TABLE).read(), re.M):
             out[(ids[m.group(1)], int(m.group(2)))] = (m.group(3), float(m.group(4)))
     return out
+
+
+def shape_class(M, N, K):
+    """The shape class the library gives an M x N x K product (shape_class in csrc/sgemm.hip,
+    restated; tests/test_autotune_cpu.py checks the two agree)."""
+    def cd(a, b):
+        return -(-a // b)
+    t64 = cd(M, 64) * cd(N, 64)
+    if N <= 32 and t64 >= 128:
+        return "narrow"
+    if N <= 64 and t64 >= 128:
+        return "skinny"
+    t = cd(M, 128) * cd(N, 128)
+    if t < 256:
+        if t64 < 128:
+            return "tiny"
+        if K < 512:
+            return "small_shortk"
+        if K >= 2048 and t64 >= 384:
+            return "medium"
+        if t64 <= 256:
+            return "small_longk" if K >= 2048 else "small"
+        return "small_full"
+    if K < 128:
+        return "tiny_k"
+    if t >= 2048:
+        return "huge"
+    if K <= 1024:
+        return "shallow"
+    if t * 100 >= cd(t, 1024) * 1024 * 85:
+        return "large"
+    return "long_k" if t >= 512 and K >= 4096 else "medium"
+
+
+def load_results(paths):
+    """The records of one or more saved runs (tuning sweeps or regret runs), a later file's record
+    of a (case, variant) replacing an earlier one's, each labelled with the shape class the library
+    gives its shape (a regret run labels its shapes "random"; an older sweep may predate a class
+    boundary)."""
+    merged = {}
+    for path in paths:
+        with open(path) as f:
+            for r in json.load(f)["results"]:
+                merged[(r["case"], r["variant"])] = dict(r, **{"class": shape_class(r["M"], r["N"], r["K"])})
+    return list(merged.values())
 
 
 def choose_winners(results, keep_margin):
@@ -233,7 +284,9 @@ def main() -> int:
     ap.add_argument("--warm-time", type=float, default=0.03,
                     help="seconds of untimed launches before timing a candidate (the engine clock ramps "
                          "up under sustained load; short kernels alone would be timed at a lower clock)")
-    ap.add_argument("--table-from", default=None, help="write the table from a saved results file (no GPU)")
+    ap.add_argument("--table-from", default=None,
+                    help="write the table from saved results files, comma-separated: tuning sweeps and regret "
+                         "runs, the later file wins for a (case, variant) both hold (no GPU)")
     ap.add_argument("--keep-margin", type=float, default=0.01,
                     help="keep the table's entry unless the winner's score beats it by more than this fraction")
     ap.add_argument("--regret", type=int, default=0,
@@ -247,9 +300,7 @@ def main() -> int:
                     help="run only the cases of this vector-load class (0: unaligned, 1: aligned)")
     args = ap.parse_args()
     if args.table_from:
-        with open(args.table_from) as f:
-            saved = json.load(f)
-        write_table(choose_winners(saved["results"], args.keep_margin))
+        write_table(choose_winners(load_results(args.table_from.split(",")), args.keep_margin))
         return 0
 
     import numpy as np

@@ -87,3 +87,43 @@ def test_committed_table_names_real_variants():
         assert info["trans_a"] == 0 and info["trans_b"] == 0, name
         seen.add((cls, vec))
     assert seen == {(c, v) for c in autotune.CLASS_IDS.values() for v in ("0", "1")}
+
+
+def test_case_labels_match_the_library_classes():
+    """Every representative case sits in the shape class it tunes: the library dispatches it to
+    the table's entry for that (class, alignment)."""
+    from fp32_gemm_05_amd.workloads import WORKLOADS
+    table = autotune.read_table()
+    names = {sg.sgemm_variant_name(i): i for i in range(sg.sgemm_num_variants())}
+    A, B, C = 0x10000000, 0x20000000, 0x30000000  # aligned, never dereferenced
+    for label, cls, wname, M, N, K, _dist, _a, _b, vec in autotune.CASES:
+        w = WORKLOADS[wname]
+        M, N, K = M or w.M, N or w.N, K or w.K
+        if vec:
+            assert N % 4 == 0 and K % 4 == 0, label
+        want = names[table[(cls, int(vec))][0]]
+        # a scalar case as the library sees unaligned data (A one float off 16-byte alignment)
+        got = sg.sgemm_select_variant(M, N, K, A + (0 if vec else 4), K, B, N, C, N)
+        assert got == want, (label, cls, sg.sgemm_variant_name(got), sg.sgemm_variant_name(want))
+
+
+def test_shape_class_mirror_matches_the_library():
+    """The tuner's restatement of the library's shape classes, on random shapes of the regret
+    distribution and on each class boundary: the library dispatches every shape to the table's
+    entry for the class the mirror gives it."""
+    import numpy as np
+    table = autotune.read_table()
+    names = {sg.sgemm_variant_name(i): i for i in range(sg.sgemm_num_variants())}
+    rng = np.random.default_rng(5)
+    shapes = [(int(np.exp(rng.uniform(np.log(16), np.log(70000)))), int(np.exp(rng.uniform(np.log(4), np.log(9000)))),
+               int(np.exp(rng.uniform(np.log(4), np.log(9000))))) for _ in range(400)]
+    shapes += [(64 * 127, 64, 512), (64 * 128, 64, 512), (2048, 32 * 64, 511), (2048, 2048, 127), (2048, 2048, 128),
+               (256 * 64, 64 * 128, 1024), (256 * 64, 64 * 128, 1025), (128 * 32, 128 * 64, 4096)]
+    for M, N, K in shapes:
+        cls = autotune.shape_class(M, N, K)
+        got = sg.sgemm_select_variant(M, N, K, 0x10000004, K, 0x20000000, N, 0x30000000, N)  # scalar class
+        assert got == names[table[(cls, 0)][0]], (M, N, K, cls, sg.sgemm_variant_name(got))
+        Na, Ka = N + (-N) % 4, K + (-K) % 4  # and the vector class (two classes can share a scalar entry)
+        got = sg.sgemm_select_variant(M, Na, Ka, 0x10000000, Ka, 0x20000000, Na, 0x30000000, Na)
+        cls = autotune.shape_class(M, Na, Ka)
+        assert got == names[table[(cls, 1)][0]], (M, Na, Ka, cls, sg.sgemm_variant_name(got))
