@@ -68,10 +68,10 @@ CASES = [
     ("longk777x1501x3001", "small_full", "ragged3001x5003x777", 777, 1501, 3001, None, None, None, False),
     ("longk1199x587x3229", "small_longk", "ragged3001x5003x777", 1199, 587, 3229, None, None, None, False),
     ("longk1003x777x2503", "small_longk", "ragged3001x5003x777", 1003, 777, 2503, None, None, None, False),
-    ("square256", "tiny", "square256", None, None, None, None, None, None, True),
-    ("shortk822x124x88", "tiny", "square256", 822, 124, 88, None, None, None, True),
-    ("shortk2664x180x284", "tiny", "square256", 2664, 180, 284, None, None, None, True),
-    ("shortk700x100x333", "tiny", "ragged3001x5003x777", 700, 100, 333, None, None, None, False),
+    ("square256", "tiny_shortk", "square256", None, None, None, None, None, None, True),
+    ("shortk822x124x88", "tiny_shortk", "square256", 822, 124, 88, None, None, None, True),
+    ("shortk2664x180x284", "tiny_shortk", "square256", 2664, 180, 284, None, None, None, True),
+    ("shortk700x100x333", "tiny_shortk", "ragged3001x5003x777", 700, 100, 333, None, None, None, False),
     ("shortk2048x1536x384", "small_shortk", "square1024_beta", 2048, 1536, 384, None, None, None, True),
     ("shortk1536x1024x256", "small_shortk", "square256", 1536, 1024, 256, None, None, None, True),
     ("shortk7195x426x167", "small_shortk", "ragged3001x5003x777", 7195, 426, 167, None, None, None, False),
@@ -112,7 +112,7 @@ STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
              "small_shortk": "kSmallShortK", "long_k": "kLongK", "small_full": "kSmallFull",
-             "narrow": "kNarrow"}
+             "narrow": "kNarrow", "tiny_shortk": "kTinyShortK"}
 
 
 def log(msg):
@@ -143,7 +143,7 @@ def shape_class(M, N, K):
     t = cd(M, 128) * cd(N, 128)
     if t < 256:
         if t64 < 128:
-            return "tiny"
+            return "tiny_shortk" if K < 512 else "tiny"
         if K < 512:
             return "small_shortk"
         if K >= 2048 and t64 >= 384:
@@ -277,8 +277,8 @@ def main() -> int:
     ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "libsgemm_autotune.json"))
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
-                    default="large,huge,long_k,shallow,medium,tiny_k,small,small_full,tiny,small_shortk,small_longk,"
-                            "skinny,narrow")
+                    default="large,huge,long_k,shallow,medium,tiny_k,small,small_full,tiny,tiny_shortk,small_shortk,"
+                            "small_longk,skinny,narrow")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
     ap.add_argument("--warm-time", type=float, default=0.03,

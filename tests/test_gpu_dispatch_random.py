@@ -26,6 +26,7 @@ REGIONS = [
     ("narrow", (8200, 40000), (1, 32), (64, 1500)),
     ("skinny", (8200, 40000), (33, 64), (64, 1500)),
     ("tiny", (40, 700), (40, 700), (512, 3000)),
+    ("tiny_shortk", (40, 700), (40, 700), (8, 511)),
     ("small_shortk", (100, 1500), (100, 1500), (8, 511)),
     ("small", (600, 1900), (600, 1900), (512, 4000)),
     ("grid", (2000, 5000), (2000, 5000), (128, 2500)),
