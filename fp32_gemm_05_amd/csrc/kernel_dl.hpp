@@ -90,12 +90,25 @@ struct DlCfg {
 // flight than there are only makes a vmcnt wait stricter.  The loads have no register results.
 // M0 holds the LDS address (M0 is reserved to the compiler, so the asm restores it); the s_nop
 // covers the wait state between an SALU write of M0 and the load that reads it.
-template <int W>
+// NT: the load does not allocate in the caches (operand panels that no other workgroup reads).
+template <int W, bool NT = false>
 __device__ __attribute__((always_inline)) inline void dl_load(const void* base, uint32_t off, uint32_t lds) {
     uint32_t keep;
-    if (W == 16)
+    if (W == 16 && NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3 nt\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(off), "s"(base)
+            : "memory");
+    else if (W == 16)
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(off), "s"(base)
+            : "memory");
+    else if (NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3 nt\n\ts_mov_b32 m0, %0"
             : "=&s"(keep)
             : "s"(lds), "v"(off), "s"(base)
             : "memory");
@@ -106,12 +119,24 @@ __device__ __attribute__((always_inline)) inline void dl_load(const void* base, 
             : "s"(lds), "v"(off), "s"(base)
             : "memory");
 }
-template <int W>
+template <int W, bool NT = false>
 __device__ __attribute__((always_inline)) inline void dl_load_at(const void* p, uint32_t lds) {
     uint32_t keep;
-    if (W == 16)
+    if (W == 16 && NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(p)
+            : "memory");
+    else if (W == 16)
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+            : "=&s"(keep)
+            : "s"(lds), "v"(p)
+            : "memory");
+    else if (NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off nt\n\ts_mov_b32 m0, %0"
             : "=&s"(keep)
             : "s"(lds), "v"(p)
             : "memory");
@@ -161,7 +186,7 @@ __device__ __attribute__((always_inline)) inline const float* uniform_ptr(const 
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
-          bool SPREAD = false, int MB = 32, int EB = 0>
+          bool SPREAD = false, int MB = 32, int EB = 0, bool NTA = false>
 __global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -227,10 +252,10 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
             if (!TAIL) {
-                dl_load<W>(a_tile + k0, a_off[j], lds_addr(sa + j * CH));
+                dl_load<W, NTA>(a_tile + k0, a_off[j], lds_addr(sa + j * CH));
             } else {
                 const int k = a_kin(j);
-                dl_load_at<W>(reinterpret_cast<const char*>(a_tile) + a_off[j] + 4L * (imin(k0 + k, K - E) - k),
+                dl_load_at<W, NTA>(reinterpret_cast<const char*>(a_tile) + a_off[j] + 4L * (imin(k0 + k, K - E) - k),
                               lds_addr(sa + j * CH));
             }
         }
@@ -249,7 +274,7 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     auto issue_one = [&](int s, int q) {
         const int st = s % STAGES, k0 = s * BK;
         if (q < LA)
-            dl_load<W>(a_tile + k0, a_off[q], lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH));
+            dl_load<W, NTA>(a_tile + k0, a_off[q], lds_addr(lds_a + st * Cfg::A_STAGE + (wave * LA + q) * CH));
         else
             dl_load<W>(b_tile + (long)k0 * ldb, b_off[q - LA],
                        lds_addr(lds_b + st * Cfg::B_STAGE + (wave * LB + q - LA) * CH));

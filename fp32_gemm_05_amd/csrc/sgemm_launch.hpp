@@ -107,10 +107,10 @@ hipError_t launch_mfma_deep(const GemmArgs& g, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, int FAIR = 0, bool CPRE = false,
-          bool SPREAD = false, int MB = 32, int EB = 0>
+          bool SPREAD = false, int MB = 32, int EB = 0, bool NTA = false>
 hipError_t launch_mfma_dl(const GemmArgs& g, hipStream_t stream) {
     using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>;
-    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SPREAD, MB, EB>;
+    auto kernel = &sgemm_mfma_dl_kernel<BM, BN, BK, WM, WN, STAGES, W, OCC, FAIR, CPRE, SPREAD, MB, EB, NTA>;
     int tiles_m = ceil_div(g.M, BM), tiles_n = ceil_div(g.N, BN);
     int group_m = group_rows(tiles_m, tiles_n);
     GemmArgs a = g;
@@ -291,6 +291,11 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
      DlCfg<BM, BN, BK, WM, WN, STAGES, W, 16>::LDS_BYTES,                                                 \
      &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, W, OCC, 0, CPRE, SP, 16>, 0, 0, 0, 0, 0, STAGES, 0, 16}
 #define DL16_NAME(BM, BN, BK, WM, WN, STAGES) "mfma16l_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #STAGES
+// A loaded without allocating in the caches ("_nta": the streamed panels of the skinny shapes)
+#define DLNT_ROW(BM, BN, BK, WM, WN, STAGES, W, FAIR, SP, NAME)                                          \
+    {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT, W == 16,                  \
+     DlCfg<BM, BN, BK, WM, WN, STAGES, W>::LDS_BYTES,                                                     \
+     &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, W, 0, FAIR, false, SP, 32, 0, true>, 0, 0, 0, 0, 0, STAGES}
 // the barrier that opens each slab EB fragment groups early ("_ebN"; 32x32 or 16x16 blocks)
 #define DLEB_ROW(BM, BN, BK, WM, WN, STAGES, W, CPRE, SP, MB, EB, NAME)                                   \
     {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W, MB>::NT, W == 16,              \
@@ -472,5 +477,9 @@ const Variant kVariants[] = {
     DLEB_ROW(64, 64, 16, 32, 32, 3, 4, false, true, 32, 1, DL_NAME(64, 64, 16, 32, 32, 3) "_sp_eb1_scalar"),
     DLEB_ROW(64, 64, 32, 32, 16, 3, 16, true, true, 16, 1, DL16_NAME(64, 64, 32, 32, 16, 3) "_cp_sp_eb1_vec"),
     DLEB_ROW(32, 64, 32, 32, 16, 3, 16, true, true, 16, 1, DL16_NAME(32, 64, 32, 32, 16, 3) "_cp_sp_eb1_vec"),
+    // nontemporal A: the skinny stream (the B swizzle needs 64-wide tiles: not the narrow one)
+    DLNT_ROW(128, 64, 32, 64, 32, 3, 16, 3, false, DL_NAME(128, 64, 32, 64, 32, 3) "_d3_nta_vec"),
+    DLNT_ROW(128, 64, 32, 64, 32, 3, 16, 3, true, DL_NAME(128, 64, 32, 64, 32, 3) "_d3_sp_nta_vec"),
+    DLNT_ROW(128, 64, 32, 64, 32, 3, 4, 3, false, DL_NAME(128, 64, 32, 64, 32, 3) "_d3_nta_scalar"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
