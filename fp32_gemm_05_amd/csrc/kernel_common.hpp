@@ -357,7 +357,7 @@ __device__ __attribute__((always_inline)) inline f32x16 mfma_step(float a, float
 // The beta term's C values and the stores of one 32x32 block whose top-left element is (r0, c0),
 // in the accumulators' layout.  Addresses are a wave-uniform row base plus a 32-bit per-lane byte
 // offset (one register however many values are in flight; the block spans 32 rows, so the offset
-// fits when ldc < 2^25 -- else `wide` takes 64-bit addresses, one value at a time).  At an edge
+// fits when ldc < 2^25 -- for a larger ldc a 64-bit address is formed for each value in turn).  At an edge
 // the loads' rows and columns are clamped into the matrix (the values read for positions outside
 // are never stored): no load sits under a per-lane condition.  A load under a per-lane branch makes
 // the compiler, which cannot count the memory operations in flight across such branches, wait for
@@ -366,7 +366,8 @@ template <bool VEC>
 __device__ __attribute__((always_inline)) inline f32x16 mfma_block_c(int M, int N, const float* __restrict__ C,
                                                                      long ldc, int r0, int c0, int li, int lh) {
     f32x16 c;
-    // (r0, c0) is the same in every lane; said so, the row base lives in scalar registers
+    // (r0, c0) is the same in every lane; stated with readfirstlane, the row base lives in scalar
+    // registers
     r0 = __builtin_amdgcn_readfirstlane(r0);
     c0 = __builtin_amdgcn_readfirstlane(c0);
     // rows min(r0 + rr, M - 1): offsets from row rb = min(r0, M - 1) are >= 0 even for a block
