@@ -53,6 +53,14 @@ __device__ __host__ inline int dl_swz_b(int k) {
     static_assert(MB == 32 || MB == 16, "32x32 or 16x16 MFMA blocks");
     return ((k >> 2) & (64 / MB - 1)) * (MB / 4);
 }
+// B rows of 32 floats (one 32x32 block wide) span only half the banks, so the column flip above has
+// no room: instead row k is stored at row k ^ ((k >> 2) & 1) (rows 4-7 of every 8 trade places in
+// pairs), which gives the rows 4 h + t of the two lane groups opposite parities, i.e. opposite
+// halves of the 64 banks.  The map is its own inverse.  Rows of 64 floats or more keep k.
+template <int BN>
+__device__ __host__ inline int dl_brow(int k) {
+    return BN == 32 ? k ^ ((k >> 2) & 1) : k;
+}
 
 // MB: edge of the MFMA blocks (32: v_mfma_f32_32x32x2_f32; 16: v_mfma_f32_16x16x4_f32, whose
 // smaller wave tiles let a workgroup of one tile hold more waves).  A fragment group spans
@@ -73,7 +81,8 @@ struct DlCfg {
     static_assert(W == 4 || W == 16, "32-bit or 128-bit loads");
     static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
     static_assert(A_STAGE % (CH * NW) == 0 && B_STAGE % (CH * NW) == 0, "whole loads per wave");
-    static_assert(BN % 64 == 0, "the B swizzle needs rows of 16 quads or more");
+    static_assert(BN % 64 == 0 || (BN == 32 && WN == 32 && MB == 32),
+                  "B rows of 16 quads or more, or one 32x32 block wide (the row-permuted layout)");
     static_assert(MB == 32 || MB == 16, "32x32 or 16x16 MFMA blocks");
     static_assert(BK % KG == 0 && BM % WM == 0 && BN % WN == 0 && WM % MB == 0 && WN % MB == 0, "tiling");
     static_assert(NT <= 1024, "workgroup size");
@@ -223,7 +232,8 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
         const int f = (wave * LA + j) * CH + E * lane;
         return 4 * (((f % BK) / 4) ^ dl_swz_a<QA, MB>(f / BK)) + f % 4;
     };
-    auto b_kin = [&](int j) { return ((wave * LB + j) * CH + E * lane) / BN; };
+    // the k of a lane's B load: the row it fills, through the row permutation of 32-float rows
+    auto b_kin = [&](int j) { return dl_brow<BN>(((wave * LB + j) * CH + E * lane) / BN); };
     uint32_t a_off[LA], b_off[LB];  // byte offsets from the slab's first element
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
@@ -234,8 +244,9 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
         const int f = (wave * LB + j) * CH + E * lane;
-        const int k = f / BN, u = (f % BN) / 4;
-        const int n = imin(n0 + 4 * (u ^ dl_swz_b<MB>(k)) + f % 4, N - E) - n0;
+        const int kr = f / BN, u = (f % BN) / 4;
+        const int k = dl_brow<BN>(kr);
+        const int n = imin(n0 + 4 * (BN == 32 ? u : u ^ dl_swz_b<MB>(kr)) + f % 4, N - E) - n0;
         b_off[j] = (uint32_t)(((long)k * ldb + n) * 4);
     }
     const float* a_tile = g.A + (long)m0 * lda;  // A(m0, 0)
@@ -314,6 +325,11 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     int b_frag[FN];
 #pragma unroll
     for (int fj = 0; fj < FN; ++fj) b_frag[fj] = 4 * lh * BN + ((wn0 + fj * MB + li) ^ (MB * lh));
+    // 32-float B rows: row 4 h + t of a fragment group sits at row dl_brow(4 h + t) (KG kk is a
+    // multiple of 8, which the permutation leaves alone)
+    int b_row32[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b_row32[t] = dl_brow<BN>(4 * lh + t) * BN + li;
     auto read_frag = [&](MfmaFrag<FM, FN>& f, int st, int kk) {
         const float* sa = lds_a + st * Cfg::A_STAGE;
         const float* sb = lds_b + st * Cfg::B_STAGE;
@@ -323,7 +339,8 @@ sgemm_mfma_dl_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) f.b[fj][t] = sb[b_frag[fj] + (Cfg::KG * kk + t) * BN];
+            for (int t = 0; t < 4; ++t)
+                f.b[fj][t] = BN == 32 ? sb[b_row32[t] + Cfg::KG * kk * BN] : sb[b_frag[fj] + (Cfg::KG * kk + t) * BN];
     };
 
     Acc acc[FM][FN];
@@ -562,6 +579,7 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, int W, int OCC, bo
 __global__ void __launch_bounds__((DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT))
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 sgemm_mfma_dlp_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    static_assert(BN % 64 == 0, "the persistent form keeps the column-flipped B layout");
     using Cfg = DlCfg<BM, BN, BK, WM, WN, STAGES, W>;
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KK = BK / 8, LA = Cfg::LA, LB = Cfg::LB, D = Cfg::D;
     constexpr int QA = Cfg::QPR_A, CH = Cfg::CH, E = W / 4;

@@ -291,7 +291,7 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
      DlCfg<BM, BN, BK, WM, WN, STAGES, W, 16>::LDS_BYTES,                                                 \
      &launch_mfma_dl<BM, BN, BK, WM, WN, STAGES, W, OCC, 0, CPRE, SP, 16>, 0, 0, 0, 0, 0, STAGES, 0, 16}
 #define DL16_NAME(BM, BN, BK, WM, WN, STAGES) "mfma16l_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #STAGES
-// A loaded without allocating in the caches ("_nta": the streamed panels of the skinny shapes)
+// A loaded without allocating in the caches ("_nta": the streamed panels of the skinny and narrow shapes)
 #define DLNT_ROW(BM, BN, BK, WM, WN, STAGES, W, FAIR, SP, NAME)                                          \
     {NAME, kMfma, BM, BN, BK, WM, WN, DlCfg<BM, BN, BK, WM, WN, STAGES, W>::NT, W == 16,                  \
      DlCfg<BM, BN, BK, WM, WN, STAGES, W>::LDS_BYTES,                                                     \
@@ -477,7 +477,14 @@ const Variant kVariants[] = {
     DLEB_ROW(64, 64, 16, 32, 32, 3, 4, false, true, 32, 1, DL_NAME(64, 64, 16, 32, 32, 3) "_sp_eb1_scalar"),
     DLEB_ROW(64, 64, 32, 32, 16, 3, 16, true, true, 16, 1, DL16_NAME(64, 64, 32, 32, 16, 3) "_cp_sp_eb1_vec"),
     DLEB_ROW(32, 64, 32, 32, 16, 3, 16, true, true, 16, 1, DL16_NAME(32, 64, 32, 32, 16, 3) "_cp_sp_eb1_vec"),
-    // nontemporal A: the skinny stream (the B swizzle needs 64-wide tiles: not the narrow one)
+    // 32x32 tiles of one wave: a workgroup's barrier waits for its own wave only (B rows of 32
+    // floats, row-permuted); slower than the 64x64 and 32x64 tiles at 256^3 and 1024^3
+    DL_ROW(32, 32, 32, 32, 32, 3, 16, 0, 0, true, true, DL_NAME(32, 32, 32, 32, 32, 3) "_cp_sp_vec"),
+    // the narrow stream's 128x32 tiles, nontemporal A: within a few per cent of the dispatched
+    // kernels, never ahead
+    DLNT_ROW(128, 32, 32, 32, 32, 3, 16, 3, false, DL_NAME(128, 32, 32, 32, 32, 3) "_d3_nta_vec"),
+    DLNT_ROW(128, 32, 32, 32, 32, 3, 4, 3, false, DL_NAME(128, 32, 32, 32, 32, 3) "_d3_nta_scalar"),
+    // nontemporal A: the skinny stream
     DLNT_ROW(128, 64, 32, 64, 32, 3, 16, 3, false, DL_NAME(128, 64, 32, 64, 32, 3) "_d3_nta_vec"),
     DLNT_ROW(128, 64, 32, 64, 32, 3, 16, 3, true, DL_NAME(128, 64, 32, 64, 32, 3) "_d3_sp_nta_vec"),
     DLNT_ROW(128, 64, 32, 64, 32, 3, 4, 3, false, DL_NAME(128, 64, 32, 64, 32, 3) "_d3_nta_scalar"),

@@ -360,6 +360,21 @@ def dl_swz_b(k, mb=32):
     return ((np.asarray(k) >> 2) & (64 // mb - 1)) * (mb // 4)
 
 
+def dl_brow(k, bn):
+    """The LDS row that holds B row k of a stage: rows of 32 floats trade rows 4-7 of every 8 in
+    pairs (k ^ ((k >> 2) & 1)); wider rows keep k."""
+    k = np.asarray(k)
+    return k ^ ((k >> 2) & 1) if bn == 32 else k
+
+
+def dl_b_read_offset(k, n, bn, mb, lh):
+    """Float offset, in a B stage, of the fragment read of B row k (of the stage), column n (of the
+    tile) by lane group lh: the column-flipped layout, or the row-permuted one for 32-float rows."""
+    if bn == 32:
+        return dl_brow(k, bn) * bn + n
+    return k * bn + (n ^ (mb * lh))
+
+
 
 DL = [v for v in VARIANTS if v.get("dl_stages")]
 
@@ -398,8 +413,8 @@ def dl_slab_model(v, M, N, K, tm, tn, s):
             f = (wave * LB + j) * CH + E * lane
             kr = f // BN
             u = (f % BN) // 4
-            n = np.minimum(n0 + 4 * (u ^ dl_swz_b(kr, MB)) + f % 4, N - E)
-            k = k0 + kr
+            n = np.minimum(n0 + 4 * (u if BN == 32 else u ^ dl_swz_b(kr, MB)) + f % 4, N - E)
+            k = k0 + dl_brow(kr, BN)
             kl = np.minimum(k, K - 1) if tail else k
             assert (kl >= 0).all() and (kl < K).all() and (n >= 0).all() and (n + E <= N).all()
             for e in range(E):
@@ -448,9 +463,8 @@ def test_dl_kernel_loads_and_fragments(v):
                                     want_k = np.where(k < K, k, -1)
                                     assert (got[:, 0] == want_r).all() and (got[:, 1] == want_k).all()
                             for fj in range(WN // MB):
-                                b_frag = 4 * lh * BN + ((wn0 + fj * MB + li) ^ (MB * lh))
                                 for t in range(4):
-                                    got = b_lds[b_frag + (KG * kk + t) * BN]
+                                    got = b_lds[dl_b_read_offset(KG * kk + 4 * lh + t, wn0 + fj * MB + li, BN, MB, lh)]
                                     k = k0 + KG * kk + 4 * lh + t
                                     col = np.minimum(tn * BN + wn0 + MB * fj + li, N - 1)
                                     # columns past N read a clamped column of the last 4-column
@@ -469,6 +483,10 @@ def test_dl_swizzles_are_row_permutations():
     for mb in (32, 16):
         for k in range(64):
             assert sorted((np.arange(16) ^ dl_swz_b(k, mb)).tolist()) == list(range(16))
+    # the 32-float rows' row permutation: a bijection of every 8 rows, its own inverse
+    k = np.arange(64)
+    assert sorted(dl_brow(k, 32).tolist()) == list(range(64)) and (dl_brow(dl_brow(k, 32), 32) == k).all()
+    assert ((dl_brow(k, 32) >> 3) == (k >> 3)).all()
 
 
 # How the LDS serves one access of 64 lanes (64 banks of 4 bytes), as measured on MI355X: two
@@ -521,7 +539,7 @@ def dl_fragment_addresses(v, swz_a=dl_swz_a):
                 out.append(("a", 4 * ((wm0 + li + MB * fi) * BK + 4 * ((G * kk + lh) ^ swz_a(wm0 + li, BK // 4, MB)))))
             for fj in range(WN // MB):
                 for t in range(4):
-                    out.append(("b", 4 * ((KG * kk + 4 * lh + t) * BN + ((wn0 + fj * MB + li) ^ (MB * lh)))))
+                    out.append(("b", 4 * dl_b_read_offset(KG * kk + 4 * lh + t, wn0 + fj * MB + li, BN, MB, lh)))
     return out
 
 
