@@ -47,6 +47,9 @@ CASES = [
     ("shallow3072x3072x768", "shallow", "square1024_beta", 3072, 3072, 768, None, None, None, True),
     ("shallow2560x3584x320", "shallow", "square256", 2560, 3584, 320, None, None, None, True),
     ("shallow2048x2048x896", "shallow", "square1024_beta", 2048, 2048, 896, None, None, None, True),
+    ("shallow2880x3776x272", "shallow", "square256", 2880, 3776, 272, None, None, None, True),
+    ("shallow5632x2432x224", "shallow", "square256", 5632, 2432, 224, None, None, None, True),
+    ("shallow2048x2560x640", "shallow", "square1024_beta", 2048, 2560, 640, None, None, None, True),
     ("medium2585x6716x2000", "medium", "square4096", 2585, 6716, 2000, None, None, None, True),
     ("medium3000x3000x3000", "medium", "square4096", 3000, 3000, 3000, None, None, None, True),
     ("shard1024x4096x4096", "medium", "square4096", 1024, 4096, 4096, None, None, None, True),
@@ -56,6 +59,10 @@ CASES = [
     ("longk1500x6000x6000", "long_k", "ragged3001x5003x777", 1500, 6000, 6001, None, None, None, False),
     ("medium2062x3171x3921", "medium", "ragged3001x5003x777", 2062, 3171, 3921, None, None, None, False),
     ("medium5000x2001x2501", "medium", "ragged3001x5003x777", 5000, 2001, 2501, None, None, None, False),
+    ("medium2301x2703x2101", "medium", "ragged3001x5003x777", 2301, 2703, 2101, None, None, None, False),
+    ("medium4201x5999x1603", "medium", "ragged3001x5003x777", 4201, 5999, 1603, None, None, None, False),
+    ("medium901x4801x1201", "medium", "ragged3001x5003x777", 901, 4801, 1201, None, None, None, False),
+    ("medium6001x401x2301", "medium", "ragged3001x5003x777", 6001, 401, 2301, None, None, None, False),
     ("tinyk5555x1124x68", "tiny_k", "square4096", 5555, 1124, 68, None, None, None, True),
     ("tinyk1953x2052x72", "tiny_k", "square4096", 1953, 2052, 72, None, None, None, True),
     ("tinyk8192x8192x32", "tiny_k", "square4096", 8192, 8192, 32, None, None, None, True),
