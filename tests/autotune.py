@@ -45,11 +45,15 @@ CASES = [
     ("ragged2500x3500x1000", "shallow", "ragged3001x5003x777", 2500, 3500, 1000, None, None, None, False),
     ("shallow4096x4096x512", "shallow", "square4096", 4096, 4096, 512, None, None, None, True),
     ("shallow3072x3072x768", "shallow", "square1024_beta", 3072, 3072, 768, None, None, None, True),
-    ("shallow2560x3584x320", "shallow", "square256", 2560, 3584, 320, None, None, None, True),
+    ("shallow2560x3584x320", "shallow_shortk", "square256", 2560, 3584, 320, None, None, None, True),
     ("shallow2048x2048x896", "shallow", "square1024_beta", 2048, 2048, 896, None, None, None, True),
-    ("shallow2880x3776x272", "shallow", "square256", 2880, 3776, 272, None, None, None, True),
-    ("shallow5632x2432x224", "shallow", "square256", 5632, 2432, 224, None, None, None, True),
+    ("shallow2880x3776x272", "shallow_shortk", "square256", 2880, 3776, 272, None, None, None, True),
+    ("shallow5632x2432x224", "shallow_shortk", "square256", 5632, 2432, 224, None, None, None, True),
     ("shallow2048x2560x640", "shallow", "square1024_beta", 2048, 2560, 640, None, None, None, True),
+    ("shallow5001x2301x251", "shallow_shortk", "ragged3001x5003x777", 5001, 2301, 251, None, None, None, False),
+    ("shallow3001x4001x301", "shallow_shortk", "ragged3001x5003x777", 3001, 4001, 301, None, None, None, False),
+    ("shallow2501x2999x449", "shallow_shortk", "ragged3001x5003x777", 2501, 2999, 449, None, None, None, False),
+    ("shallow4401x2901x263", "shallow_shortk", "ragged3001x5003x777", 4401, 2901, 263, None, None, None, False),
     ("medium2585x6716x2000", "medium", "square4096", 2585, 6716, 2000, None, None, None, True),
     ("medium3000x3000x3000", "medium", "square4096", 3000, 3000, 3000, None, None, None, True),
     ("shard1024x4096x4096", "medium", "square4096", 1024, 4096, 4096, None, None, None, True),
@@ -119,7 +123,8 @@ STATES = ("warm", "cold", "dirty")
 CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": "kHuge", "shallow": "kShallow",
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
              "small_shortk": "kSmallShortK", "long_k": "kLongK", "small_full": "kSmallFull",
-             "narrow": "kNarrow", "tiny_shortk": "kTinyShortK"}
+             "narrow": "kNarrow", "tiny_shortk": "kTinyShortK",
+             "shallow_shortk": "kShallowShortK"}
 
 
 def log(msg):
@@ -163,7 +168,7 @@ def shape_class(M, N, K):
     if t >= 2048:
         return "huge"
     if K <= 1024:
-        return "shallow"
+        return "shallow_shortk" if K < 512 else "shallow"
     if t * 100 >= cd(t, 1024) * 1024 * 85:
         return "large"
     return "long_k" if t >= 512 and K >= 4096 else "medium"
@@ -284,7 +289,7 @@ def main() -> int:
     ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "libsgemm_autotune.json"))
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
-                    default="large,huge,long_k,shallow,medium,tiny_k,small,small_full,tiny,tiny_shortk,small_shortk,"
+                    default="large,huge,long_k,shallow,shallow_shortk,medium,tiny_k,small,small_full,tiny,tiny_shortk,small_shortk,"
                             "small_longk,skinny,narrow")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")
@@ -304,10 +309,14 @@ def main() -> int:
                     help="comma-separated name substrings: sweep only the variants whose name contains one "
                          "(the table's current entries are always swept, so the winner is compared with them)")
     ap.add_argument("--vec-class", type=int, default=None, choices=[0, 1],
-                    help="run only the cases of this vector-load class (0: unaligned, 1: aligned)")
+                    help="run only the cases of this vector-load class (0: unaligned, 1: aligned); with "
+                         "--table-from, rewrite only its entries (--classes limits the classes likewise)")
     args = ap.parse_args()
     if args.table_from:
-        write_table(choose_winners(load_results(args.table_from.split(",")), args.keep_margin))
+        classes = set(args.classes.split(","))
+        results = [r for r in load_results(args.table_from.split(","))
+                   if r["class"] in classes and (args.vec_class is None or r["vec_class"] == args.vec_class)]
+        write_table(choose_winners(results, args.keep_margin))
         return 0
 
     import numpy as np
