@@ -154,7 +154,7 @@ def shape_class(M, N, K):
         return "skinny"
     t = cd(M, 128) * cd(N, 128)
     if t < 256:
-        if t64 < 128:
+        if cd(M, 32) * cd(N, 64) <= 256:
             return "tiny_shortk" if K < 512 else "tiny"
         if K < 512:
             return "small_shortk"
