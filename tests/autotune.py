@@ -85,6 +85,7 @@ CASES = [
     ("shortk700x100x333", "tiny_shortk", "ragged3001x5003x777", 700, 100, 333, None, None, None, False),
     ("shortk2048x1536x384", "small_shortk", "square1024_beta", 2048, 1536, 384, None, None, None, True),
     ("shortk1536x1024x256", "small_shortk", "square256", 1536, 1024, 256, None, None, None, True),
+    ("shortk3600x284x148", "small_shortk", "square256", 3600, 284, 148, None, None, None, True),
     ("shortk7195x426x167", "small_shortk", "ragged3001x5003x777", 7195, 426, 167, None, None, None, False),
     ("shortk516x1306x236", "small_shortk", "ragged3001x5003x777", 516, 1306, 236, None, None, None, False),
     ("tiny1554x64x5093", "tiny", "ragged3001x5003x777", 1554, 64, 5093, None, None, None, False),
