@@ -1,6 +1,6 @@
 """Default dispatch on seeded random shapes drawn region by region over the shape classes
 (narrow, skinny, tiny, small with short, medium and long K, shallow / medium / large grids and
-tiny K), with random scalars, alignment, pointer offsets and transpositions, checked against
+tiny K, and shapes that the 32x64 tile count makes tiny although they have 128 or more 64x64 tiles), with random scalars, alignment, pointer offsets and transpositions, checked against
 the float64 oracle on sampled outputs: integer-valued inputs exactly, random floats within
 1e-5*(|alpha|*sum|a*b| + |beta*c|) + 1e-6.  Every call also checks that nothing outside C's
 M x N window was written.
@@ -56,6 +56,23 @@ def _cases():
             dist = "int" if rng.random() < 0.5 else "uniform"
             out.append((f"{region}{i}_{ta}{tb}_{M}x{N}x{K}", M, N, K, ta, tb, alpha, beta, dist, aligned,
                         int(rng.integers(0, 1 << 30))))
+    # tiny by the 32x64 tile count although t64 >= 128: a 64-row tiles, of which the last holds at
+    # most 32 rows, times b 64-column tiles, with a*b >= 128 and (2a - 1)*b <= 256
+    for i in range(PER_REGION):
+        a = int(rng.choice([a for a in range(2, 17) if -(-128 // a) <= 256 // (2 * a - 1)]))
+        b = int(rng.integers(-(-128 // a), 256 // (2 * a - 1) + 1))
+        M = int(rng.integers(64 * (a - 1) + 1, 64 * a - 31))
+        N = int(rng.integers(64 * (b - 1) + 4, 64 * b + 1))
+        K = _loguniform(rng, 8, 511) if i % 2 else _loguniform(rng, 512, 3000)  # tiny_shortk, tiny
+        aligned = bool(rng.integers(0, 2))
+        if aligned:
+            N, K = N - N % 4, max(4, K - K % 4)
+        ta, tb = ("T" if rng.random() < 0.5 else "N"), ("T" if rng.random() < 0.5 else "N")
+        alpha = float(rng.choice([1.0, 0.5, -2.0]))
+        beta = float(rng.choice([0.0, 0.5, -1.5]))
+        dist = "int" if rng.random() < 0.5 else "uniform"
+        out.append((f"tiny_edge{i}_{ta}{tb}_{M}x{N}x{K}", M, N, K, ta, tb, alpha, beta, dist, aligned,
+                    int(rng.integers(0, 1 << 30))))
     return out
 
 
