@@ -198,6 +198,7 @@ def test_dispatch_families(M, N, K, ld_odd, prefix):
     ("T", "N", 333, 555, 777, True, True),     # tiny: every transposition
     ("N", "T", 333, 555, 777, True, True),
     ("T", "T", 512, 512, 512, False, True),
+    ("T", "T", 88, 5428, 2500, False, True),      # tiny by the 32x64 tile count
     ("T", "N", 1001, 1003, 777, True, True),   # small: only with A transposed
     ("N", "T", 1001, 1003, 777, True, False),
     ("T", "T", 4096, 4096, 4096, False, False),
