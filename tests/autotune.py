@@ -93,8 +93,16 @@ CASES = [
     ("ragged1001x1003x777", "small", "ragged3001x5003x777", 1001, 1003, 777, None, None, None, False),
     ("full1111x1113x1001", "small_full", "ragged3001x5003x777", 1111, 1113, 1001, None, None, None, False),
     ("full900x1500x833", "small_full", "ragged3001x5003x777", 900, 1500, 833, None, None, None, False),
-    ("full1200x1300x700", "small_full", "square1024_beta", 1200, 1300, 700, None, None, None, True),
+    ("full1200x1300x700", "small_multi", "square1024_beta", 1200, 1300, 700, None, None, None, True),
     ("full1400x1000x1400", "small_full", "square256", 1400, 1000, 1400, None, None, None, True),
+    ("full1100x1100x1000", "small_full", "square1024_beta", 1100, 1100, 1000, None, None, None, True),
+    ("multi763x2487x641", "small_multi", "ragged3001x5003x777", 763, 2487, 641, None, None, None, False),
+    ("multi1531x1527x1101", "small_multi", "ragged3001x5003x777", 1531, 1527, 1101, None, None, None, False),
+    ("multi1915x1783x1901", "small_multi", "ragged3001x5003x777", 1915, 1783, 1901, None, None, None, False),
+    ("multi635x5111x701", "small_multi", "ragged3001x5003x777", 635, 5111, 701, None, None, None, False),
+    ("multi764x2484x640", "small_multi", "square1024_beta", 764, 2484, 640, None, None, None, True),
+    ("multi1532x1524x1100", "small_multi", "square1024_beta", 1532, 1524, 1100, None, None, None, True),
+    ("multi1916x1780x1900", "small_multi", "square1024_beta", 1916, 1780, 1900, None, None, None, True),
     ("small892x1083x609", "small", "ragged3001x5003x777", 892, 1083, 609, None, None, None, False),
     ("small1000x800x1000", "small", "square1024_beta", 1000, 800, 1000, None, None, None, True),
     ("small512x512x512", "tiny", "square256", 512, 512, 512, None, None, None, True),
@@ -125,7 +133,7 @@ CLASS_IDS = {"skinny": "kSkinny", "small": "kSmall", "large": "kLarge", "huge": 
              "medium": "kMedium", "small_longk": "kSmallLongK", "tiny_k": "kTinyK", "tiny": "kTiny",
              "small_shortk": "kSmallShortK", "long_k": "kLongK", "small_full": "kSmallFull",
              "narrow": "kNarrow", "tiny_shortk": "kTinyShortK",
-             "shallow_shortk": "kShallowShortK"}
+             "shallow_shortk": "kShallowShortK", "small_multi": "kSmallMulti"}
 
 
 def log(msg):
@@ -163,7 +171,7 @@ def shape_class(M, N, K):
             return "medium"
         if t64 <= 256:
             return "small_longk" if K >= 2048 else "small"
-        return "small_full"
+        return "small_full" if t64 <= 384 else "small_multi"
     if K < 128:
         return "tiny_k"
     if t >= 2048:
@@ -290,7 +298,7 @@ def main() -> int:
     ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "libsgemm_autotune.json"))
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--classes",
-                    default="large,huge,long_k,shallow,shallow_shortk,medium,tiny_k,small,small_full,tiny,tiny_shortk,small_shortk,"
+                    default="large,huge,long_k,shallow,shallow_shortk,medium,tiny_k,small,small_full,small_multi,tiny,tiny_shortk,small_shortk,"
                             "small_longk,skinny,narrow")
     ap.add_argument("--min-time", type=float, default=0.15, help="seconds of timed launches per candidate")
     ap.add_argument("--points", type=int, default=2048, help="sampled outputs checked per candidate")

@@ -119,7 +119,8 @@ def test_shape_class_mirror_matches_the_library():
                int(np.exp(rng.uniform(np.log(4), np.log(9000))))) for _ in range(400)]
     shapes += [(64 * 127, 64, 512), (64 * 128, 64, 512), (2048, 32 * 64, 511), (2048, 2048, 127), (2048, 2048, 128),
                (256 * 64, 64 * 128, 1024), (256 * 64, 64 * 128, 1025), (128 * 32, 128 * 64, 4096),
-               (512, 1024, 700), (513, 1024, 700), (512, 1024, 300), (513, 1024, 300), (472, 1079, 2500)]
+               (512, 1024, 700), (513, 1024, 700), (512, 1024, 300), (513, 1024, 300), (472, 1079, 2500),
+               (1024, 1536, 700), (1025, 1536, 700), (1025, 1536, 2048)]
     for M, N, K in shapes:
         cls = autotune.shape_class(M, N, K)
         got = sg.sgemm_select_variant(M, N, K, 0x10000004, K, 0x20000000, N, 0x30000000, N)  # scalar class
