@@ -1,7 +1,8 @@
 // hbm_read.hip -- a streaming-read kernel used as the read-bandwidth reference of the
 // profiling summaries (what a plain read of a buffer reaches on this GPU), next to which the
-// HBM-bound SGEMM workload is judged.  Not part of libsgemm: built as libhbm_read.so and
-// called only by fp32_gemm_05_amd/profiling.py.
+// HBM-bound SGEMM workload is judged, and a write of a matrix in the order in which the MFMA
+// epilogue stores C (the write reference of the store-heavy shapes).  Not part of libsgemm:
+// built as libhbm_read.so and called only by fp32_gemm_05_amd/profiling.py.
 #include <hip/hip_runtime.h>
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -33,6 +34,28 @@ __global__ void __launch_bounds__(kThreads) hbm_read_kernel(const f32x4* __restr
 
 long chunk_elems(int chunk_kib) { return (long)chunk_kib * 1024 / 16; }
 
+// Workgroup b writes the 64x64 tile (b / tiles_n, b % tiles_n) of the M x N matrix c (row
+// stride ldc) the way the 32x32x2 MFMA epilogue stores it: wave w owns the 32x32 block
+// (w / 2, w % 2), and value i of lane l goes to row 8 * (i / 4) + 4 * (l / 32) + i % 4 and
+// column l % 32 of the block; NT selects nontemporal stores.
+template <bool NT>
+__global__ void __launch_bounds__(kThreads) tile_write_kernel(float* __restrict__ c, int ldc, int tiles_n,
+                                                               float v) {
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+    const long r0 = (long)tm * 64 + (w / 2) * 32;
+    const long c0 = (long)tn * 64 + (w % 2) * 32 + l % 32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const long r = r0 + 8 * (i / 4) + 4 * (l / 32) + i % 4;
+        const float x = v + (float)i;
+        if (NT)
+            __builtin_nontemporal_store(x, c + r * ldc + c0);
+        else
+            c[r * ldc + c0] = x;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +82,24 @@ __attribute__((visibility("default"))) int hbm_read(const void* buf, long bytes,
     void* args[] = {&p, &n, &chunk, &out};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&hbm_read_kernel), dim3((unsigned)nwg),
                                    dim3(kThreads), args, 0, stream);
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+// Write the M x N matrix at device address c (row stride ldc floats) in 64x64 tiles in the MFMA
+// epilogue's store order, with nontemporal stores when nt != 0.  M and N must be positive
+// multiples of 64 with N <= ldc and (M / 64) * (N / 64) < 2^31.  Returns 0, -1 on invalid
+// arguments, or the hipError_t of the launch.
+__attribute__((visibility("default"))) int hbm_write_tiles(float* c, int M, int N, int ldc, int nt,
+                                                           hipStream_t stream) {
+    if (c == nullptr || M <= 0 || N <= 0 || M % 64 != 0 || N % 64 != 0 || N > ldc) return -1;
+    const long nwg = (long)(M / 64) * (N / 64);
+    if (nwg > 0x7fffffffL) return -1;
+    int tiles_n = N / 64;
+    float v = 1.0f;
+    void* args[] = {&c, &ldc, &tiles_n, &v};
+    const void* k = nt ? reinterpret_cast<const void*>(&tile_write_kernel<true>)
+                       : reinterpret_cast<const void*>(&tile_write_kernel<false>);
+    hipError_t e = hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), args, 0, stream);
     return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -6,6 +6,9 @@
     python -m fp32_gemm_05_amd.profiling read --mib 256 [--mode warm|cold|cold-dirty]
         a streaming read of known size (a hand-written read kernel, libhbm_read.so), warm or after
         evicting the caches: the read bandwidth an HBM-bound kernel can expect under the same protocol.
+    python -m fp32_gemm_05_amd.profiling write --m 8192 --n 8192
+        a matrix written in 64x64 tiles in the MFMA epilogue's store order (plain and nontemporal
+        stores) and by torch's fill_: the write bandwidth a store-heavy shape can expect.
     python -m fp32_gemm_05_amd.profiling stats <kernel_stats.csv> --command "..." --out X.md
         short text summary of a `rocprofv3 --kernel-trace --stats` run.
     python -m fp32_gemm_05_amd.profiling traffic --kernel SUBSTR --fetch F.csv --write W.csv
@@ -122,6 +125,9 @@ def _hbm_read_lib():
     lib.hbm_read_workgroups.argtypes = [ctypes.c_long, ctypes.c_int]
     lib.hbm_read.restype = ctypes.c_int
     lib.hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.hbm_write_tiles.restype = ctypes.c_int
+    lib.hbm_write_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
     return lib
 
 
@@ -252,6 +258,41 @@ def run_read(mib: int, reps: int, mode: str, chunk_kib: int = 1024) -> None:
     med = times[len(times) // 2]
     print(f"read: {mib} MiB {mode}, median {med * 1e3:.1f} us (min {times[0] * 1e3:.1f}) over {reps} -> "
           f"{nbytes / (med * 1e-3) / 1e12:.2f} TB/s", flush=True)
+
+
+def run_write(m: int, n: int, reps: int) -> None:
+    """Write-bandwidth reference: an m x n matrix written in 64x64 tiles in the MFMA epilogue's
+    store order (csrc/hbm_read.hip, hbm_write_tiles), with plain and with nontemporal stores, next
+    to torch's fill_ of the same buffer; medians of back-to-back writes, each between its own
+    events, after 200 untimed ones."""
+    import torch
+    lib = _hbm_read_lib()
+    buf = torch.empty(m * n, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    nbytes = m * n * 4
+
+    def tiles(nt):
+        rc = lib.hbm_write_tiles(buf.data_ptr(), m, n, n, nt, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hbm_write_tiles returned {rc}")
+
+    for label, go in (("tile order, plain stores", lambda: tiles(0)),
+                      ("tile order, nontemporal stores", lambda: tiles(1)),
+                      ("torch fill_", lambda: buf.fill_(2.0))):
+        for _ in range(200):
+            go()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            go()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        med = times[len(times) // 2]
+        print(f"write {m}x{n} ({nbytes / 2**20:.0f} MiB), {label}: median {med * 1e3:.1f} us "
+              f"(min {times[0] * 1e3:.1f}) over {reps} -> {nbytes / (med * 1e-3) / 1e12:.2f} TB/s", flush=True)
+    if float(buf[-1]) != 2.0:
+        raise RuntimeError("fill_ did not write the buffer")
 
 
 def _read_counters(path: str, kernel_substr: str):
@@ -877,6 +918,10 @@ def main(argv=None) -> int:
     p.add_argument("--reps", type=int, default=50)
     p.add_argument("--mode", default="warm", choices=["warm", "cold", "cold-dirty"])
     p.add_argument("--chunk-kib", type=int, default=1024)
+    p = sub.add_parser("write")
+    p.add_argument("--m", type=int, default=8192)
+    p.add_argument("--n", type=int, default=8192)
+    p.add_argument("--reps", type=int, default=50)
     p = sub.add_parser("stats")
     p.add_argument("csv")
     p.add_argument("--title", default="")
@@ -953,6 +998,10 @@ def main(argv=None) -> int:
         run_copy(args.mib, args.reps)
     elif args.cmd == "read":
         run_read(args.mib, args.reps, args.mode, args.chunk_kib)
+    elif args.cmd == "write":
+        if args.m % 64 or args.n % 64 or args.m <= 0 or args.n <= 0:
+            raise SystemExit("write: --m and --n must be positive multiples of 64")
+        run_write(args.m, args.n, args.reps)
     elif args.cmd == "stats":
         cmd_stats(args)
     elif args.cmd == "traffic":

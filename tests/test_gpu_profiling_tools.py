@@ -92,3 +92,23 @@ def test_mfma_issue_rates():
     assert 60.0 <= r32[0] <= 72.0
     assert 30.0 <= r16[0] <= 38.0
     assert d16[0] >= r16[0] - 0.5
+
+
+@pytest.mark.parametrize("nt", [0, 1])
+def test_write_reference_writes_every_element_once(nt):
+    """The write reference stores each element of the M x N window exactly where the MFMA
+    epilogue's lane order puts it (the value it writes depends on the row within a 32-row block
+    only) and nothing in the row padding."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    lib = profiling._hbm_read_lib()
+    M, N, ldc = 128, 192, 256
+    _say(f"[write reference] {M}x{N} ldc={ldc} nt={nt}")
+    buf = torch.full((M, ldc), -7.0, dtype=torch.float32, device="cuda")
+    assert lib.hbm_write_tiles(buf.data_ptr(), M, N, ldc, nt, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    rb = np.arange(M) % 32
+    want = (1.0 + 4 * (rb // 8) + rb % 4).astype(np.float32)
+    assert np.array_equal(got[:, :N], np.repeat(want[:, None], N, axis=1))
+    assert np.all(got[:, N:] == -7.0)

@@ -166,3 +166,15 @@ def test_lds_model_matches_the_committed_measurement():
     for (width, i), lanes in table.items():
         (mine,) = [set(p) - {i} for p in _lds_model_passes(width) if i in p]
         assert lanes == mine, (width, i)
+
+
+def test_write_reference_rejects_bad_shapes_without_launching():
+    """hbm_write_tiles checks its arguments before any HIP call: a null matrix, sizes that are not
+    positive multiples of 64 and a row stride shorter than a row are refused with -1."""
+    lib = profiling._hbm_read_lib()
+    fake = 0x10000000
+    assert lib.hbm_write_tiles(None, 64, 64, 64, 0, None) == -1
+    assert lib.hbm_write_tiles(fake, 63, 64, 64, 0, None) == -1
+    assert lib.hbm_write_tiles(fake, 64, 96, 128, 1, None) == -1
+    assert lib.hbm_write_tiles(fake, 64, 128, 64, 0, None) == -1
+    assert lib.hbm_write_tiles(fake, 0, 64, 64, 0, None) == -1
