@@ -249,27 +249,45 @@ def write_table(winners):
     log(f"wrote {TABLE}")
 
 
+def parse_shapes(text):
+    """"MxNxK,MxNxK,...": explicit shapes for the regret mode (128-bit loads when N and K are
+    multiples of 4, beta 0)."""
+    out = []
+    for item in text.split(","):
+        M, N, K = (int(x) for x in item.lower().split("x"))
+        if min(M, N, K) <= 0:
+            raise ValueError(f"bad shape {item!r}")
+        out.append((M, N, K, N % 4 == 0 and K % 4 == 0, 0.0))
+    return out
+
+
 def regret_mode(args, sg, sweep) -> int:
-    """Dispatch regret on random shapes: for each, every variant is timed and the dispatched one
-    compared with the fastest (time of the dispatched variant / best time)."""
+    """Dispatch regret on random shapes (or on the shapes given with --shapes): for each, every
+    variant is timed and the dispatched one compared with the fastest (time of the dispatched
+    variant / best time)."""
     import numpy as np
 
     rng = np.random.default_rng(args.regret_seed)
     records, summary = [], []
-    for c in range(args.regret):
-        M = int(np.exp(rng.uniform(np.log(256), np.log(8192))))
-        N = int(np.exp(rng.uniform(np.log(64), np.log(8192))))
-        K = int(np.exp(rng.uniform(np.log(64), np.log(8192))))
-        aligned = bool(rng.integers(0, 2))
-        if aligned:
-            N, K = max(4, N - N % 4), max(4, K - K % 4)
-        elif N % 4 == 0 and K % 4 == 0:
-            K += 1
-        beta = float(rng.choice([0.0, 0.5]))
+    shapes = parse_shapes(args.shapes) if args.shapes else []
+    for c in range(len(shapes) if shapes else args.regret):
+        if shapes:
+            M, N, K, aligned, beta = shapes[c]
+            rng = np.random.default_rng(args.regret_seed + c)
+        else:
+            M = int(np.exp(rng.uniform(np.log(256), np.log(8192))))
+            N = int(np.exp(rng.uniform(np.log(64), np.log(8192))))
+            K = int(np.exp(rng.uniform(np.log(64), np.log(8192))))
+            aligned = bool(rng.integers(0, 2))
+            if aligned:
+                N, K = max(4, N - N % 4), max(4, K - K % 4)
+            elif N % 4 == 0 and K % 4 == 0:
+                K += 1
+            beta = float(rng.choice([0.0, 0.5]))
         A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
         B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
         C0 = rng.uniform(-1, 1, (M, N)).astype(np.float32) if beta else np.zeros((M, N), np.float32)
-        label = f"random{c}_{M}x{N}x{K}"
+        label = f"{'shape' if shapes else 'random'}{c}_{M}x{N}x{K}"
         # the variant sgemm would dispatch for these arguments (pointer alignment as torch gives it)
         disp = sg.sgemm_variant_name(sg.sgemm_select_variant(M, N, K, 256, K, 512, N, 768, N))
         recs = sweep(label, "random", A, B, C0, 1.0, beta, aligned, 4242 + c)
@@ -314,6 +332,9 @@ def main() -> int:
                     help="instead of tuning: time every variant on this many random shapes and report how far "
                          "the dispatched variant is from the fastest")
     ap.add_argument("--regret-seed", type=int, default=2024)
+    ap.add_argument("--shapes", default=None,
+                    help="regret mode on these shapes instead of random ones: MxNxK,MxNxK,... (128-bit "
+                         "loads where N and K are multiples of 4); with --only, a probe of chosen variants")
     ap.add_argument("--only", default=None,
                     help="comma-separated name substrings: sweep only the variants whose name contains one "
                          "(the table's current entries are always swept, so the winner is compared with them)")
@@ -421,7 +442,7 @@ def main() -> int:
         torch.cuda.empty_cache()
         return out
 
-    if args.regret:
+    if args.regret or args.shapes:
         return regret_mode(args, sg, sweep)
 
     classes = set(args.classes.split(","))

@@ -129,3 +129,11 @@ def test_shape_class_mirror_matches_the_library():
         got = sg.sgemm_select_variant(M, Na, Ka, 0x10000000, Ka, 0x20000000, Na, 0x30000000, Na)
         cls = autotune.shape_class(M, Na, Ka)
         assert got == names[table[(cls, 1)][0]], (M, Na, Ka, cls, sg.sgemm_variant_name(got))
+
+
+def test_parse_shapes():
+    assert autotune.parse_shapes("472x1079x700,88X5431x2501") == [(472, 1079, 700, False, 0.0),
+                                                                   (88, 5431, 2501, False, 0.0)]
+    assert autotune.parse_shapes("512x1024x560") == [(512, 1024, 560, True, 0.0)]
+    with pytest.raises(ValueError):
+        autotune.parse_shapes("0x4x4")
