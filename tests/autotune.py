@@ -187,11 +187,13 @@ def load_results(paths):
     """The records of one or more saved runs (tuning sweeps or regret runs), a later file's record
     of a (case, variant) replacing an earlier one's, each labelled with the shape class the library
     gives its shape (a regret run labels its shapes "random"; an older sweep may predate a class
-    boundary)."""
+    boundary); records of transposed operand forms are left out."""
     merged = {}
     for path in paths:
         with open(path) as f:
             for r in json.load(f)["results"]:
+                if r.get("op", "NN") != "NN":
+                    continue  # transposed forms are dispatched by their own rules, not by the table
                 merged[(r["case"], r["variant"])] = dict(r, **{"class": shape_class(r["M"], r["N"], r["K"])})
     return list(merged.values())
 
@@ -250,14 +252,20 @@ def write_table(winners):
 
 
 def parse_shapes(text):
-    """"MxNxK,MxNxK,...": explicit shapes for the regret mode (128-bit loads when N and K are
-    multiples of 4, beta 0)."""
+    """"[OP:]MxNxK,...": explicit shapes for the regret mode, OP one of NN (the default), NT, TN,
+    TT (128-bit loads when every stored row length -- N and K, and M for a transposed A -- is a
+    multiple of 4; beta 0).  Returns (M, N, K, aligned, beta, op) tuples."""
     out = []
     for item in text.split(","):
-        M, N, K = (int(x) for x in item.lower().split("x"))
+        op, _, dims = item.rpartition(":")
+        op = (op or "NN").upper()
+        if op not in ("NN", "NT", "TN", "TT"):
+            raise ValueError(f"bad operand form in {item!r}")
+        M, N, K = (int(x) for x in dims.lower().split("x"))
         if min(M, N, K) <= 0:
             raise ValueError(f"bad shape {item!r}")
-        out.append((M, N, K, N % 4 == 0 and K % 4 == 0, 0.0))
+        aligned = N % 4 == 0 and K % 4 == 0 and (op[0] == "N" or M % 4 == 0)
+        out.append((M, N, K, aligned, 0.0, op))
     return out
 
 
@@ -271,8 +279,9 @@ def regret_mode(args, sg, sweep) -> int:
     records, summary = [], []
     shapes = parse_shapes(args.shapes) if args.shapes else []
     for c in range(len(shapes) if shapes else args.regret):
+        op = "NN"
         if shapes:
-            M, N, K, aligned, beta = shapes[c]
+            M, N, K, aligned, beta, op = shapes[c]
             rng = np.random.default_rng(args.regret_seed + c)
         else:
             M = int(np.exp(rng.uniform(np.log(256), np.log(8192))))
@@ -287,10 +296,11 @@ def regret_mode(args, sg, sweep) -> int:
         A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
         B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
         C0 = rng.uniform(-1, 1, (M, N)).astype(np.float32) if beta else np.zeros((M, N), np.float32)
-        label = f"{'shape' if shapes else 'random'}{c}_{M}x{N}x{K}"
-        # the variant sgemm would dispatch for these arguments (pointer alignment as torch gives it)
-        disp = sg.sgemm_variant_name(sg.sgemm_select_variant(M, N, K, 256, K, 512, N, 768, N))
-        recs = sweep(label, "random", A, B, C0, 1.0, beta, aligned, 4242 + c)
+        label = f"{'shape' if shapes else 'random'}{c}_{'' if op == 'NN' else op + '_'}{M}x{N}x{K}"
+        # the variant sgemm_op would dispatch for these arguments (pointer alignment as torch gives it)
+        lda, ldb = (M if op[0] == "T" else K), (K if op[1] == "T" else N)
+        disp = sg.sgemm_variant_name(sg.sgemm_op_select_variant(op[0], op[1], M, N, K, 256, lda, 512, ldb, 768, N))
+        recs = sweep(label, "random", A, B, C0, 1.0, beta, aligned, 4242 + c, op)
         good = [r for r in recs if r["parity"]]
         best = min(good, key=lambda r: r["ms_median"])
         mine = [r for r in good if r["variant"] == disp]
@@ -368,9 +378,11 @@ def main() -> int:
 
     flush = {}
 
-    def sweep(label, cls, A, B, C0, alpha, beta, vec_ok, points_seed):
-        """Time every applicable plain-operand variant on one problem; parity-gate each on sampled
-        outputs.  Returns the result records."""
+    def sweep(label, cls, A, B, C0, alpha, beta, vec_ok, points_seed, op="NN"):
+        """Time every applicable variant of the operand form op ("NN": plain; "NT", "TN", "TT":
+        op(A), op(B) with the transposed operands stored transposed, through sgemm_op) on one
+        problem; parity-gate each on sampled outputs.  Returns the result records."""
+        ta, tb = op[0] == "T", op[1] == "T"
         states = STATES if cls in COLD_CLASSES else ("warm",)
         if len(states) > 1 and not flush:
             flush["buf"] = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
@@ -380,8 +392,9 @@ def main() -> int:
         out = []
         I, J = sample_points(M, N, args.points, seed=points_seed, tile=64)
         ref, bound = oracle.ref_points(A, B, C0, I, J, alpha, beta)
-        dA = torch.from_numpy(A).cuda()
-        dB = torch.from_numpy(B).cuda()
+        dA = torch.from_numpy(np.ascontiguousarray(A.T) if ta else A).cuda()
+        dB = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
+        lda, ldb = dA.shape[1], dB.shape[1]
         dC0 = torch.from_numpy(C0).cuda()
         dC = torch.empty_like(dC0)
         flops = 2.0 * M * N * K
@@ -391,13 +404,13 @@ def main() -> int:
                 continue
             if info["vec"] and not vec_ok:
                 continue
-            if info["trans_a"] or info["trans_b"]:
-                continue  # transposed-operand variants serve sgemm_op only
+            if (bool(info["trans_a"]), bool(info["trans_b"])) != (ta, tb):
+                continue  # each variant serves one operand form
             dC.copy_(dC0)
 
             def call():
-                sg.sgemm_ex(M, N, K, alpha, dA.data_ptr(), K, dB.data_ptr(), N, beta, dC.data_ptr(), N,
-                            stream=stream.cuda_stream, variant=v)
+                sg.sgemm_op_ex(op[0], op[1], M, N, K, alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta,
+                               dC.data_ptr(), N, stream=stream.cuda_stream, variant=v)
 
             call()
             torch.cuda.synchronize()
@@ -432,7 +445,7 @@ def main() -> int:
                 ts = sorted(s.elapsed_time(e) for s, e in evs)
                 med = ts[len(ts) // 2]
                 case = label if len(states) == 1 else f"{label}@{state}"
-                rec = {"case": case, "class": cls, "vec_class": int(vec_ok), "state": state, "M": M, "N": N,
+                rec = {"case": case, "class": cls, "vec_class": int(vec_ok), "state": state, "op": op, "M": M, "N": N,
                        "K": K, "variant": info["name"], "variant_id": v, "parity": ok, "max_err_over_bound": ratio,
                        "ms_median": med, "ms_min": ts[0], "reps": reps, "tflops": flops / (med * 1e-3) / 1e12}
                 out.append(rec)

@@ -199,6 +199,12 @@ def test_dispatch_families(M, N, K, ld_odd, prefix):
     ("N", "T", 333, 555, 777, True, True),
     ("T", "T", 512, 512, 512, False, True),
     ("T", "T", 88, 5428, 2500, False, True),      # tiny by the 32x64 tile count
+    ("T", "N", 768, 512, 600, False, False),      # aligned, A transposed, K < 800, partial 128-deep
+    ("T", "T", 640, 384, 700, False, True),       # panel: 64x64 in T N, the 96-deep form in T T
+    ("N", "T", 768, 512, 600, False, True),
+    ("T", "N", 384, 640, 640, False, True),       # K a multiple of 128
+    ("T", "N", 640, 384, 701, True, True),        # unaligned
+    ("T", "N", 640, 896, 720, False, False),      # small, aligned: 64x64 transposed kernels
     ("T", "N", 1001, 1003, 777, True, True),   # small: only with A transposed
     ("N", "T", 1001, 1003, 777, True, False),
     ("T", "T", 4096, 4096, 4096, False, False),
@@ -215,6 +221,8 @@ def test_op_dispatch_families(ta, tb, M, N, K, odd, direct):
     info = sg.sgemm_variant_info(v)
     assert (info["trans_a"], info["trans_b"]) == (int(ta == "T"), int(tb == "T"))
     assert _name(v).startswith("mfma32r_") == direct, _name(v)
+    if direct and not odd and ta == "T" and K < 800 and K % 128:
+        assert _name(v).startswith("mfma32r_32x32x96_") and _name(v).endswith("_scalar"), _name(v)
     if ta == "N" and tb == "T" and N <= 64 and M >= 65536:
         assert "_nta_nt_" in _name(v) and info["BN"] == (32 if N <= 32 else 64), _name(v)
 

@@ -6,6 +6,7 @@ oracle check on every representative case, the one with the smallest geometric m
 the keep margin.  The table must name only variants the library has, and a vector-load variant
 never serves the scalar class.
 """
+import json
 import math
 import re
 
@@ -132,8 +133,22 @@ def test_shape_class_mirror_matches_the_library():
 
 
 def test_parse_shapes():
-    assert autotune.parse_shapes("472x1079x700,88X5431x2501") == [(472, 1079, 700, False, 0.0),
-                                                                   (88, 5431, 2501, False, 0.0)]
-    assert autotune.parse_shapes("512x1024x560") == [(512, 1024, 560, True, 0.0)]
-    with pytest.raises(ValueError):
-        autotune.parse_shapes("0x4x4")
+    assert autotune.parse_shapes("472x1079x700,88X5431x2501") == [(472, 1079, 700, False, 0.0, "NN"),
+                                                                   (88, 5431, 2501, False, 0.0, "NN")]
+    assert autotune.parse_shapes("512x1024x560,nt:512x1024x560") == [(512, 1024, 560, True, 0.0, "NN"),
+                                                                      (512, 1024, 560, True, 0.0, "NT")]
+    # a transposed A is stored K x M: its rows are M long
+    assert autotune.parse_shapes("TN:510x1024x560,TT:512x1024x560") == [(510, 1024, 560, False, 0.0, "TN"),
+                                                                         (512, 1024, 560, True, 0.0, "TT")]
+    for bad in ("0x4x4", "XN:4x4x4"):
+        with pytest.raises(ValueError):
+            autotune.parse_shapes(bad)
+
+
+def test_transposed_records_stay_out_of_the_table(tmp_path):
+    rec = {"case": "c", "class": "random", "vec_class": 1, "state": "warm", "M": 512, "N": 512, "K": 512,
+           "variant": "v", "parity": True, "ms_median": 1.0}
+    path = tmp_path / "r.json"
+    path.write_text(json.dumps({"results": [dict(rec, op="TN"), dict(rec, variant="w"), dict(rec, variant="x", op="NN")]}))
+    got = autotune.load_results([str(path)])
+    assert sorted(r["variant"] for r in got) == ["w", "x"]
