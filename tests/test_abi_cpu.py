@@ -205,6 +205,9 @@ def test_dispatch_families(M, N, K, ld_odd, prefix):
     ("T", "N", 384, 640, 640, False, True),       # K a multiple of 128
     ("T", "N", 640, 384, 701, True, True),        # unaligned
     ("T", "N", 640, 896, 720, False, False),      # small, aligned: 64x64 transposed kernels
+    ("N", "T", 900, 1100, 1800, False, True),     # small_full with at most 1024 32x32 tiles
+    ("T", "T", 901, 1101, 1801, True, True),
+    ("T", "N", 1100, 1100, 1800, False, False),   # small_full with more: 64x64 transposed kernels
     ("T", "N", 1001, 1003, 777, True, True),   # small: only with A transposed
     ("N", "T", 1001, 1003, 777, True, False),
     ("T", "T", 4096, 4096, 4096, False, False),

@@ -291,3 +291,22 @@ def test_trans_full_size_elementwise(wname, ta, tb, kind):
         check_exact(got, ref, f"full {ta}{tb}")
     else:
         check_within_bound(got, ref, bound, f"full {ta}{tb}")
+
+
+# Shapes of the transposed dispatch's finer rules: aligned tiny shapes with A transposed, K < 800
+# and a partial last 128-deep K panel (64x64 kernels in T N, the 96-deep LDS-free form in T T),
+# and small_full shapes with at most 1024 32x32 tiles (the LDS-free kernel in every form).
+RULE_SHAPES = [(768, 512, 600), (640, 384, 700), (900, 1100, 1800), (901, 1101, 1801), (600, 1688, 900)]
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS, ids=["".join(c) for c in COMBOS])
+def test_trans_dispatch_rule_shapes(ta, tb):
+    w = WORKLOADS["ragged3001x5003x777"].as_int()
+    for (M, N, K) in RULE_SHAPES:
+        A, B, C = make_inputs(w, M=M, N=N, K=K, seed=7000 + M + 7 * N + 13 * K)
+        As, Bs = stored(A, B, ta, tb)
+        vid = sg.sgemm_op_select_variant(ta, tb, M, N, K, 256, As.shape[1], 512, Bs.shape[1], 768, N)
+        _say(f"[trans-rule-dispatch] {ta}{tb} {M}x{N}x{K} variant={sg.sgemm_variant_name(vid)}")
+        got = run_op(ta, tb, A, B, C, 0.5, -1.5)
+        ref, _ = oracle.ref_rows(A, B, C, 0.5, -1.5)
+        check_exact(got, ref, f"{ta}{tb} {M}x{N}x{K}")
