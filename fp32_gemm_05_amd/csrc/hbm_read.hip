@@ -1,6 +1,6 @@
 // hbm_read.hip -- a streaming-read kernel used as the read-bandwidth reference of the
 // profiling summaries (what a plain read of a buffer reaches on this GPU), next to which the
-// HBM-bound SGEMM workload is judged, and a write of a matrix in the order in which the MFMA
+// HBM-bound SGEMM workload is compared, and a write of a matrix in the order in which the MFMA
 // epilogue stores C (the write reference of the store-heavy shapes).  Not part of libsgemm:
 // built as libhbm_read.so and called only by fp32_gemm_05_amd/profiling.py.
 #include <hip/hip_runtime.h>
