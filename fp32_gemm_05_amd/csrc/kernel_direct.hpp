@@ -58,11 +58,12 @@ struct DirectOperand {
     __device__ inline void advance() { pos += step; }
 
     // Slot d's values for k = kb + t, kb = 8 g + 4h.  Without TAIL, group g is the trip's
-    // (D + d)-th group from its position and lies wholly below K.  With TAIL (any group), k >= K
-    // gives zero: such elements are read at k = K - 1 (K - 4 for the 128-bit load) and then
-    // replaced, so that no load is conditional (a branch around a load would stop the compiler
-    // from counting the loads in flight across the loop, and it would wait for all of them at
-    // the top of every trip).
+    // (D + d)-th group from its position and lies wholly below K.  With TAIL (any group), the
+    // elements with k >= K are read at k = K - 1 (K - 4 for the 128-bit load), so that no load is
+    // conditional and no address outside the operand is formed; the caller zeroes them when it
+    // multiplies the slot (zero_past_k), one trip later.  Zeroing them here, right after the load,
+    // made the compiler wait for each load in turn (vmcnt(0) after every tail load); a branch
+    // around a load would make it wait for all loads in flight at the top of every trip.
     template <bool TAIL>
     __device__ inline void load(f32x4& v, int d, int kb, int K) {
         if (KC) {
@@ -75,15 +76,11 @@ struct DirectOperand {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = reinterpret_cast<const float*>(q)[t];
             } else if (VEC) {  // K % 4 == 0: the four k are all below K or all at or past it
-                const f32x4 x = *reinterpret_cast<const f32x4*>(origin + ((long)r * ld + imin(kb, K - 4)) * 4);
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                v = kb < K ? x : z;
+                v = *reinterpret_cast<const f32x4*>(origin + ((long)r * ld + imin(kb, K - 4)) * 4);
             } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float x = *reinterpret_cast<const float*>(origin + ((long)r * ld + imin(kb + t, K - 1)) * 4);
-                    v[t] = kb + t < K ? x : 0.f;
-                }
+                for (int t = 0; t < 4; ++t)
+                    v[t] = *reinterpret_cast<const float*>(origin + ((long)r * ld + imin(kb + t, K - 1)) * 4);
             }
         } else {
 #pragma unroll
@@ -92,13 +89,20 @@ struct DirectOperand {
                     asm volatile("" : "+v"(off[d * 4 + t]));
                     v[t] = *reinterpret_cast<const float*>(origin + pos + off[d * 4 + t]);
                 } else {
-                    const float x = *reinterpret_cast<const float*>(origin + ((long)imin(kb + t, K - 1) * ld + r) * 4);
-                    v[t] = kb + t < K ? x : 0.f;
+                    v[t] = *reinterpret_cast<const float*>(origin + ((long)imin(kb + t, K - 1) * ld + r) * 4);
                 }
             }
         }
     }
 };
+
+// The values a TAIL load read for k >= K (k = kb + t) replaced by zeros, in both operands, so
+// that the padded steps add exact zeros (0 * x with x finite, and never 0 * inf).
+__device__ inline f32x4 zero_past_k(f32x4 v, int kb, int K) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = kb + t < K ? v[t] : 0.f;
+    return v;
+}
 
 template <bool VEC, int D, bool TA = false, bool TB = false, bool CPRE = false>
 __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
@@ -126,6 +130,12 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[0][0] = mfma_step<VEC>(ra[d][t], rb[d][t], acc[0][0]);
     };
+    auto mfma_tail = [&](int d, int grp) {  // slot d holds group grp, which may reach past K
+        const int kb = 8 * grp + 4 * lh;
+        const f32x4 a = zero_past_k(ra[d], kb, K), b = zero_past_k(rb[d], kb, K);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[0][0] = mfma_step<VEC>(a[t], b[t], acc[0][0]);
+    };
     auto advance = [&]() {
         oa.advance();
         ob.advance();
@@ -140,6 +150,7 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
     f32x16 cv[1][1];  // CPRE: C for the beta term, read after the ring's first loads
     if (CPRE && g.beta != 0.f) mfma_load_c<1, 1, VEC>(g.M, g.N, g.C, g.ldc, cv, m0, n0, li, lh);
     int q = 0;
+    // main trips: slots q .. q + D - 1 hold groups below nfull, read exactly
     for (; q + 2 * D <= nfull; q += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -151,12 +162,12 @@ __global__ void __launch_bounds__(64) sgemm_mfma_direct_kernel(GemmArgs g, int t
     for (; q + D < ngroups; q += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            mfma(d);
+            mfma_tail(d, q + d);
             load(d, q + D + d, Tail{});
         }
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d) mfma(d);
+    for (int d = 0; d < D; ++d) mfma_tail(d, q + d);
 
     mfma_epilogue<1, 1, VEC, CPRE>(g.M, g.N, g.alpha, g.beta, g.C, g.ldc, acc, m0, n0, li, lh, cv);
 }
