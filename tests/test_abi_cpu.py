@@ -178,7 +178,8 @@ def _name(v):
     (333, 555, 777, True, "mfma16l_32x64"),
     (1554, 64, 5093, True, "mfma16l_32x64"),   # skinny with few tiles joins the small classes
     (1024, 1024, 1024, False, "mfma32l_64x64"),  # small, aligned: 64x64 workgroups fill the CUs
-    (1001, 1003, 777, True, "mfma16l_64x64"),  # small, unaligned: 16x16-block workgroups of 8 waves
+    (1001, 1003, 777, True, "mfma32r_32x32x96"),  # small, unaligned: the LDS-free kernel, 96-deep
+    (1199, 587, 3229, True, "mfma32r_32x32x96"),  # small_longk, unaligned
     (1111, 1113, 1001, True, "mfma16l_32x64"),  # small_full, unaligned
     (1089, 728, 5752, False, "mfma32l_64x64"),  # small_longk, aligned: the direct-to-LDS ring
     (4096, 4096, 4096, False, "mfma32_128x128"),
@@ -199,15 +200,17 @@ def test_dispatch_families(M, N, K, ld_odd, prefix):
     ("N", "T", 333, 555, 777, True, True),
     ("T", "T", 512, 512, 512, False, True),
     ("T", "T", 88, 5428, 2500, False, True),      # tiny by the 32x64 tile count
-    ("T", "N", 768, 512, 600, False, False),      # aligned, A transposed, K < 800, partial 128-deep
-    ("T", "T", 640, 384, 700, False, True),       # panel: 64x64 in T N, the 96-deep form in T T
+    ("T", "N", 768, 512, 600, False, True),       # aligned T N: the 96-deep form unless K % 128 == 0
+    ("T", "T", 640, 384, 700, False, True),       # aligned T T: the 128-deep form below K = 768
+    ("T", "T", 332, 552, 776, False, True),       # ... and the 96-deep one from there on
     ("N", "T", 768, 512, 600, False, True),
     ("T", "N", 384, 640, 640, False, True),       # K a multiple of 128
     ("T", "N", 640, 384, 701, True, True),        # unaligned
-    ("T", "N", 640, 896, 720, False, False),      # small, aligned: 64x64 transposed kernels
+    ("T", "N", 640, 896, 720, False, True),       # small, aligned: the LDS-free kernel too
     ("N", "T", 900, 1100, 1800, False, True),     # small_full with at most 1024 32x32 tiles
     ("T", "T", 901, 1101, 1801, True, True),
-    ("T", "N", 1100, 1100, 1800, False, False),   # small_full with more: 64x64 transposed kernels
+    ("T", "T", 1100, 1100, 1800, False, False),   # small_full with more: 64x64 transposed kernels
+    ("T", "N", 1300, 1000, 1200, False, True),    # ... but for T N
     ("T", "N", 1001, 1003, 777, True, True),   # small: only with A transposed
     ("N", "T", 1001, 1003, 777, True, False),
     ("T", "T", 4096, 4096, 4096, False, False),
@@ -224,8 +227,9 @@ def test_op_dispatch_families(ta, tb, M, N, K, odd, direct):
     info = sg.sgemm_variant_info(v)
     assert (info["trans_a"], info["trans_b"]) == (int(ta == "T"), int(tb == "T"))
     assert _name(v).startswith("mfma32r_") == direct, _name(v)
-    if direct and not odd and ta == "T" and K < 800 and K % 128:
-        assert _name(v).startswith("mfma32r_32x32x96_") and _name(v).endswith("_scalar"), _name(v)
+    if direct:  # its form: 128-deep 128-bit loads, or 96-deep 32-bit loads
+        deep128 = not odd and (ta == "N" or K % 128 == 0 or (tb == "T" and K < 768))
+        assert _name(v).startswith("mfma32r_32x32x128_" if deep128 else "mfma32r_32x32x96_"), _name(v)
     if ta == "N" and tb == "T" and N <= 64 and M >= 65536:
         assert "_nta_nt_" in _name(v) and info["BN"] == (32 if N <= 32 else 64), _name(v)
 
